@@ -1,0 +1,306 @@
+/*
+ * dspark_oracle.c -- CPU oracle for the DSpark ancestral draft-block sampler.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the plain, slow, obviously correct
+ * statement of what the sampler computes. Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the GPU library
+ * never calls it and shares no code with it.
+ *
+ * Sources (page titles as on the pages):
+ *  - "brb-nv/TensorRT-LLM pull 21", section "2. Golden sampling semantics":
+ *    position k is drawn from softmax((base_k + bias(d_{k-1})) / T), with
+ *    d_{k-1} the token drawn before it; drafts use the temperature only;
+ *    greedy requests draft the argmax chain; the distribution each draft was
+ *    drawn from is stored as its proposal.
+ *  - "brb-nv/TensorRT-LLM pull 27", section "2. One fused kernel per draft
+ *    position": the Markov bias is added, the logits are scaled by 1/T, the
+ *    token is the argmax of the scaled logits plus Gumbel noise; the noise is
+ *    a counter-based Philox stream keyed by the request's (seed, offset) slot
+ *    and the position; the drafter logits are read as f32 or bf16 and the
+ *    biased logits are kept in float32; the proposal q_k = softmax(logits_k/T)
+ *    is recomputed from those float32 logits exactly as the draw used them;
+ *    CUDA-graph padding rows draw from the bias alone.
+ *  - Philox4x32-10: Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+ *    As Easy as 1, 2, 3", SC'11, section 3 (the Philox round and key schedule).
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *  - bias(d) = E[d] . W with E [V,r] and W [r,V] in bf16; the bias is the
+ *    exact sum rounded once to float32 (here: double accumulation of exact
+ *    bf16 products, then one rounding).
+ *  - logit = float32(base) + float32(bias), one float32 addition. Padding
+ *    rows (b >= n_real) use base = 0 and never read their base row.
+ *  - Greedy rows are those with !(T > 0): their token is the lowest index of
+ *    the largest logit and their proposal is one-hot at that token.
+ *  - Sampling rows: invT = float32(1/T); s = float32(logit * invT).
+ *    Philox key = (lo32(seed), hi32(seed)); counter = (v >> 2, k,
+ *    lo32(offset), hi32(offset)); the noise word is output word (v & 3).
+ *    u = ((x >> 9) + 1/2) * 2^-23, which is exact and lies in
+ *    [2^-24, 1 - 2^-24]; g = -ln(-ln u), evaluated in double and rounded to
+ *    float32; the perturbed score is z = float32(s + g). The draw is the
+ *    lowest index of the largest z (the decision is taken in float32, the
+ *    precision the GPU kernel uses). A NaN score never wins; a row whose
+ *    every score is NaN draws token 0.
+ *  - Proposal: M = max s, S = sum exp(s - M), q = exp(s - M) / S, in double.
+ *  - prev_token is clamped into [0, V).
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math):
+ * every float expression above is a single IEEE binary32 operation.
+ */
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- Philox4x32-10 (SC'11, section 3) ---------------------------------- */
+
+/* Multipliers and Weyl key increments of Philox4x32 as given in the paper. */
+static const uint32_t kPhiloxMul0 = 0xD2511F53u;
+static const uint32_t kPhiloxMul1 = 0xCD9E8D57u;
+static const uint32_t kPhiloxWeyl0 = 0x9E3779B9u;
+static const uint32_t kPhiloxWeyl1 = 0xBB67AE85u;
+
+/* Ten rounds of the Philox4x32 bijection on `ctr` under `key`.
+ * One round: the products M0*c0 and M1*c2 are split into high and low
+ * words; the new block is (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2),
+ * hi(M0*c0) ^ c3 ^ k1, lo(M0*c0)). The key is bumped by the Weyl
+ * constants before every round after the first. */
+void dspark_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += kPhiloxWeyl0;
+            k1 += kPhiloxWeyl1;
+        }
+        uint64_t p0 = (uint64_t)kPhiloxMul0 * (uint64_t)c0;
+        uint64_t p1 = (uint64_t)kPhiloxMul1 * (uint64_t)c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The 32-bit noise word of vocabulary entry v at draft position k for the
+ * slot (seed, offset). */
+uint32_t dspark_oracle_noise_word(uint64_t seed, uint64_t offset, uint32_t k, uint32_t v)
+{
+    uint32_t ctr[4] = { v >> 2, k, (uint32_t)offset, (uint32_t)(offset >> 32) };
+    uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) };
+    uint32_t out[4];
+    dspark_oracle_philox4x32_10(ctr, key, out);
+    return out[v & 3u];
+}
+
+/* Uniform in the open unit interval from the top 23 bits of a word. */
+double dspark_oracle_uniform(uint32_t x)
+{
+    return ((double)(x >> 9) + 0.5) / 8388608.0; /* 2^23 */
+}
+
+/* Standard Gumbel variate -ln(-ln u), rounded to float32. */
+float dspark_oracle_gumbel(uint32_t x)
+{
+    double u = dspark_oracle_uniform(x);
+    return (float)(-log(-log(u)));
+}
+
+void dspark_oracle_uniform_batch(const uint32_t* x, double* u, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) u[i] = dspark_oracle_uniform(x[i]);
+}
+
+void dspark_oracle_gumbel_batch(const uint32_t* x, float* g, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) g[i] = dspark_oracle_gumbel(x[i]);
+}
+
+/* ---- the draft block ------------------------------------------------------ */
+
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+typedef struct {
+    const void* base; int base_is_bf16;     /* [B,K,V] */
+    const uint16_t* E;                      /* [V,r] bf16 */
+    const uint16_t* W;                      /* [r,V] bf16 */
+    const int32_t* prev_token;              /* [B] */
+    const int64_t* seed;                    /* [B] */
+    const int64_t* offset;                  /* [B] */
+    const float* temperature;               /* [B] */
+    int n_real;                             /* < 0: every row is real */
+    int B, K, V, r;
+    const int32_t* forced;                  /* [B,K] or NULL; >= 0 replaces the token */
+    double tie_eps;
+    int max_cand;
+    int32_t* tokens;                        /* [B,K] the token each position carries */
+    int32_t* own_tokens;                    /* [B,K] or NULL: the oracle's own draw */
+    float* logits;                          /* [B,K,V] or NULL */
+    double* q;                              /* [B,K,V] or NULL */
+    double* margin;                         /* [B,K] or NULL */
+    int32_t* ncand;                         /* [B,K] or NULL */
+    int32_t* cand;                          /* [B,K,max_cand] or NULL */
+} OracleArgs;
+
+static float base_at(const OracleArgs* a, int b, int k, int v)
+{
+    size_t i = ((size_t)b * a->K + k) * a->V + v;
+    if (a->base_is_bf16) return bf16_to_float(((const uint16_t*)a->base)[i]);
+    return ((const float*)a->base)[i];
+}
+
+/* Does score za at index ia beat zb at index ib?  NaN never wins; equal
+ * scores go to the lower index. */
+static int beats(float za, int ia, float zb, int ib)
+{
+    if (isnan(za)) return 0;
+    if (ib < 0 || isnan(zb)) return 1;
+    if (za > zb) return 1;
+    if (za < zb) return 0;
+    return ia < ib;
+}
+
+static void draft_row(const OracleArgs* a, int b, double* acc, float* lg, float* s, float* z)
+{
+    const int K = a->K, V = a->V, r = a->r;
+    const int pad = (a->n_real >= 0 && b >= a->n_real);
+    const float T = a->temperature[b];
+    const int greedy = !(T > 0.0f);
+    const float invT = greedy ? 0.0f : 1.0f / T;
+    const uint64_t seed = (uint64_t)a->seed[b];
+    const uint64_t off = (uint64_t)a->offset[b];
+    int32_t d = a->prev_token[b];
+    if (d < 0) d = 0;
+    if (d > V - 1) d = V - 1;
+
+    for (int k = 0; k < K; ++k) {
+        /* bias[v] = sum_j E[d,j] * W[j,v]: exact products, double sum, one rounding */
+        for (int v = 0; v < V; ++v) acc[v] = 0.0;
+        for (int j = 0; j < r; ++j) {
+            const double e = (double)bf16_to_float(a->E[(size_t)d * r + j]);
+            const uint16_t* wrow = a->W + (size_t)j * V;
+            for (int v = 0; v < V; ++v) acc[v] += e * (double)bf16_to_float(wrow[v]);
+        }
+        for (int v = 0; v < V; ++v) {
+            const float base_v = pad ? 0.0f : base_at(a, b, k, v);
+            lg[v] = base_v + (float)acc[v];
+        }
+
+        /* scores and the draw */
+        int best = -1;
+        for (int v = 0; v < V; ++v) {
+            if (greedy) {
+                z[v] = lg[v];
+            } else {
+                s[v] = lg[v] * invT;
+                const float g = dspark_oracle_gumbel(dspark_oracle_noise_word(seed, off, (uint32_t)k, (uint32_t)v));
+                z[v] = s[v] + g;
+            }
+            if (beats(z[v], v, best < 0 ? 0.0f : z[best], best)) best = v;
+        }
+        const int own = best < 0 ? 0 : best;
+
+        /* runner-up score and the set of near-tied candidates */
+        double second = -INFINITY;
+        int n_near = 0;
+        for (int v = 0; v < V; ++v) {
+            if (isnan(z[v])) continue;
+            if (v != best && (double)z[v] > second) second = (double)z[v];
+            if (best >= 0 && (double)z[v] >= (double)z[best] - a->tie_eps) {
+                if (a->cand && n_near < a->max_cand)
+                    a->cand[((size_t)b * K + k) * a->max_cand + n_near] = v;
+                ++n_near;
+            }
+        }
+        const size_t bk = (size_t)b * K + k;
+        if (a->margin) a->margin[bk] = best < 0 ? INFINITY : (double)z[best] - second;
+        if (a->ncand) a->ncand[bk] = n_near;
+        if (a->own_tokens) a->own_tokens[bk] = own;
+
+        int carried = own;
+        if (a->forced && a->forced[bk] >= 0) carried = a->forced[bk];
+        a->tokens[bk] = carried;
+
+        if (a->logits) memcpy(a->logits + bk * V, lg, (size_t)V * sizeof(float));
+
+        if (a->q) {
+            double* q = a->q + bk * V;
+            if (greedy) {
+                for (int v = 0; v < V; ++v) q[v] = (v == carried) ? 1.0 : 0.0;
+            } else {
+                double M = -INFINITY;
+                for (int v = 0; v < V; ++v)
+                    if ((double)s[v] > M) M = (double)s[v];
+                double S = 0.0;
+                for (int v = 0; v < V; ++v) S += exp((double)s[v] - M);
+                for (int v = 0; v < V; ++v) q[v] = exp((double)s[v] - M) / S;
+            }
+        }
+        d = carried;
+    }
+}
+
+/* Run the sampler over every row.  Returns 0, or -1 on bad arguments. */
+int dspark_oracle_draft_block(
+    const void* base, int base_is_bf16, const uint16_t* E, const uint16_t* W,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, int n_real, int B, int K, int V, int r,
+    const int32_t* forced, double tie_eps, int max_cand,
+    int32_t* tokens, int32_t* own_tokens, float* logits, double* q,
+    double* margin, int32_t* ncand, int32_t* cand, int num_threads)
+{
+    if (B < 0 || K < 0 || V <= 0 || r <= 0) return -1;
+    if (B == 0 || K == 0) return 0;
+    if (!base || !E || !W || !prev_token || !seed || !offset || !temperature || !tokens) return -1;
+    if (cand && max_cand <= 0) return -1;
+    OracleArgs a = { base, base_is_bf16, E, W, prev_token, seed, offset, temperature, n_real,
+                     B, K, V, r, forced, tie_eps, max_cand, tokens, own_tokens, logits, q,
+                     margin, ncand, cand };
+    int failed = 0;
+#ifdef _OPENMP
+    if (num_threads <= 0) num_threads = omp_get_max_threads();
+#pragma omp parallel num_threads(num_threads)
+#endif
+    {
+        double* acc = (double*)malloc((size_t)V * sizeof(double));
+        float* lg = (float*)malloc((size_t)V * sizeof(float));
+        float* s = (float*)malloc((size_t)V * sizeof(float));
+        float* z = (float*)malloc((size_t)V * sizeof(float));
+        if (!acc || !lg || !s || !z) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int b = 0; b < B; ++b)
+            if (acc && lg && s && z) draft_row(&a, b, acc, lg, s, z);
+        free(acc); free(lg); free(s); free(z);
+    }
+    return failed ? -2 : 0;
+}
+
+/* Number of threads the oracle uses when asked for the default. */
+int dspark_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
