@@ -1,0 +1,130 @@
+"""DSpark ancestral draft-block sampler for MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libdspark.so`` (declared in
+``include/dspark.h``). Every step of the sampler runs in the library's HIP
+kernels; this module only loads the library and turns torch device tensors
+into pointers and sizes. It has no fallback: if the library is missing or a
+call fails, it raises.
+
+PyTorch supplies device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdspark.so")
+
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+DSPARK_OK = 0
+DSPARK_ERR_ARG = -1
+DSPARK_ERR_UNSUPPORTED = -2
+DSPARK_ERR_WORKSPACE = -3
+DSPARK_ERR_HIP = -4
+
+EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
+            "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_status_string")
+
+_lib = None
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {status} ({status_string(status)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libdspark.so`` (built by ``__graft_entry__.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch ships its own HIP runtime; import it first so the library binds to
+    # that same runtime (one runtime per process: streams and pointers agree)
+    import torch  # noqa: F401
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.dspark_init.argtypes = []
+    lib.dspark_init.restype = I
+    lib.dspark_workspace_bytes.argtypes = [I, I, I, I]
+    lib.dspark_workspace_bytes.restype = Z
+    block_args = [P, I, P, P, P, P, P, P, P, I, I, I, I]
+    out_args = [P, P, P, P, Z, P]
+    lib.dspark_draft_block.argtypes = block_args + out_args
+    lib.dspark_draft_block.restype = I
+    lib.dspark_draft_block_chunked.argtypes = block_args + [I] + out_args
+    lib.dspark_draft_block_chunked.restype = I
+    lib.dspark_draft_block_events.argtypes = block_args + out_args + [P, I]
+    lib.dspark_draft_block_events.restype = I
+    lib.dspark_status_string.argtypes = [I]
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().dspark_status_string(int(status)).decode()
+
+
+def dspark_init() -> None:
+    rc = load_library().dspark_init()
+    if rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_init")
+
+
+def dspark_workspace_bytes(B: int, K: int, V: int, r: int) -> int:
+    return int(load_library().dspark_workspace_bytes(B, K, V, r))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, offset, temperature,
+                       n_real, B: int, K: int, V: int, r: int, tokens, logits_f32, draft_probs,
+                       workspace, workspace_bytes: int, stream=None, chunk_cols: Optional[int] = None,
+                       events=None, check: bool = True) -> int:
+    """Enqueue one draft block; arguments as in ``include/dspark.h``.
+
+    Tensor arguments may be torch device tensors or raw device addresses
+    (ints); ``n_real`` may be None. ``stream`` is a torch stream, a raw
+    hipStream_t, or None for torch's current stream. Returns the status; with
+    ``check`` a nonzero status raises. ``events`` (a ctypes array of
+    hipEvent_t handles, at least 2K + 2) selects ``dspark_draft_block_events``.
+    """
+    lib = load_library()
+    args = [_ptr(base_logits), int(base_dtype), _ptr(E), _ptr(W), _ptr(prev_token), _ptr(seed),
+            _ptr(offset), _ptr(temperature), _ptr(n_real), int(B), int(K), int(V), int(r)]
+    outs = [_ptr(tokens), _ptr(logits_f32), _ptr(draft_probs), _ptr(workspace), int(workspace_bytes),
+            _stream_ptr(stream)]
+    if events is not None:
+        rc = lib.dspark_draft_block_events(*args, *outs, ctypes.cast(events, ctypes.c_void_p), len(events))
+        where = "dspark_draft_block_events"
+    elif chunk_cols is None:
+        rc = lib.dspark_draft_block(*args, *outs)
+        where = "dspark_draft_block"
+    else:
+        rc = lib.dspark_draft_block_chunked(*args, int(chunk_cols), *outs)
+        where = "dspark_draft_block_chunked"
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, where)
+    return rc

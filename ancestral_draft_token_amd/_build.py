@@ -1,0 +1,49 @@
+"""Build the HIP library in-tree for gfx950 (MI355X).
+
+``hipcc`` cross-compiles without a GPU. The library is one shared object,
+``ancestral_draft_token_amd/libdspark.so``, exporting the C ABI declared in
+``include/dspark.h``.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "dspark.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdspark.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # the bit-for-bit logits/T recompute needs every float op rounded on its own
+    "-ffp-contract=off",
+    # no packed-FP32 instructions: ordinary float code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build_library(out: str = LIB, extra_flags=()) -> str:
+    """Compile ``csrc/dspark.hip`` into ``out`` (always recompiles)."""
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", "-o", tmp, SRC]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build_library())

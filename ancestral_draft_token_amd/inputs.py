@@ -30,13 +30,17 @@ BF16 = "bf16"
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); NaN stays a quiet NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb can wrap only for NaN bit patterns, which are replaced below
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        rounded = rounded.copy()
-        rounded[nan] = np.uint16(0x7FC0)
-    return rounded
+        out[nan] = np.uint16(0x7FC0)
+    return out
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:

@@ -1,0 +1,232 @@
+"""Benchmark of the DSpark ancestral draft block on one MI355X.
+
+One step = one replay of the hipGraph that holds the whole K-position block
+(K fused per-position kernels, K pick_and_gather launches, one proposal
+kernel) over one batch of synthetic inputs already resident in HBM.
+
+Default workload: single-request decode, B=1, K=7, V=200064, r=256, bf16
+base logits -- the drafting-alone setup of the pages ("brb-nv/TensorRT-LLM
+pull 27", section "Commits 1-2: fixed-shape decode", drafting-alone table).
+
+MALL ("cold", the default): before every timed replay a 1 GiB buffer is
+written, outside the timed region, so W (102 MB) does not start in the
+256 MB Infinity Cache -- as after a target-model forward in serving. "warm"
+replays back to back. A step's time is the HIP-event time of its replay.
+
+Prints ONE JSON line (rank 0, N=1).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, AMD published peak
+PAGES_B1_US = 148.0           # the pages' drafting-alone time at B=1 (GB300), context only
+METRIC = "µs per K=7 draft block (V=200064) at B=1/8/44/88; % of HBM roofline"
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move (see the byte model in the design notes).
+
+    Per position: base (real rows), W once, float32 logits written, the
+    embedding rows gathered. Per block: logits re-read and q written by the
+    proposal, tokens written.
+    """
+    s_base = 2 if w.base_dtype == "bf16" else 4
+    B, K, V, r = w.B, w.K, w.V, w.r
+    k1 = w.n_real_rows * V * s_base + r * V * 2 + B * V * 4 + B * r * 2
+    prop = B * K * V * (4 + 4)
+    total = K * k1 + prop + B * K * 4
+    return {"fused_per_launch": k1, "proposal_per_launch": prop, "block": total}
+
+
+class Bench:
+    def __init__(self, w, mall="cold"):
+        import torch
+        from ancestral_draft_token_amd.device import DeviceProblem
+        self.torch = torch
+        self.w = w
+        self.mall = mall
+        self.p = DeviceProblem(w)
+        self.stream = torch.cuda.Stream()
+        self.flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        self.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            self.p.enqueue()                      # eager call before capture
+            self.graph.capture_begin()
+            self.p.enqueue()
+            self.graph.capture_end()
+        torch.cuda.synchronize()
+
+    def flush(self):
+        if self.mall == "cold":
+            self.flush_buf.fill_(1)
+
+    def steps(self, n):
+        """n timed replays; returns per-replay microseconds (HIP events on the replay stream)."""
+        torch = self.torch
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        with torch.cuda.stream(self.stream):
+            for i in range(n):
+                self.flush()
+                starts[i].record(self.stream)
+                self.graph.replay()
+                ends[i].record(self.stream)
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]
+
+    def kernel_times(self, reps):
+        """Eager blocks with an event after every launch: mean us per launch of each kernel."""
+        torch = self.torch
+        from ancestral_draft_token_amd.hip_events import EventSet
+        K = self.w.K
+        fused, pick, prop = [], [], []
+        ev = EventSet(2 * K + 2)
+        try:
+            for _ in range(reps):
+                with torch.cuda.stream(self.stream):
+                    self.flush()
+                    self.p.enqueue(stream=self.stream, events=ev.handles, chunk_cols=None)
+                ev.synchronize()
+                for k in range(K):
+                    fused.append(ev.elapsed_ms(2 * k, 2 * k + 1) * 1e3)
+                    pick.append(ev.elapsed_ms(2 * k + 1, 2 * k + 2) * 1e3)
+                prop.append(ev.elapsed_ms(2 * K, 2 * K + 1) * 1e3)
+        finally:
+            torch.cuda.synchronize()
+            ev.close()
+        return {"markov_bias_gumbel_argmax": statistics.mean(fused),
+                "pick_and_gather": statistics.mean(pick),
+                "proposal_softmax": statistics.mean(prop)}
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The CPU oracle, as it stands, on the same workload: whole blocks, repeated."""
+    import oracle
+    threads = min(w.B, oracle.max_threads())
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.draft_block(w, num_threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    return {"value": el / reps * 1e6, "unit": "us/block", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full blocks of {w.name} (all {w.K} positions, V={w.V}), "
+                      f"{el:.1f} s of CPU work"}
+
+
+def measure(w, steps, warmup, mall, kernel_reps=5):
+    b = Bench(w, mall=mall)
+    b.steps(warmup)
+    torch = b.torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    us = b.steps(steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = b.kernel_times(kernel_reps)
+    ab = algorithmic_bytes(w)
+    med = statistics.median(us)
+    res = {
+        "us_per_block": statistics.mean(us),
+        "us_median": med,
+        "us_p10": sorted(us)[len(us) // 10],
+        "us_p90": sorted(us)[(len(us) * 9) // 10],
+        "wall_s": wall,
+        "kernels_us": kt,
+        "bytes": ab,
+        "block_gbs": ab["block"] / (statistics.mean(us) * 1e-6) / 1e9,
+    }
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b1", choices=["tiny", "b1", "b8", "b44", "b88"])
+    ap.add_argument("--mall", default="cold", choices=["cold", "warm"])
+    ap.add_argument("--no-sweep", action="store_true", help="skip the B=8/44/88 lines in 'also'")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the sampler has no multi-GPU path in this build "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ancestral_draft_token_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = inputs.WORKLOADS[args.workload]()
+    print(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}, MALL {args.mall}",
+          file=sys.stderr, flush=True)
+    r = measure(w, args.steps, args.warmup, args.mall)
+    fused_us = r["kernels_us"]["markov_bias_gumbel_argmax"]
+    achieved = r["bytes"]["fused_per_launch"] / (fused_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(r["us_per_block"], 2),
+        "unit": "us/block",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["us_per_block"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": (round(r["us_per_block"] / PAGES_B1_US, 4) if args.workload == "b1" else None),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "B_real": w.n_real_rows, "K": w.K, "V": w.V,
+                   "r": w.r, "base": w.base_dtype, "mall": args.mall,
+                   "graph": "one hipGraph per block (2K+1 launches)"},
+        "us_median": round(r["us_median"], 2),
+        "us_p10": round(r["us_p10"], 2),
+        "us_p90": round(r["us_p90"], 2),
+        "block_roofline_frac": round(r["block_gbs"] / HBM_PEAK_GBS, 4),
+        "kernels_us": {k: round(v, 2) for k, v in r["kernels_us"].items()},
+        "roofline": {"bound": "hbm", "kernel": "markov_bias_gumbel_argmax",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": r["bytes"]["fused_per_launch"]},
+    }
+    if not args.no_sweep:
+        also = {}
+        for name in ("b8", "b44", "b88"):
+            if name == args.workload:
+                continue
+            wo = inputs.WORKLOADS[name]()
+            print(f"[bench] also {wo.name}", file=sys.stderr, flush=True)
+            ro = measure(wo, max(10, args.steps // 4), 3, args.mall)
+            also[name] = {"workload": wo.name, "us_per_block": round(ro["us_per_block"], 2),
+                          "block_roofline_frac": round(ro["block_gbs"] / HBM_PEAK_GBS, 4),
+                          "kernels_us": {k: round(v, 2) for k, v in ro["kernels_us"].items()}}
+            del wo
+        line["also"] = also
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

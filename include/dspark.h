@@ -1,0 +1,150 @@
+/*
+ * dspark.h -- C ABI of the DSpark ancestral draft-block sampler for MI355X (gfx950).
+ *
+ * What one call computes ("brb-nv/TensorRT-LLM pull 21", section "2. Golden
+ * sampling semantics"; "brb-nv/TensorRT-LLM pull 27", section "2. One fused
+ * kernel per draft position"): for each row b and each draft position
+ * k = 0..K-1,
+ *
+ *     logits[b,k,:] = float32(base[b,k,:]) + bias(d_{k-1}),   bias(d) = E[d,:] . W
+ *     d_k           = argmax_v ( logits[b,k,v] * (1/T_b) + Gumbel noise ),
+ *
+ * where d_{-1} = prev_token[b] and the Gumbel noise comes from a counter-based
+ * Philox4x32-10 stream keyed by the row's (seed, offset) slot and k. After the
+ * block, draft_probs[b,k,:] = softmax(logits[b,k,:] * (1/T_b)), recomputed
+ * bit for bit from the stored float32 logits exactly as the draw used them.
+ * Greedy rows (!(T_b > 0)) take the argmax chain of the logits and get a
+ * one-hot proposal. Graph-padding rows (b >= *n_real) draw from the bias
+ * alone: their base row is never read.
+ *
+ * Exact conventions (the pages leave these open; this library fixes them):
+ *   - bias accumulates exact bf16 x bf16 products in float32 and is added to
+ *     the float32 base in one float32 addition; it is never rounded to bf16.
+ *   - invT = float32(1 / T); s = float32(logit * invT).
+ *   - Philox key = (lo32(seed), hi32(seed)); counter = (v >> 2, k,
+ *     lo32(offset), hi32(offset)); noise word = output word (v & 3).
+ *   - u = ((x >> 9) + 0.5) * 2^-23 (exact, in [2^-24, 1 - 2^-24]);
+ *     g = -ln(-ln u); z = float32(s + g). Greedy rows use z = logit.
+ *   - d_k is the lowest index among the largest z. NaN scores never win; a
+ *     row whose every score is NaN draws token 0.
+ *   - q = exp(s - M) / S with M the row maximum of s and S = sum exp(s - M).
+ *
+ * Memory: every array argument is a DEVICE pointer owned by the caller,
+ * row-major and contiguous, 16-byte aligned. The library never allocates,
+ * frees, synchronises, or reads device data on the host, so a call can be
+ * captured into a hipGraph and replayed; seeds, offsets, temperatures and
+ * n_real are read on the device, so replays see new values without a new
+ * capture. The caller advances `offset` between blocks (a new offset draws
+ * anew).
+ *
+ * Errors: argument checks run on the host before anything is enqueued; a
+ * failed check returns a negative status and enqueues nothing. A failed
+ * kernel launch returns DSPARK_ERR_HIP. No C++ exception crosses the ABI.
+ * Device data never causes an error: an out-of-range prev_token is clamped
+ * into [0, V), and the drawn token is always in [0, V).
+ *
+ * Concurrency: calls on different streams must use different workspaces
+ * and outputs.
+ */
+#ifndef DSPARK_H_
+#define DSPARK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSPARK_F32 = 0,   /* base logits are float32 */
+    DSPARK_BF16 = 1   /* base logits are bfloat16 (uint16 bit patterns) */
+} dspark_dtype_t;
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_ERR_ARG = -1,          /* null pointer, bad size, misaligned pointer, bad dtype */
+    DSPARK_ERR_UNSUPPORTED = -2,  /* V % 8 != 0, r % 32 != 0, r > 1024, K > 255, ... */
+    DSPARK_ERR_WORKSPACE = -3,    /* workspace missing or smaller than dspark_workspace_bytes */
+    DSPARK_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} dspark_status_t;
+
+/* Loads the kernels on the current device. Call once per device before any
+ * stream capture. Returns DSPARK_OK or DSPARK_ERR_HIP. */
+int dspark_init(void);
+
+/* Device workspace bytes a call with these sizes needs (for any chunking).
+ * Returns 0 for sizes the library does not support. */
+size_t dspark_workspace_bytes(int B, int K, int V, int r);
+
+/* One K-position draft block ("brb-nv/TensorRT-LLM pull 27", section
+ * "2. One fused kernel per draft position").
+ *
+ *   base_logits  [B,K,V] float32 or bf16 (per base_dtype); read only, never written
+ *   E            [V,r]   bf16 Markov embedding
+ *   W            [r,V]   bf16 Markov head
+ *   prev_token   [B]     int32, d_{-1}: the row's last committed token (clamped)
+ *   seed         [B]     int64, Philox key bits
+ *   offset       [B]     int64, Philox slot offset
+ *   temperature  [B]     float32; !(T > 0) marks a greedy row
+ *   n_real       device int32 scalar, or NULL (all rows real); rows b >= *n_real
+ *                are graph padding
+ *   B, K, V, r   sizes: B >= 0, 0 <= K <= 255, V > 0 and V % 8 == 0,
+ *                0 < r <= 1024 and r % 32 == 0. B == 0 or K == 0 enqueues nothing.
+ *   tokens       [B,K]   int32 out: the drawn tokens
+ *   logits_f32   [B,K,V] float32 out: base + bias, before the 1/T scaling
+ *   draft_probs  [B,K,V] float32 out: the proposal q_k
+ *   workspace    device scratch of at least dspark_workspace_bytes(B,K,V,r) bytes;
+ *                its contents need no initialisation and are not meaningful after
+ *   stream       hipStream_t to enqueue on (NULL = the null stream)
+ */
+int dspark_draft_block(
+    const void* base_logits, int base_dtype,
+    const uint16_t* E, const uint16_t* W,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, const int32_t* n_real,
+    int B, int K, int V, int r,
+    int32_t* tokens, float* logits_f32, float* draft_probs,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same block with an explicit vocabulary chunking: each workgroup of the
+ * fused per-position kernel owns `chunk_cols` consecutive vocabulary columns
+ * (a positive multiple of 128; 0 = the library's choice) and writes one
+ * softmax-statistics and argmax partial per row. The pages test one and three
+ * vocabulary chunks ("brb-nv/TensorRT-LLM pull 27", section "Test Coverage");
+ * tokens and logits do not depend on the chunking, q only through the order
+ * of a float32 sum. */
+int dspark_draft_block_chunked(
+    const void* base_logits, int base_dtype,
+    const uint16_t* E, const uint16_t* W,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, const int32_t* n_real,
+    int B, int K, int V, int r, int chunk_cols,
+    int32_t* tokens, float* logits_f32, float* draft_probs,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The default-chunked block with timing marks, for measurement: events[0]
+ * is recorded on `stream` before the first launch and events[i + 1] after
+ * the i-th launch, in launch order (position k's fused kernel is launch 2k,
+ * its pick_and_gather launch 2k + 1, the proposal kernel launch 2K), so
+ * n_events must be at least 2K + 2. The events are caller-created
+ * hipEvent_t handles passed as void*. Returns DSPARK_ERR_ARG if events is
+ * NULL or too short; otherwise as dspark_draft_block. */
+int dspark_draft_block_events(
+    const void* base_logits, int base_dtype,
+    const uint16_t* E, const uint16_t* W,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, const int32_t* n_real,
+    int B, int K, int V, int r,
+    int32_t* tokens, float* logits_f32, float* draft_probs,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int n_events);
+
+/* A static, human-readable name for a status code. */
+const char* dspark_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H_ */

@@ -1,0 +1,40 @@
+"""Helpers shared by the GPU tests: run a workload through the C ABI and fetch rows."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+
+def require_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(msg: str):
+    """Name the case before each GPU step, flushed, so a crash still says where it was."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w, chunk_cols=None):
+    """Run one block on cuda:0; return (problem, tokens, logits, q) as host arrays."""
+    import torch
+    from ancestral_draft_token_amd.device import DeviceProblem
+    say(f"run {w.name} B={w.B} K={w.K} V={w.V} r={w.r} base={w.base_dtype} chunk={chunk_cols}")
+    p = DeviceProblem(w, chunk_cols=chunk_cols)
+    p.enqueue()
+    torch.cuda.synchronize()
+    return p
+
+
+def rows_to_host(p, rows):
+    rows = np.asarray(rows, dtype=np.int64)
+    import torch
+    idx = torch.from_numpy(rows).to(p.tokens.device)
+    return (p.tokens.index_select(0, idx).cpu().numpy(),
+            p.logits.index_select(0, idx).cpu().numpy(),
+            p.q.index_select(0, idx).cpu().numpy())

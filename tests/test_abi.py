@@ -1,0 +1,124 @@
+"""The C-ABI library loads and exports every symbol the header declares; host-side
+argument checks return their documented status before anything is enqueued.
+
+No kernel runs here: every call below fails a host check (or has B == 0), so
+the library returns before its first HIP call.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import ancestral_draft_token_amd as adt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(adt.LIB_PATH):
+        from ancestral_draft_token_amd import _build
+        _build.build_library()
+    return adt.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(adt.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code in (adt.DSPARK_OK, adt.DSPARK_ERR_ARG, adt.DSPARK_ERR_UNSUPPORTED,
+                 adt.DSPARK_ERR_WORKSPACE, adt.DSPARK_ERR_HIP):
+        assert adt.status_string(code) and adt.status_string(code) != "unknown status"
+    assert adt.status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    small = adt.dspark_workspace_bytes(1, 7, 4096, 32)
+    big = adt.dspark_workspace_bytes(96, 7, 200064, 256)
+    assert 0 < small < big
+    # partials for 1563 chunks of 96 rows (16 B each), plus stats and the embedding rows
+    assert big >= 96 * 1563 * 16 + 96 * 7 * 8 + 96 * 256 * 2
+    assert big < 8 << 20
+    assert adt.dspark_workspace_bytes(1, 7, 4100, 32) == 0      # V % 8 != 0
+    assert adt.dspark_workspace_bytes(1, 7, 4096, 48) == 0      # r % 32 != 0
+    assert adt.dspark_workspace_bytes(1, 7, 4096, 2048) == 0    # r > 1024
+    assert adt.dspark_workspace_bytes(1, 256, 4096, 32) == 0    # K > 255
+    assert adt.dspark_workspace_bytes(-1, 7, 4096, 32) == 0
+
+
+FAKE = 1 << 20          # a 16-byte aligned address that is never dereferenced
+
+
+def call(**kw):
+    args = dict(base_logits=FAKE, base_dtype=adt.DSPARK_F32, E=FAKE, W=FAKE, prev_token=FAKE,
+                seed=FAKE, offset=FAKE, temperature=FAKE, n_real=None, B=2, K=7, V=4096, r=32,
+                tokens=FAKE, logits_f32=FAKE, draft_probs=FAKE, workspace=FAKE,
+                workspace_bytes=adt.dspark_workspace_bytes(2, 7, 4096, 32), stream=0, check=False)
+    args.update(kw)
+    return adt.dspark_draft_block(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=4100), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(r=48), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(K=300), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(B=-1), adt.DSPARK_ERR_ARG),
+    (dict(V=0), adt.DSPARK_ERR_ARG),
+    (dict(base_dtype=7), adt.DSPARK_ERR_ARG),
+    (dict(base_logits=None), adt.DSPARK_ERR_ARG),
+    (dict(E=None), adt.DSPARK_ERR_ARG),
+    (dict(W=None), adt.DSPARK_ERR_ARG),
+    (dict(prev_token=None), adt.DSPARK_ERR_ARG),
+    (dict(seed=None), adt.DSPARK_ERR_ARG),
+    (dict(offset=None), adt.DSPARK_ERR_ARG),
+    (dict(temperature=None), adt.DSPARK_ERR_ARG),
+    (dict(tokens=None), adt.DSPARK_ERR_ARG),
+    (dict(logits_f32=None), adt.DSPARK_ERR_ARG),
+    (dict(draft_probs=None), adt.DSPARK_ERR_ARG),
+    (dict(base_logits=FAKE + 4), adt.DSPARK_ERR_ARG),
+    (dict(W=FAKE + 2), adt.DSPARK_ERR_ARG),
+    (dict(draft_probs=FAKE + 8), adt.DSPARK_ERR_ARG),
+    (dict(workspace=None), adt.DSPARK_ERR_WORKSPACE),
+    (dict(workspace_bytes=100), adt.DSPARK_ERR_WORKSPACE),
+])
+def test_host_checks(lib, kw, status):
+    assert call(**kw) == status
+
+
+def test_bad_chunking(lib):
+    assert call(chunk_cols=100) == adt.DSPARK_ERR_UNSUPPORTED
+    assert call(chunk_cols=-128) == adt.DSPARK_ERR_UNSUPPORTED
+
+
+def test_empty_block_enqueues_nothing(lib):
+    assert call(B=0, tokens=None, logits_f32=None, draft_probs=None, workspace=None) == adt.DSPARK_OK
+    assert call(K=0, tokens=None, logits_f32=None, draft_probs=None, workspace=None) == adt.DSPARK_OK
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(adt.DSparkError):
+        call(V=4100, check=True)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(adt, "_lib", None)
+    with pytest.raises(RuntimeError):
+        adt.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,132 @@
+"""GPU path vs the CPU oracle, through the C ABI.
+
+Small cases compare every output entry; the full-size workloads (V = 200064,
+r = 256, the launch configuration the benchmark times) run every row on the
+GPU and compare sampled rows with the oracle at full width, plus properties
+that hold for every row (legal tokens, rows of q summing to 1, one-hot greedy
+proposals).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from ancestral_draft_token_amd import inputs
+from oracle import parity
+
+from gpu_util import require_gpu, rows_to_host, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def full_check(w, chunk_cols=None):
+    p = run_gpu(w, chunk_cols=chunk_cols)
+    tokens, logits, q = p.outputs()
+    rep = parity.check(w, tokens, logits, q)
+    say(f"parity ok {rep.as_dict()}")
+    return p, rep
+
+
+# ---------------------------------------------------------------------------
+# small cases: every entry
+# ---------------------------------------------------------------------------
+
+def test_tiny_reference():
+    full_check(inputs.tiny())
+
+
+@pytest.mark.parametrize("chunk_cols", [4096, 1408, 128, 256])
+def test_tiny_chunkings(chunk_cols):
+    """One and three vocabulary chunks (4096 and 1408 columns), and the finest ones."""
+    full_check(inputs.tiny(), chunk_cols=chunk_cols)
+
+
+def test_tiny_bf16_base():
+    full_check(inputs.tiny(base_dtype="bf16"))
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=5, K=3, V=1000, r=64, temperature=lambda b: [1.0, 0.0, 0.7, 2.5, 0.0][b], n_real=4),
+    dict(B=9, K=2, V=8, r=32, temperature=0.9),
+    dict(B=3, K=1, V=2056, r=96, temperature=0.0),
+    dict(B=6, K=4, V=3320, r=32, temperature=1.3, base_dtype="bf16", n_real=2, pad_base="nan"),
+    dict(B=17, K=2, V=264, r=128, temperature=lambda b: 0.5 + 0.1 * (b % 3)),
+])
+def test_ragged_shapes(case):
+    w = inputs.tiny(fixed_seed=None, fixed_offset=None, data_seed=99, **case)
+    full_check(w)
+
+
+def test_prev_token_out_of_range_is_clamped():
+    w = inputs.tiny(B=3, K=3, fixed_seed=None, fixed_offset=None)
+    w.prev_token[:] = [-7, w.V, 2**30]
+    full_check(w)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled rows at full width + properties on all rows
+# ---------------------------------------------------------------------------
+
+FULL = {
+    "b1": (inputs.single_request, [0]),
+    "b8": (inputs.small_batch, [0, 5]),
+    "b44": (inputs.mixed_batch, [0, 1, 43]),
+    "b88": (inputs.large_padded, [0, 87, 88, 95]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size(name):
+    make, rows = FULL[name]
+    w = make()
+    p = run_gpu(w)
+    import torch
+    tok = p.tokens
+    assert bool(((tok >= 0) & (tok < w.V)).all())
+    sums = p.q.double().sum(dim=-1)
+    assert float((sums - 1.0).abs().max()) <= parity.Q_SUM_ATOL
+    greedy = torch.from_numpy(~(w.temperature > 0)).to(tok.device)
+    if bool(greedy.any()):
+        gq = p.q[greedy]
+        assert bool((gq.gather(-1, tok[greedy].long().unsqueeze(-1)) == 1.0).all())
+        assert float(gq.sum()) == float(gq.shape[0] * gq.shape[1])
+    sub, order = w.subset_rows(rows)
+    t, l, q = rows_to_host(p, order)
+    say(f"oracle on rows {list(order)} of {name}")
+    rep = parity.check(sub, t, l, q)
+    say(f"parity ok {name} {rep.as_dict()}")
+
+
+def test_full_size_padding_rows_ignore_nan_base():
+    w0 = inputs.large_padded()
+    wn = inputs.large_padded(pad_base="nan")
+    assert np.isnan(wn.base[88:]).all()
+    p0 = run_gpu(w0)
+    pn = run_gpu(wn)
+    assert bool((p0.tokens == pn.tokens).all())
+    assert bool(torch_equal(p0.logits, pn.logits))
+    assert bool(torch_equal(p0.q, pn.q))
+    assert bool(pn.q[88:].isfinite().all())
+
+
+def torch_equal(a, b):
+    import torch
+    return torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n_chunks", [1, 3])
+def test_full_size_chunk_count_invariance(n_chunks):
+    """Tokens and logits are bitwise independent of the chunking; q within 1e-6."""
+    w = inputs.small_batch()
+    ref = run_gpu(w)
+    chunk = -(-(w.V // 128) // n_chunks) * 128
+    alt = run_gpu(w, chunk_cols=chunk)
+    assert bool((ref.tokens == alt.tokens).all())
+    assert torch_equal(ref.logits, alt.logits)
+    assert float((ref.q - alt.q).abs().max()) <= parity.Q_ATOL
