@@ -9,9 +9,11 @@ base logits -- the drafting-alone setup of the pages ("brb-nv/TensorRT-LLM
 pull 27", section "Commits 1-2: fixed-shape decode", drafting-alone table).
 
 MALL ("cold", the default): before every timed replay a 1 GiB buffer is
-written, outside the timed region, so W (102 MB) does not start in the
-256 MB Infinity Cache -- as after a target-model forward in serving. "warm"
-replays back to back. A step's time is the HIP-event time of its replay.
+read, outside the timed region, so W (102 MB) does not start in the 256 MB
+Infinity Cache -- as after a target-model forward, which mostly reads
+weights. (A flush that writes would leave dirty lines whose write-back the
+next kernel pays for.) "warm" replays back to back. A step's time is the
+HIP-event time of its replay.
 
 Prints ONE JSON line (rank 0, N=1).
 """
@@ -58,7 +60,8 @@ class Bench:
         self.mall = mall
         self.p = DeviceProblem(w)
         self.stream = torch.cuda.Stream()
-        self.flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        self.flush_buf = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda:0")
+        self.flush_out = torch.empty((), dtype=torch.float32, device="cuda:0")
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
         self.stream.wait_stream(torch.cuda.current_stream())
@@ -71,7 +74,8 @@ class Bench:
 
     def flush(self):
         if self.mall == "cold":
-            self.flush_buf.fill_(1)
+            torch = self.torch
+            torch.amax(self.flush_buf, dim=0, out=self.flush_out)   # reads 1 GiB
 
     def steps(self, n):
         """n timed replays; returns per-replay microseconds (HIP events on the replay stream)."""
@@ -91,25 +95,27 @@ class Bench:
         """Eager blocks with an event after every launch: mean us per launch of each kernel."""
         torch = self.torch
         from ancestral_draft_token_amd.hip_events import EventSet
-        K = self.w.K
-        fused, pick, prop = [], [], []
-        ev = EventSet(2 * K + 2)
+        w = self.w
+        K = w.K
+        # launch order (include/dspark.h): at B == 1 the K fused kernels pick the
+        # previous token themselves; otherwise each is followed by pick_and_gather
+        fused_pick = w.B == 1 and -(-w.V // 128) <= 2048
+        names = (["markov_bias_gumbel_argmax"] * K if fused_pick
+                 else ["markov_bias_gumbel_argmax", "pick_and_gather"] * K) + ["proposal_softmax"]
+        times = {n: [] for n in names}
+        ev = EventSet(len(names) + 1)
         try:
             for _ in range(reps):
                 with torch.cuda.stream(self.stream):
                     self.flush()
                     self.p.enqueue(stream=self.stream, events=ev.handles, chunk_cols=None)
                 ev.synchronize()
-                for k in range(K):
-                    fused.append(ev.elapsed_ms(2 * k, 2 * k + 1) * 1e3)
-                    pick.append(ev.elapsed_ms(2 * k + 1, 2 * k + 2) * 1e3)
-                prop.append(ev.elapsed_ms(2 * K, 2 * K + 1) * 1e3)
+                for i, n in enumerate(names):
+                    times[n].append(ev.elapsed_ms(i, i + 1) * 1e3)
         finally:
             torch.cuda.synchronize()
             ev.close()
-        return {"markov_bias_gumbel_argmax": statistics.mean(fused),
-                "pick_and_gather": statistics.mean(pick),
-                "proposal_softmax": statistics.mean(prop)}
+        return {n: statistics.mean(v) for n, v in times.items()}
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -166,8 +172,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the sampler has no multi-GPU path in this build "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the draft-block sampler is built and measured on "
+              "a single GPU (its multi-GPU sharding is a design, not code); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -125,11 +125,14 @@ int dspark_draft_block_chunked(
 
 /* The default-chunked block with timing marks, for measurement: events[0]
  * is recorded on `stream` before the first launch and events[i + 1] after
- * the i-th launch, in launch order (position k's fused kernel is launch 2k,
- * its pick_and_gather launch 2k + 1, the proposal kernel launch 2K), so
- * n_events must be at least 2K + 2. The events are caller-created
- * hipEvent_t handles passed as void*. Returns DSPARK_ERR_ARG if events is
- * NULL or too short; otherwise as dspark_draft_block. */
+ * the i-th launch, in launch order. With B == 1 (and at most 2048 vocabulary
+ * chunks) the block is K + 1 launches: the K fused per-position kernels, then
+ * the proposal kernel (each fused kernel picks the previous position's token
+ * itself). Otherwise it is 2K + 1 launches: each fused kernel followed by its
+ * pick_and_gather, then the proposal kernel. n_events must be at least the
+ * launch count plus one; the events are caller-created hipEvent_t handles
+ * passed as void*. Returns DSPARK_ERR_ARG if events is NULL or too short;
+ * otherwise as dspark_draft_block. */
 int dspark_draft_block_events(
     const void* base_logits, int base_dtype,
     const uint16_t* E, const uint16_t* W,
