@@ -27,7 +27,11 @@ DSPARK_ERR_WORKSPACE = -3
 DSPARK_ERR_HIP = -4
 
 EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
-            "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_status_string")
+            "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_launch_plan",
+            "dspark_status_string")
+
+LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
+                3: "resident_clear", 4: "markov_bias_gumbel_argmax"}
 
 _lib = None
 
@@ -62,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_draft_block_chunked.restype = I
     lib.dspark_draft_block_events.argtypes = block_args + out_args + [P, I]
     lib.dspark_draft_block_events.restype = I
+    lib.dspark_launch_plan.argtypes = [I, I, I, I, P, I]
+    lib.dspark_launch_plan.restype = I
     lib.dspark_status_string.argtypes = [I]
     lib.dspark_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -80,6 +86,16 @@ def dspark_init() -> None:
 
 def dspark_workspace_bytes(B: int, K: int, V: int, r: int) -> int:
     return int(load_library().dspark_workspace_bytes(B, K, V, r))
+
+
+def dspark_launch_plan(B: int, K: int, V: int, r: int):
+    """The launch kinds (ints) one block enqueues on the current device, in order."""
+    lib = load_library()
+    kinds = (ctypes.c_int * (2 * K + 4))()
+    n = lib.dspark_launch_plan(B, K, V, r, kinds, len(kinds))
+    if n < 0:
+        raise DSparkError(n, "dspark_launch_plan")
+    return [int(kinds[i]) for i in range(n)]
 
 
 def _ptr(t) -> Optional[int]:

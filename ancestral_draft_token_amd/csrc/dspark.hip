@@ -154,19 +154,24 @@ struct RowState {
   uint32_t key0, key1, ctr2, ctr3;
 };
 
-__device__ __forceinline__ RowState row_state(const StepArgs& a, int b, int n_real) {
+__device__ __forceinline__ RowState row_state(const float* temperature, const int64_t* seed,
+                                              const int64_t* offset, int b, int n_real) {
   RowState rs;
-  const float T = a.temperature[b];
+  const float T = temperature[b];
   rs.greedy = !(T > 0.0f);
   rs.invT = rs.greedy ? 0.0f : __fdiv_rn(1.0f, T);
   rs.pad = b >= n_real;
-  const uint64_t sd = (uint64_t)a.seed[b];
-  const uint64_t of = (uint64_t)a.offset[b];
+  const uint64_t sd = (uint64_t)seed[b];
+  const uint64_t of = (uint64_t)offset[b];
   rs.key0 = (uint32_t)sd;
   rs.key1 = (uint32_t)(sd >> 32);
   rs.ctr2 = (uint32_t)of;
   rs.ctr3 = (uint32_t)(of >> 32);
   return rs;
+}
+
+__device__ __forceinline__ RowState row_state(const StepArgs& a, int b, int n_real) {
+  return row_state(a.temperature, a.seed, a.offset, b, n_real);
 }
 
 // Base logits of 4 consecutive columns, loaded early and widened late.
@@ -602,10 +607,12 @@ struct PropArgs {
   Stat* row_stat;
   const uint64_t* last_key;   // [B,C] partials of position K-1 (last_from_partials)
   const Stat* last_stat;
+  const Stat* part_stat;      // [K,B,n_part] per-workgroup statistics (n_part > 0)
   float* q;
   int B, K, V, n_chunks;
   int blocks_per_row;
   int last_from_partials;
+  int n_part;
 };
 
 __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
@@ -635,6 +642,15 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
       a.tokens[bk] = tok;
       a.row_stat[bk] = st;
     }
+  } else if (a.n_part > 0) {
+    // the resident kernel leaves one statistics partial per workgroup
+    Stat sst{-INFINITY, 0.0f};
+    uint64_t unused = 0;
+    const Stat* ps = a.part_stat + ((size_t)k * a.B + b) * a.n_part;
+    for (int i = threadIdx.x; i < a.n_part; i += kThreads) sst = stat_merge(sst, ps[i]);
+    wg_reduce(unused, sst, s_key, s_stat);
+    st = sst;
+    tok = a.tokens[bk];
   } else {
     st = a.row_stat[bk];
     tok = a.tokens[bk];
@@ -658,6 +674,458 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Resident path (B <= 4): one persistent launch runs all K positions, and each
+// workgroup keeps its slice of W on chip for the whole block, so W is read
+// from HBM once per block instead of once per position.
+//
+// One 512-thread workgroup per compute unit owns up to 784 vocabulary columns
+// (98 groups of 8). A (group, rank slice of 32 rows) unit holds 8 columns x 16
+// bf16 pairs (rows 2p, 2p+1 packed in one dword); groups 0..63 live in VGPRs
+// (thread = one unit), groups 64..97 in LDS. The bias GEMV is v_dot2 of those
+// pairs with the embedding pairs, then a reduce-scatter over the 8 rank
+// slices leaves each lane 4 consecutive columns of one row, so one Philox
+// block serves its epilogue. Positions are separated by an exchange: each
+// workgroup publishes its per-row argmax partial as one 64-bit word tagged
+// with the position, and every workgroup polls all words (a bounded wait)
+// and reduces them in the same order, so all agree on d_k. The Gumbel noise
+// and base logits of position k+1 do not depend on d_k and are prepared while
+// the exchange is in flight.
+// ---------------------------------------------------------------------------
+constexpr int kResThreads = 512;
+constexpr int kResWaves = kResThreads / 64;
+constexpr int kResSlice = 784;                             // max columns per workgroup
+constexpr int kResGroups = kResSlice / 8;                  // 98 groups of 8 columns
+constexpr int kResRegGroups = kResWaves * 8;               // 64 groups in VGPRs
+constexpr int kResLdsUnits = (kResGroups - kResRegGroups) * 8;  // 272 units in LDS
+constexpr int kResRank = 256;                              // 8 rank slices of 32 rows
+constexpr int kResPairs = 16;                              // bf16 pairs per unit column
+constexpr int kResRowsMax = 4;
+constexpr size_t kResLdsW = (size_t)kResPairs * kResLdsUnits * 32;   // 139,264 bytes
+constexpr size_t kResLdsE = (size_t)kResRowsMax * kResRank * 2;      // 2,048 bytes
+constexpr size_t kResLdsBytes = kResLdsW + kResLdsE;
+constexpr int kResTagShift = 50;                           // word: tag | ord(z) | index
+constexpr uint64_t kResIdxMask = (1ull << 18) - 1;         // V <= 2^18
+constexpr int kResMaxCUs = 1024;
+
+struct ResArgs {
+  const void* base;
+  const uint16_t* E;
+  const uint16_t* W;
+  const int32_t* prev_token;
+  const int64_t* seed;
+  const int64_t* offset;
+  const float* temperature;
+  const int32_t* n_real;
+  float* logits;
+  int32_t* tokens;
+  uint64_t* xkey;      // [2][G][kResRowsMax] tagged exchange words, zeroed by res_clear
+  Stat* stat_part;     // [K][B][G] per-workgroup softmax statistics
+  int* fail;           // set when a bounded device wait expires
+  int B, K, V, r, slice;
+  unsigned spin_limit;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t e, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, e),
+                                        acc, false);
+}
+
+// (a.lo16, b.lo16) and (a.hi16, b.hi16): bf16 pairs of two rank rows
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+// rows 2p (x) and 2p+1 (y), 8 columns each -> 8 column pairs
+__device__ __forceinline__ void pack_pairs(uint4 x, uint4 y, uint32_t out[8]) {
+  out[0] = pair_lo(x.x, y.x); out[1] = pair_hi(x.x, y.x);
+  out[2] = pair_lo(x.y, y.y); out[3] = pair_hi(x.y, y.y);
+  out[4] = pair_lo(x.z, y.z); out[5] = pair_hi(x.z, y.z);
+  out[6] = pair_lo(x.w, y.w); out[7] = pair_hi(x.w, y.w);
+}
+
+__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reduce-scatter of acc[RB][8] over the 8 rank-slice lanes of a column group
+// (lanes differing in bits 0..2): lane js ends with the sums of 4 columns
+// (4 * (js & 1) ..) of row er (RB = 4: js >> 1; RB = 2: js >> 2; RB = 1: 0).
+template <int RB>
+__device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js, float bias[4]) {
+  const int b0 = js & 1, b1 = (js >> 1) & 1, b2 = (js >> 2) & 1;
+  float h2[8];
+  if (RB == 4) {
+    float h[2][8];
+#pragma unroll
+    for (int r0 = 0; r0 < 2; ++r0)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float keep = b2 ? acc[(2 + r0) % RB][c] : acc[r0 % RB][c];
+        const float send = b2 ? acc[r0 % RB][c] : acc[(2 + r0) % RB][c];
+        h[r0][c] = __fadd_rn(keep, __shfl_xor(send, 4, 64));
+      }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float keep = b1 ? h[1][c] : h[0][c];
+      const float send = b1 ? h[0][c] : h[1][c];
+      h2[c] = __fadd_rn(keep, __shfl_xor(send, 2, 64));
+    }
+  } else if (RB == 2) {
+    float h[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float keep = b2 ? acc[1 % RB][c] : acc[0][c];
+      const float send = b2 ? acc[0][c] : acc[1 % RB][c];
+      h[c] = __fadd_rn(keep, __shfl_xor(send, 4, 64));
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], __shfl_xor(h[c], 2, 64));
+  } else {
+    float h[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) h[c] = __fadd_rn(acc[0][c], __shfl_xor(acc[0][c], 4, 64));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], __shfl_xor(h[c], 2, 64));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b0 ? h2[4 + i] : h2[i];
+    const float send = b0 ? h2[i] : h2[4 + i];
+    bias[i] = __fadd_rn(keep, __shfl_xor(send, 1, 64));
+  }
+}
+
+// Gumbel noise of the 4 columns v0..v0+3 at position k.
+__device__ __forceinline__ void noise4(const RowState& rs, int k, uint32_t v0, float g[4]) {
+  const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
+  g[0] = gumbel_from_bits(x.x);
+  g[1] = gumbel_from_bits(x.y);
+  g[2] = gumbel_from_bits(x.z);
+  g[3] = gumbel_from_bits(x.w);
+}
+
+// The epilogue of 4 columns with the noise already drawn (same arithmetic as epilogue4).
+__device__ __forceinline__ void epilogue4_noise(const RowState& rs, uint32_t v0, const float base[4],
+                                                const float bias[4], const float g[4], float* logits_out,
+                                                uint64_t& best, Stat& st) {
+  float lg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(base[i], bias[i]);
+  *reinterpret_cast<float4*>(logits_out) = make_float4(lg[0], lg[1], lg[2], lg[3]);
+  if (rs.greedy) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) best = umax64(best, score_key(lg[i], v0 + i));
+    return;
+  }
+  float s[4];
+  float m4 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = __fmul_rn(lg[i], rs.invT);
+    const float z = __fadd_rn(s[i], g[i]);
+    best = umax64(best, score_key(z, v0 + i));
+    m4 = fmaxf(m4, s[i]);
+  }
+  float l4 = 0.0f;
+  if (m4 != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l4 = __fadd_rn(l4, __expf(__fsub_rn(s[i], m4)));
+  }
+  st = stat_merge(st, Stat{m4, l4});
+}
+
+template <int RB, bool kBf16Base>
+__global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resident(ResArgs a) {
+  extern __shared__ __align__(16) unsigned char res_lds[];
+  uint32_t* lds_w = reinterpret_cast<uint32_t*>(res_lds);               // [16][272][8]
+  uint32_t* lds_e = reinterpret_cast<uint32_t*>(res_lds + kResLdsW);    // [RB][128] bf16 pairs
+  __shared__ uint64_t s_key[kResWaves][RB];
+  __shared__ Stat s_stat[kResWaves][RB];
+  __shared__ uint64_t s_x[kResWaves][RB];
+  __shared__ int s_fail;
+
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int V = a.V, r = a.r, K = a.K, B = a.B;
+  const int js = lane & 7;                    // rank slice: rows 32 js .. 32 js + 31
+  const bool j_ok = 32 * js < r;
+  const int col0 = g * a.slice;
+  const int ncols = max(0, min(a.slice, V - col0));
+  const int ngroups = ncols / 8;
+  const int cg_r = 8 * wv + (lane >> 3);      // this thread's VGPR unit: column group
+  const bool reg_ok = cg_r < ngroups;
+  const int n_lds_units = max(0, ngroups - kResRegGroups) * 8;
+  const bool lds_ok = t < n_lds_units;        // this thread's LDS unit (if any) is unit t
+  const int cg_l = kResRegGroups + (t >> 3);
+  const int n_real = a.n_real ? *a.n_real : B;
+
+  // epilogue lane mapping after the reduce-scatter
+  const int er = RB == 4 ? (js >> 1) : RB == 2 ? (js >> 2) : 0;
+  const int eh = js & 1;
+  const bool e_act = (RB == 4 ? true : RB == 2 ? ((js >> 1) & 1) == 0 : js < 2) && er < B;
+
+  // row states (uniform scalar loads) and this lane's row
+  RowState rows[RB];
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr)
+    rows[rr] = rr < B ? row_state(a.temperature, a.seed, a.offset, rr, n_real) : RowState{};
+  RowState rs = rows[0];
+#pragma unroll
+  for (int rr = 1; rr < RB; ++rr)
+    if (er == rr) rs = rows[rr];
+  if (t == 0) s_fail = 0;
+
+  const uint32_t v_r = (uint32_t)(col0 + 8 * cg_r + 4 * eh);   // epilogue columns, VGPR unit
+  const uint32_t v_l = (uint32_t)(col0 + 8 * cg_l + 4 * eh);   // epilogue columns, LDS unit
+  const bool ep_r = e_act && reg_ok;
+  const bool ep_l = e_act && lds_ok;
+
+  // ---- (1) this thread's VGPR unit of W: 32 rank rows x 8 columns, 8 rows per
+  // batch (512 threads x 8 x 16 B = 64 KB in flight per workgroup)
+  uint32_t wr[8][kResPairs];
+  {
+    const bool ok = reg_ok && j_ok;
+    const uint16_t* src = a.W + (ok ? (size_t)(32 * js) * V + col0 + 8 * cg_r : 0);
+    const size_t stride = ok ? (size_t)V : 0;
+#pragma unroll
+    for (int b8 = 0; b8 < 4; ++b8) {
+      uint4 raw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (8 * b8 + i) * stride);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        uint32_t pr[8];
+        pack_pairs(raw[2 * pp], raw[2 * pp + 1], pr);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) wr[c][4 * b8 + pp] = pr[c];
+      }
+    }
+  }
+
+  // ---- (2) noise and base logits of a position for this lane's epilogue quads
+  float gq[2][4];
+  Base4<kBf16Base> bq[2];
+  auto prepare = [&](int k) {
+    if (e_act && !rs.greedy) {
+      noise4(rs, k, v_r, gq[0]);
+      if (lds_ok) noise4(rs, k, v_l, gq[1]);
+    }
+    const size_t row_off = ((size_t)er * K + k) * (size_t)V;
+    const bool br = ep_r && !rs.pad, bl = ep_l && !rs.pad;
+    load_base4<kBf16Base>(bq[0], a.base, br ? row_off + v_r : 0);
+    load_base4<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
+  };
+
+  // ---- (3) the LDS units of W, 8 rank rows at a time
+  if (lds_ok) {
+    const uint16_t* src = a.W + (j_ok ? (size_t)(32 * js) * V + col0 + 8 * cg_l : 0);
+    const size_t stride = j_ok ? (size_t)V : 0;
+#pragma unroll
+    for (int b8 = 0; b8 < 4; ++b8) {
+      uint4 raw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (8 * b8 + i) * stride);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        uint32_t pr[8];
+        pack_pairs(raw[2 * pp], raw[2 * pp + 1], pr);
+        uint4* dst = reinterpret_cast<uint4*>(lds_w + ((size_t)(4 * b8 + pp) * kResLdsUnits + t) * 8);
+        dst[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+        dst[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+      }
+    }
+  }
+
+  // ---- (4) embedding rows of position 0: E[clamp(prev_token)]
+  auto gather_e = [&](const int* d) {
+    const uint32_t* E32 = reinterpret_cast<const uint32_t*>(a.E);
+    for (int i = t; i < RB * (kResRank / 2); i += kResThreads) {
+      const int rr = i / (kResRank / 2), jj = i % (kResRank / 2);
+      uint32_t v = 0u;
+      if (rr < B && jj < r / 2) v = E32[(size_t)d[rr] * (r / 2) + jj];
+      lds_e[rr * (kResRank / 2) + jj] = v;
+    }
+  };
+  {
+    int d0[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) d0[rr] = rr < B ? clamp_token(a.prev_token[rr], V) : 0;
+    gather_e(d0);
+  }
+  prepare(0);
+  __syncthreads();
+
+  for (int k = 0; k < K; ++k) {
+    // ---- bias GEMV: VGPR unit, then LDS unit; reduce-scatter over the rank slices
+    float bias_r[4], bias_l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      float acc[RB][8];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[rr][c] = 0.0f;
+      if (j_ok) {
+#pragma unroll
+        for (int pq = 0; pq < kResPairs / 4; ++pq) {
+          uint4 e4[RB];
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+            e4[rr] = *reinterpret_cast<const uint4*>(lds_e + rr * (kResRank / 2) + 16 * js + 4 * pq);
+#pragma unroll
+          for (int p4 = 0; p4 < 4; ++p4) {
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+              const uint32_t e = p4 == 0 ? e4[rr].x : p4 == 1 ? e4[rr].y : p4 == 2 ? e4[rr].z : e4[rr].w;
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[rr][c] = dot2_bf16(wr[c][4 * pq + p4], e, acc[rr][c]);
+            }
+          }
+        }
+      }
+      reduce_scatter<RB>(acc, js, bias_r);
+    }
+    if (lds_ok) {   // whole groups of 8 lanes take this branch together
+      float acc[RB][8];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[rr][c] = 0.0f;
+      if (j_ok) {
+#pragma unroll
+        for (int pq = 0; pq < kResPairs / 4; ++pq) {
+          uint4 e4[RB];
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+            e4[rr] = *reinterpret_cast<const uint4*>(lds_e + rr * (kResRank / 2) + 16 * js + 4 * pq);
+#pragma unroll
+          for (int p4 = 0; p4 < 4; ++p4) {
+            const int p = 4 * pq + p4;
+            const uint4* src = reinterpret_cast<const uint4*>(lds_w + ((size_t)p * kResLdsUnits + t) * 8);
+            const uint4 w0 = src[0], w1 = src[1];
+            const uint32_t wl[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+              const uint32_t e = p4 == 0 ? e4[rr].x : p4 == 1 ? e4[rr].y : p4 == 2 ? e4[rr].z : e4[rr].w;
+#pragma unroll
+              for (int c = 0; c < 8; ++c) acc[rr][c] = dot2_bf16(wl[c], e, acc[rr][c]);
+            }
+          }
+        }
+      }
+      reduce_scatter<RB>(acc, js, bias_l);
+    }
+
+    // ---- epilogue of the lane's quads
+    uint64_t best = 0;
+    Stat st{-INFINITY, 0.0f};
+    {
+      float* out = a.logits + ((size_t)er * K + k) * (size_t)V;
+      if (ep_r) {
+        float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!rs.pad) widen_base4<kBf16Base>(bq[0], base);
+        epilogue4_noise(rs, v_r, base, bias_r, gq[0], out + v_r, best, st);
+      }
+      if (ep_l) {
+        float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!rs.pad) widen_base4<kBf16Base>(bq[1], base);
+        epilogue4_noise(rs, v_l, base, bias_l, gq[1], out + v_l, best, st);
+      }
+    }
+
+    // ---- this workgroup's partial per row: lanes, then waves in order
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      uint64_t kk = (er == rr) ? best : 0ull;
+      Stat ss = (er == rr) ? st : Stat{-INFINITY, 0.0f};
+      reduce_lanes(kk, ss, 64);
+      if (lane == 0) {
+        s_key[wv][rr] = kk;
+        s_stat[wv][rr] = ss;
+      }
+    }
+    __syncthreads();
+    if (t < B) {
+      uint64_t kk = s_key[0][t];
+      Stat ss = s_stat[0][t];
+#pragma unroll
+      for (int w = 1; w < kResWaves; ++w) {
+        kk = umax64(kk, s_key[w][t]);
+        ss = stat_merge(ss, s_stat[w][t]);
+      }
+      a.stat_part[((size_t)k * B + t) * G + g] = ss;
+      // a workgroup without columns has no candidate (kk == 0): it publishes the
+      // tag alone, which every real candidate beats
+      const uint64_t ord = kk >> 32;
+      const uint64_t idx = kk ? kResIdxMask - (uint64_t)key_token(kk) : 0ull;
+      const uint64_t word = ((uint64_t)(k + 1) << kResTagShift) | (ord << 18) | idx;
+      st_agent_u64(a.xkey + ((size_t)(k & 1) * G + g) * kResRowsMax + t, word);
+    }
+
+    // ---- position k+1's noise and base do not depend on d_k: prepare them now
+    if (k + 1 < K) prepare(k + 1);
+
+    // ---- exchange: every workgroup's word for every row. Thread t polls row
+    // t % RB (RB is a power of two dividing the thread count) of workgroups
+    // t / RB, t / RB + 512 / RB, ...; rows >= B are padding and not polled.
+    uint64_t xb = 0;
+    bool failed = false;
+    const int xr = t % RB;
+    if (xr < B) {
+      for (int gg = t / RB; gg < G; gg += kResThreads / RB) {
+        const uint64_t* pw = a.xkey + ((size_t)(k & 1) * G + gg) * kResRowsMax + xr;
+        uint64_t w = ld_agent_u64(pw);
+        unsigned spins = 0;
+        while ((int)(w >> kResTagShift) != k + 1) {
+          if (++spins > a.spin_limit) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          w = ld_agent_u64(pw);
+        }
+        xb = umax64(xb, w);
+      }
+    }
+    if (failed) {
+      s_fail = 1;
+      atomicExch(a.fail, 1);
+    }
+    // lanes of the same row (equal t % RB) combine: xor over the bits above log2(RB)
+    for (int mask = RB; mask < 64; mask <<= 1) xb = umax64(xb, shfl_xor_u64(xb, mask, 64));
+    if (lane < RB) s_x[wv][lane] = xb;
+    __syncthreads();
+    if (s_fail) {
+      if (g == 0 && t < B)
+        for (int kk = k; kk < K; ++kk) a.tokens[(size_t)t * K + kk] = -1;
+      return;
+    }
+    int d[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      uint64_t x = s_x[0][rr];
+#pragma unroll
+      for (int w = 1; w < kResWaves; ++w) x = umax64(x, s_x[w][rr]);
+      d[rr] = clamp_token((int)(kResIdxMask - (x & kResIdxMask)), V);
+    }
+    if (g == 0 && t < B) a.tokens[(size_t)t * K + k] = d[t % RB];
+    if (k + 1 < K) {
+      gather_e(d);
+      __syncthreads();
+    }
+  }
+}
+
+// Zero the exchange words and the failure flag before a resident launch.
+__global__ __launch_bounds__(kThreads) void res_clear(uint64_t* xkey, int n, int* fail) {
+  for (int i = threadIdx.x + blockIdx.x * kThreads; i < n; i += kThreads * gridDim.x) xkey[i] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *fail = 0;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Workspace {
@@ -665,11 +1133,15 @@ struct Workspace {
   Stat* part_stat[2];
   Stat* row_stat;
   uint16_t* e_buf;
+  uint64_t* xkey;          // resident path: [2][kResMaxCUs][kResRowsMax]
+  Stat* stat_part;         // resident path: [K][B][kResMaxCUs]
+  int* fail;               // resident path: bounded-wait failure flag
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Layout for the largest chunk count (chunk = 128 columns).
+// Layout for the largest chunk count (chunk = 128 columns), plus the resident
+// path's exchange words and per-workgroup statistics when B <= 4.
 inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* base) {
   const size_t max_chunks = (size_t)(V + kTile - 1) / kTile;
   size_t off = 0;
@@ -680,6 +1152,12 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
   }
   const size_t o_rst = off; off = align_up(off + (size_t)B * K * sizeof(Stat), 256);
   const size_t o_e = off;   off = align_up(off + (size_t)B * r * sizeof(uint16_t), 256);
+  size_t o_x = 0, o_sp = 0, o_f = 0;
+  if (B <= kResRowsMax) {
+    o_x = off;  off = align_up(off + (size_t)2 * kResMaxCUs * kResRowsMax * sizeof(uint64_t), 256);
+    o_sp = off; off = align_up(off + (size_t)K * B * kResMaxCUs * sizeof(Stat), 256);
+    o_f = off;  off = align_up(off + sizeof(int), 256);
+  }
   if (ws) {
     for (int i = 0; i < 2; ++i) {
       ws->part_key[i] = reinterpret_cast<uint64_t*>(base + o_key[i]);
@@ -687,8 +1165,50 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
     }
     ws->row_stat = reinterpret_cast<Stat*>(base + o_rst);
     ws->e_buf = reinterpret_cast<uint16_t*>(base + o_e);
+    ws->xkey = B <= kResRowsMax ? reinterpret_cast<uint64_t*>(base + o_x) : nullptr;
+    ws->stat_part = B <= kResRowsMax ? reinterpret_cast<Stat*>(base + o_sp) : nullptr;
+    ws->fail = B <= kResRowsMax ? reinterpret_cast<int*>(base + o_f) : nullptr;
   }
   return off;
+}
+
+// Per-device facts the resident path needs (filled by dspark_init).
+struct DeviceInfo {
+  bool ready;
+  bool resident_ok;   // one 512-thread workgroup with kResLdsBytes of LDS fits on every CU
+  int cus;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+
+template <int RB, bool kBf16>
+bool prepare_resident_kernel() {
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident<RB, kBf16>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResLdsBytes) != hipSuccess)
+    return false;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident<RB, kBf16>,
+                                                   kResThreads, kResLdsBytes) != hipSuccess)
+    return false;
+  return occ >= 1;
+}
+
+int init_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_HIP;
+  DeviceInfo& info = g_devices[dev];
+  if (info.ready) return DSPARK_OK;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  bool ok = cus > 0 && cus <= kResMaxCUs;
+  ok = ok && prepare_resident_kernel<1, false>() && prepare_resident_kernel<1, true>();
+  ok = ok && prepare_resident_kernel<2, false>() && prepare_resident_kernel<2, true>();
+  ok = ok && prepare_resident_kernel<4, false>() && prepare_resident_kernel<4, true>();
+  info.cus = cus;
+  info.resident_ok = ok;
+  info.ready = true;
+  return DSPARK_OK;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -718,6 +1238,37 @@ hipError_t launch_fused(const StepArgs& sa, bool in_kernel_pick, hipStream_t str
   return hipGetLastError();
 }
 
+// Which kernels one call enqueues, in order.
+struct Plan {
+  bool resident;
+  bool in_kernel_pick;
+  int n_chunks;
+  int chunk_cols;
+  int G;
+  int slice;
+};
+
+int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
+  (void)K;
+  const bool explicit_chunk = chunk_cols != 0;
+  if (chunk_cols == 0) chunk_cols = kDefaultChunk;
+  int rc = init_device();
+  if (rc != DSPARK_OK) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
+  const DeviceInfo& info = g_devices[dev];
+  plan->G = info.cus;
+  plan->slice = info.cus > 0 ? ((V + info.cus - 1) / info.cus + 7) / 8 * 8 : 0;
+  // resident path: all positions in one persistent launch with W kept on chip
+  plan->resident = !explicit_chunk && info.resident_ok && B <= kResRowsMax && r <= kResRank &&
+                   V <= (int)kResIdxMask + 1 && plan->slice <= kResSlice;
+  plan->chunk_cols = chunk_cols;
+  plan->n_chunks = (V + chunk_cols - 1) / chunk_cols;
+  // one row: every workgroup picks the previous token itself (no pick launch)
+  plan->in_kernel_pick = (B == 1) && plan->n_chunks <= kPickPerThread * kThreads;
+  return DSPARK_OK;
+}
+
 int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const uint16_t* W,
                      const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
                      const float* temperature, const int32_t* n_real, int B, int K, int V, int r,
@@ -728,6 +1279,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   if (rc != DSPARK_OK) return rc;
   if (base_dtype != DSPARK_F32 && base_dtype != DSPARK_BF16) return DSPARK_ERR_ARG;
   if (chunk_cols < 0 || chunk_cols % kTile != 0) return DSPARK_ERR_UNSUPPORTED;
+  const bool explicit_chunk = chunk_cols != 0;
   if (chunk_cols == 0) chunk_cols = kDefaultChunk;
   if (B == 0 || K == 0) return DSPARK_OK;
   if (!base || !E || !W || !prev_token || !seed || !offset || !temperature || !tokens || !logits ||
@@ -738,10 +1290,15 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   const size_t need = workspace_layout(B, K, V, r, nullptr, nullptr);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
 
-  const int n_chunks = (V + chunk_cols - 1) / chunk_cols;
-  // one row: every workgroup picks the previous token itself (no pick launch)
-  const bool in_kernel_pick = (B == 1) && n_chunks <= kPickPerThread * kThreads;
-  const int n_launches = in_kernel_pick ? K + 1 : 2 * K + 1;
+  Plan plan;
+  rc = make_plan(B, K, V, r, explicit_chunk ? chunk_cols : 0, &plan);
+  if (rc != DSPARK_OK) return rc;
+  const bool resident = plan.resident;
+  const bool in_kernel_pick = plan.in_kernel_pick;
+  const int n_chunks = plan.n_chunks;
+  const int G = plan.G;
+  const int slice = plan.slice;
+  const int n_launches = resident ? 3 : in_kernel_pick ? K + 1 : 2 * K + 1;
   if (events && n_events < n_launches + 1) return DSPARK_ERR_ARG;
 
   Workspace ws;
@@ -755,7 +1312,30 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   if (!mark()) return DSPARK_ERR_HIP;
   const bool bf16 = base_dtype == DSPARK_BF16;
 
-  for (int k = 0; k < K; ++k) {
+  if (resident) {
+    hipLaunchKernelGGL(res_clear, dim3(1), dim3(kThreads), 0, stream, ws.xkey, 2 * G * kResRowsMax, ws.fail);
+    if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
+    ResArgs ra;
+    ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
+    ra.temperature = temperature; ra.n_real = n_real; ra.logits = logits; ra.tokens = tokens;
+    ra.xkey = ws.xkey; ra.stat_part = ws.stat_part; ra.fail = ws.fail;
+    ra.B = B; ra.K = K; ra.V = V; ra.r = r; ra.slice = slice;
+    ra.spin_limit = 1u << 20;
+    const dim3 grid(G), block(kResThreads);
+    if (B == 1) {
+      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, true>), grid, block, kResLdsBytes, stream, ra);
+      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, false>), grid, block, kResLdsBytes, stream, ra);
+    } else if (B == 2) {
+      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, true>), grid, block, kResLdsBytes, stream, ra);
+      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, false>), grid, block, kResLdsBytes, stream, ra);
+    } else {
+      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, true>), grid, block, kResLdsBytes, stream, ra);
+      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, false>), grid, block, kResLdsBytes, stream, ra);
+    }
+    if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
+  }
+
+  for (int k = 0; k < K && !resident; ++k) {
     StepArgs sa;
     sa.base = base; sa.E = E; sa.W = W; sa.prev_token = prev_token; sa.e_buf = ws.e_buf;
     sa.prev_key = ws.part_key[(k + 1) & 1]; sa.prev_stat = ws.part_stat[(k + 1) & 1];
@@ -782,7 +1362,9 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   pr.logits = logits; pr.temperature = temperature; pr.tokens = tokens; pr.row_stat = ws.row_stat;
   pr.last_key = ws.part_key[(K - 1) & 1]; pr.last_stat = ws.part_stat[(K - 1) & 1];
   pr.q = q; pr.B = B; pr.K = K; pr.V = V; pr.n_chunks = n_chunks;
-  pr.last_from_partials = in_kernel_pick ? 1 : 0;
+  pr.last_from_partials = (in_kernel_pick && !resident) ? 1 : 0;
+  pr.part_stat = resident ? ws.stat_part : nullptr;
+  pr.n_part = resident ? G : 0;
   pr.blocks_per_row = (V + kThreads * 4 - 1) / (kThreads * 4);
   const long long n_blocks = (long long)pr.blocks_per_row * B * K;
   if (n_blocks >= (1LL << 31)) return DSPARK_ERR_UNSUPPORTED;
@@ -797,8 +1379,7 @@ extern "C" {
 
 int dspark_init(void) {
   using namespace dspark;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
+  if (init_device() != DSPARK_OK) return DSPARK_ERR_HIP;
   hipFuncAttributes attr;
   const void* kernels[] = {
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_gemv<1, false, true>),
@@ -813,6 +1394,7 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_rows<true>),
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax),
+      reinterpret_cast<const void*>(&res_clear),
   };
   for (const void* kfn : kernels)
     if (hipFuncGetAttributes(&attr, kfn) != hipSuccess) return DSPARK_ERR_HIP;
@@ -855,6 +1437,31 @@ int dspark_draft_block_events(const void* base_logits, int base_dtype, const uin
   return dspark::draft_block_impl(base_logits, base_dtype, E, W, prev_token, seed, offset, temperature,
                                   n_real, B, K, V, r, 0, tokens, logits_f32, draft_probs, workspace,
                                   workspace_bytes, stream, events, n_events);
+}
+
+int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds) {
+  using namespace dspark;
+  if (check_sizes(B, K, V, r) != DSPARK_OK) return DSPARK_ERR_UNSUPPORTED;
+  if (B == 0 || K == 0) return 0;
+  Plan plan;
+  const int rc = make_plan(B, K, V, r, 0, &plan);
+  if (rc != DSPARK_OK) return rc;
+  int n = 0;
+  auto put = [&](int kind) {
+    if (kinds && n < max_kinds) kinds[n] = kind;
+    ++n;
+  };
+  if (plan.resident) {
+    put(DSPARK_LAUNCH_CLEAR);
+    put(DSPARK_LAUNCH_RESIDENT_BLOCK);
+  } else {
+    for (int k = 0; k < K; ++k) {
+      put(DSPARK_LAUNCH_FUSED_POSITION);
+      if (!plan.in_kernel_pick) put(DSPARK_LAUNCH_PICK);
+    }
+  }
+  put(DSPARK_LAUNCH_PROPOSAL);
+  return n;
 }
 
 const char* dspark_status_string(int status) {

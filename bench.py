@@ -95,13 +95,11 @@ class Bench:
         """Eager blocks with an event after every launch: mean us per launch of each kernel."""
         torch = self.torch
         from ancestral_draft_token_amd.hip_events import EventSet
+        from ancestral_draft_token_amd import LAUNCH_KINDS, dspark_launch_plan
         w = self.w
-        K = w.K
-        # launch order (include/dspark.h): at B == 1 the K fused kernels pick the
-        # previous token themselves; otherwise each is followed by pick_and_gather
-        fused_pick = w.B == 1 and -(-w.V // 128) <= 2048
-        names = (["markov_bias_gumbel_argmax"] * K if fused_pick
-                 else ["markov_bias_gumbel_argmax", "pick_and_gather"] * K) + ["proposal_softmax"]
+        plan = dspark_launch_plan(w.B, w.K, w.V, w.r)
+        names = [LAUNCH_KINDS[kind] for kind in plan]
+        self.plan = plan
         times = {n: [] for n in names}
         ev = EventSet(len(names) + 1)
         try:

@@ -125,14 +125,10 @@ int dspark_draft_block_chunked(
 
 /* The default-chunked block with timing marks, for measurement: events[0]
  * is recorded on `stream` before the first launch and events[i + 1] after
- * the i-th launch, in launch order. With B == 1 (and at most 2048 vocabulary
- * chunks) the block is K + 1 launches: the K fused per-position kernels, then
- * the proposal kernel (each fused kernel picks the previous position's token
- * itself). Otherwise it is 2K + 1 launches: each fused kernel followed by its
- * pick_and_gather, then the proposal kernel. n_events must be at least the
- * launch count plus one; the events are caller-created hipEvent_t handles
- * passed as void*. Returns DSPARK_ERR_ARG if events is NULL or too short;
- * otherwise as dspark_draft_block. */
+ * the i-th launch, in the order dspark_launch_plan reports. n_events must be
+ * at least the launch count plus one; the events are caller-created
+ * hipEvent_t handles passed as void*. Returns DSPARK_ERR_ARG if events is
+ * NULL or too short; otherwise as dspark_draft_block. */
 int dspark_draft_block_events(
     const void* base_logits, int base_dtype,
     const uint16_t* E, const uint16_t* W,
@@ -142,6 +138,31 @@ int dspark_draft_block_events(
     int32_t* tokens, float* logits_f32, float* draft_probs,
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int n_events);
+
+/* Kinds of kernel launch a block is made of. */
+typedef enum {
+    DSPARK_LAUNCH_FUSED_POSITION = 0,  /* markov_bias_gumbel_argmax for one position */
+    DSPARK_LAUNCH_PICK = 1,            /* pick_and_gather for one position */
+    DSPARK_LAUNCH_PROPOSAL = 2,        /* proposal_softmax for the whole block */
+    DSPARK_LAUNCH_CLEAR = 3,           /* clears the exchange words of the resident block */
+    DSPARK_LAUNCH_RESIDENT_BLOCK = 4   /* markov_bias_gumbel_argmax for all K positions at once */
+} dspark_launch_kind_t;
+
+/* The launches dspark_draft_block enqueues on the current device for these
+ * sizes, in order: writes up to max_kinds dspark_launch_kind_t values to
+ * `kinds` (host memory, may be NULL) and returns the launch count, or a
+ * negative status. Three plans exist:
+ *   - resident (B <= 4, r <= 256, V <= 2^18 and V <= 784 x the device's CU
+ *     count): CLEAR, RESIDENT_BLOCK, PROPOSAL. One persistent launch runs all K
+ *     positions; each workgroup keeps its slice of W on chip for the block.
+ *     It needs every workgroup resident at once (one per compute unit); its
+ *     device-side waits are bounded, and if one expires the call's tokens are
+ *     -1 instead of hanging.
+ *   - B == 1 otherwise: K x FUSED_POSITION, PROPOSAL (each fused kernel picks
+ *     the previous position's token itself).
+ *   - otherwise: K x (FUSED_POSITION, PICK), PROPOSAL.
+ * dspark_draft_block_chunked always uses the last two plans. */
+int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds);
 
 /* A static, human-readable name for a status code. */
 const char* dspark_status_string(int status);

@@ -130,3 +130,27 @@ def test_full_size_chunk_count_invariance(n_chunks):
     assert bool((ref.tokens == alt.tokens).all())
     assert torch_equal(ref.logits, alt.logits)
     assert float((ref.q - alt.q).abs().max()) <= parity.Q_ATOL
+
+
+@pytest.mark.parametrize("B", [2, 3, 4])
+def test_full_size_resident_batches(B):
+    """Batches the resident (one persistent launch) plan serves, at full width."""
+    from ancestral_draft_token_amd import dspark_launch_plan
+    w = inputs.small_batch(B=B, base_dtype="bf16" if B == 3 else "f32",
+                           temperature=lambda b: [1.0, 0.0, 0.6, 1.3][b])
+    say(f"plan {dspark_launch_plan(w.B, w.K, w.V, w.r)}")
+    p = run_gpu(w)
+    t, l, q = rows_to_host(p, list(range(B)))
+    rep = parity.check(w, t, l, q)
+    say(f"parity ok B={B} {rep.as_dict()}")
+
+
+def test_resident_and_streaming_plans_agree():
+    """The one-launch resident plan and the per-position plan (forced by an explicit
+    chunking) draw the same tokens; logits agree to the parity tolerance."""
+    w = inputs.single_request()
+    a = run_gpu(w)
+    b = run_gpu(w, chunk_cols=128)
+    assert bool((a.tokens == b.tokens).all())
+    assert float((a.logits - b.logits).abs().max()) <= parity.LOGIT_ATOL
+    assert float((a.q - b.q).abs().max()) <= parity.Q_ATOL
