@@ -1,0 +1,108 @@
+"""Turn rocprofv3 outputs into the short summaries kept under profiles/.
+
+Two summaries:
+  * kernel_summary(): per-kernel call counts and durations from a
+    ``--kernel-trace --stats -f csv`` run (the ``*_kernel_stats.csv`` file);
+  * traffic_summary(): HBM bytes per dispatch from two ``--pmc`` runs
+    (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by
+    what the same counter reads for a plain device copy of known size that
+    ``bench.py --pmc-run`` launches first.
+
+Usage (from the repository root, after the rocprofv3 runs):
+  python -m ancestral_draft_token_amd.profiling kernels <stats.csv> <out.md> <command...>
+  python -m ancestral_draft_token_amd.profiling traffic <fetch.csv> <write.csv> <workload> <mall> <out.json> <command...>
+"""
+
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 512 << 20       # the calibration copy in bench.py --pmc-run: reads and writes this much
+DOMINANT = "markov_bias_gumbel_argmax"
+
+
+def source_hash() -> str:
+    with open(os.path.join(PKG, "csrc", "dspark.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kernel_summary(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel summary", "", f"command: `{command}`", "",
+             f"source sha256[:16] of csrc/dspark.hip: {source_hash()}", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "/")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path: str, counter: str):
+    """[(dispatch id, kernel name, value)] for one counter, summed over its dimensions."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    return sorted((d, n, v) for (d, n), v in acc.items())
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, mall: str, out_json: str,
+                    command: str = "") -> dict:
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    # the calibration copies: the device-to-device copies that write COPY_BYTES
+    calib = [d for d, n, v in write if "copy" in n.lower() and abs(v - kib) < 0.05 * kib][:3]
+    if not calib:
+        raise SystemExit("no calibration copy dispatch found")
+    fmap = {d: v for d, _, v in fetch}
+    wmap = {d: v for d, _, v in write}
+    copy_f = statistics.median(fmap[d] for d in calib)
+    copy_w = statistics.median(wmap[d] for d in calib)
+    f_scale, w_scale = kib / copy_f, kib / copy_w
+    dom = [d for d, n, _ in write if DOMINANT in n]
+    rec = {
+        "workload": workload, "mall": mall, "kernel": DOMINANT, "source_sha": source_hash(),
+        "command": command,
+        "copy_bytes": COPY_BYTES, "copy_dispatches": calib,
+        "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "dispatches": len(dom),
+        "fetch_bytes_per_launch": statistics.median(fmap[d] for d in dom) * f_scale * 1024.0,
+        "write_bytes_per_launch": statistics.median(wmap[d] for d in dom) * w_scale * 1024.0,
+    }
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    others = {}
+    for d, n, v in write:
+        if d in calib or DOMINANT in n or d not in fmap:
+            continue
+        name = n.split("(")[0][:70]
+        others.setdefault(name, []).append((fmap[d] * f_scale * 1024.0, v * w_scale * 1024.0))
+    rec["other_kernels"] = {n: {"fetch_bytes": statistics.median(x[0] for x in v),
+                                "write_bytes": statistics.median(x[1] for x in v), "dispatches": len(v)}
+                            for n, v in others.items()}
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "kernels":
+        kernel_summary(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic_summary(*sys.argv[2:7], command=" ".join(sys.argv[7:])), indent=1))
+    else:
+        raise SystemExit(__doc__)

@@ -116,6 +116,21 @@ class Bench:
         return {n: statistics.mean(v) for n, v in times.items()}
 
 
+def traffic_for(w, args):
+    """Measured HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 counter summary for this workload (profiles/), scaled by the
+    copy-kernel calibration recorded there; None if there is none."""
+    from ancestral_draft_token_amd.profiling import source_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}_{args.mall}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_hash():
+        return None          # the kernel changed since the counters were taken
+    return round(rec["bytes_per_launch"])
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU oracle, as it stands, on the same workload: whole blocks, repeated."""
     import oracle
@@ -151,6 +166,8 @@ def measure(w, steps, warmup, mall, kernel_reps=5):
         "us_p90": sorted(us)[(len(us) * 9) // 10],
         "wall_s": wall,
         "kernels_us": kt,
+        "plan": b.plan,
+        "resident": 4 in b.plan,
         "bytes": ab,
         "block_gbs": ab["block"] / (statistics.mean(us) * 1e-6) / 1e9,
     }
@@ -168,6 +185,8 @@ def main():
     ap.add_argument("--mall", default="cold", choices=["cold", "warm"])
     ap.add_argument("--no-sweep", action="store_true", help="skip the B=8/44/88 lines in 'also'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="for rocprofv3 --pmc: a calibration copy of known size, then a few replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the draft-block sampler is built and measured on "
@@ -182,11 +201,28 @@ def main():
         sys.exit(1)
 
     w = inputs.WORKLOADS[args.workload]()
+    if args.pmc_run:
+        from ancestral_draft_token_amd.profiling import COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        b = Bench(w, mall=args.mall)
+        b.steps(max(3, args.steps))
+        torch.cuda.synchronize()
+        print(f"[bench] pmc run done: {w.name}", file=sys.stderr, flush=True)
+        return
     print(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}, MALL {args.mall}",
           file=sys.stderr, flush=True)
     r = measure(w, args.steps, args.warmup, args.mall)
     fused_us = r["kernels_us"]["markov_bias_gumbel_argmax"]
-    achieved = r["bytes"]["fused_per_launch"] / (fused_us * 1e-6) / 1e9
+    # the dominant kernel: with the one-launch (resident) plan it covers all K
+    # positions, otherwise one position per launch
+    positions_per_launch = w.K if r["resident"] else 1
+    bytes_per_launch = r["bytes"]["fused_per_launch"] * positions_per_launch
+    achieved = bytes_per_launch / (fused_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(r["us_per_block"], 2),
@@ -202,7 +238,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "B_real": w.n_real_rows, "K": w.K, "V": w.V,
                    "r": w.r, "base": w.base_dtype, "mall": args.mall,
-                   "graph": "one hipGraph per block (2K+1 launches)"},
+                   "graph": "one hipGraph per block", "launches": r["plan"]},
         "us_median": round(r["us_median"], 2),
         "us_p10": round(r["us_p10"], 2),
         "us_p90": round(r["us_p90"], 2),
@@ -210,8 +246,9 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in r["kernels_us"].items()},
         "roofline": {"bound": "hbm", "kernel": "markov_bias_gumbel_argmax",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": r["bytes"]["fused_per_launch"]},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(w, args),
+                     "bytes_per_launch": bytes_per_launch,
+                     "positions_per_launch": positions_per_launch},
     }
     if not args.no_sweep:
         also = {}
