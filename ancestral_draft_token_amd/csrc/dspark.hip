@@ -57,20 +57,23 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo_a = 0xD2511F53u * c.x;
-    const uint32_t hi_a = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo_b = 0xCD9E8D57u * c.z;
-    const uint32_t hi_b = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi_b ^ c.y ^ k0, lo_b, hi_a ^ c.w ^ k1, lo_a);
+    // full 64-bit products: one v_mad_u64_u32 each instead of a mul_lo/mul_hi pair
+    const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c.x;
+    const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
+    c = make_uint4((uint32_t)(pb >> 32) ^ c.y ^ k0, (uint32_t)pb, (uint32_t)(pa >> 32) ^ c.w ^ k1,
+                   (uint32_t)pa);
   }
   return c;
 }
 
 // Standard Gumbel variate from the top 23 bits of a Philox word:
-// u = ((x >> 9) + 1/2) 2^-23 is exact in float32; g = -ln(-ln u).
+// u = ((x >> 9) + 1/2) 2^-23 is exact in float32; g = -ln(-ln u), evaluated
+// with the hardware base-2 logarithm as -ln2 * (log2(-log2 u) + log2(ln 2)).
+// Over all 2^23 values of u this is within 2.0e-6 of -ln(-ln u) in double.
 __device__ __forceinline__ float gumbel_from_bits(uint32_t x) {
   const float u = __fmul_rn(__fadd_rn((float)(x >> 9), 0.5f), 0x1p-23f);
-  return -logf(-logf(u));
+  const float e2 = -__builtin_amdgcn_logf(u);                 // -log2(u) > 0
+  return -0.693147182f * (__builtin_amdgcn_logf(e2) + -0.528766364f);
 }
 
 // Total-order key of a score: larger key = better; NaN is the smallest key;
@@ -1126,6 +1129,375 @@ __global__ __launch_bounds__(kThreads) void res_clear(uint64_t* xkey, int n, int
 }
 
 // ---------------------------------------------------------------------------
+// Resident path, MFMA form (4 < B <= 128). Same block structure as the VALU
+// resident kernel: one persistent launch, one 512-thread workgroup per CU
+// owning up to 784 columns, W on chip for the whole block. Here the slice is
+// held as bf16 A-operand fragments of v_mfma_f32_16x16x32_bf16 (A = W^T: 16
+// columns x 32 rank rows; lane l holds column l % 16, rank rows 8 (l / 16) ..
+// + 7): M-tiles 0..31 in VGPRs (four per wave), 32..48 in LDS. The B operand
+// is the embedding rows of one N-tile of 16 rows, staged in LDS
+// (double-buffered) and held in registers while every M-tile of the wave
+// uses it. The accumulator leaves each lane 4 consecutive columns of one row
+// (rows 4 (l / 16) .. + 3 of D = columns, column l % 16 of D = row), the
+// epilogue's shape: one Philox block per lane.
+// Positions are separated by a two-level exchange: every workgroup publishes
+// one tagged word per row; the workgroup owning a row reduces its G words and
+// publishes the row's tagged winner; every workgroup reads the B winners.
+// ---------------------------------------------------------------------------
+constexpr int kMfThreads = 256;                            // one wave per SIMD: 512 registers a lane
+constexpr int kMfWaves = kMfThreads / 64;
+constexpr int kMfTilesPerWave = 8;                         // VGPR M-tiles per wave (256 registers)
+constexpr int kMfRegTiles = kMfWaves * kMfTilesPerWave;    // 32
+constexpr int kMfLdsTiles = kResSlice / 16 - kMfRegTiles;  // 17
+constexpr int kMfLdsPerWave = (kMfLdsTiles + kMfWaves - 1) / kMfWaves;   // 5
+constexpr int kMfTilesMax = kMfTilesPerWave + kMfLdsPerWave;            // 13
+constexpr int kMfKSteps = kResRank / 32;                   // 8
+constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
+constexpr int kMfERow = 520;                               // bytes per staged E row (512 + pad)
+constexpr size_t kMfLdsW = (size_t)kMfLdsTiles * kMfKSteps * 64 * 16;   // 139,264 bytes
+constexpr size_t kMfLdsE = (size_t)2 * 16 * kMfERow;                    // 16,640 bytes
+constexpr size_t kMfLdsBytes = kMfLdsW + kMfLdsE;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+struct MfArgs {
+  const void* base;
+  const uint16_t* E;
+  const uint16_t* W;
+  const int32_t* prev_token;
+  const int64_t* seed;
+  const int64_t* offset;
+  const float* temperature;
+  const int32_t* n_real;
+  float* logits;
+  int32_t* tokens;
+  uint64_t* xrow;      // [2][G][kMfRowsMax] per-workgroup tagged words
+  uint64_t* xwin;      // [2][kMfRowsMax] tagged row winners
+  Stat* stat_part;     // [K][B][G]
+  int* fail;
+  int B, K, V, r, slice;
+  unsigned spin_limit;
+};
+
+// Row state kept in LDS for the whole launch (temperature, slot, padding).
+struct MfRow {
+  float invT;
+  uint32_t flags;        // bit 0: greedy, bit 1: padding
+  uint32_t key0, key1, ctr2, ctr3;
+};
+
+// Stage the embedding rows of N-tile nt (16 rows x 512 bytes) into an LDS
+// buffer: thread t copies 32 bytes (row t / 16, bytes 32 (t % 16) ..) of E[d[row]].
+struct ERow2 {
+  uint4 lo, hi;
+};
+
+__device__ __forceinline__ ERow2 mf_load_erow(const MfArgs& a, const int* s_d, int nt, int t) {
+  const int row = 16 * nt + t / 16, j16 = 16 * (t % 16);
+  const bool ok = row < a.B && j16 < a.r;
+  const uint16_t* src = a.E + (ok ? (size_t)s_d[row] * a.r + j16 : 0);
+  ERow2 v{*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8)};
+  if (!ok) v = ERow2{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  return v;
+}
+
+__device__ __forceinline__ void mf_store_erow(unsigned char* ebuf, int t, const ERow2& v) {
+  uint4* dst = reinterpret_cast<uint4*>(ebuf + (t / 16) * kMfERow + 32 * (t % 16));
+  dst[0] = v.lo;
+  dst[1] = v.hi;
+}
+
+template <bool kBf16Base>
+__global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resident_mfma(MfArgs a) {
+  extern __shared__ __align__(16) unsigned char mf_lds[];
+  unsigned char* lds_w = mf_lds;                         // [17][8][64][16 B] fragments
+  unsigned char* lds_e = mf_lds + kMfLdsW;               // [2][16][kMfERow]
+  __shared__ uint64_t s_rk[2][kMfWaves][16];             // per-wave row partials, by N-tile parity
+  __shared__ Stat s_rs[2][kMfWaves][16];
+  __shared__ MfRow s_row[kMfRowsMax];
+  __shared__ int s_d[kMfRowsMax];                        // previous token per row
+  __shared__ int s_fail;
+
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int V = a.V, r = a.r, K = a.K, B = a.B;
+  const int NT = (B + 15) / 16;
+  const int col0 = g * a.slice;
+  const int ncols = max(0, min(a.slice, V - col0));
+  const int n_real = a.n_real ? *a.n_real : B;
+  const int lr = lane & 15;           // row of an N-tile / column of an M-tile
+  const int lq = lane >> 4;           // quad: rank rows 8 lq .. of a K-step; columns 4 lq .. of D
+
+  if (t == 0) s_fail = 0;
+  for (int b = t; b < B; b += kMfThreads) {
+    const RowState rs = row_state(a.temperature, a.seed, a.offset, b, n_real);
+    s_row[b] = MfRow{rs.invT, (rs.greedy ? 1u : 0u) | (rs.pad ? 2u : 0u), rs.key0, rs.key1, rs.ctr2, rs.ctr3};
+    s_d[b] = clamp_token(a.prev_token[b], V);
+  }
+
+  // ---- (1) LDS M-tiles 32..48: each 16-byte load (8 columns of one rank row)
+  // is scattered into the fragment layout (element e of lane l at byte l*16 + 2e)
+  {
+    const int items = kMfLdsTiles * kResRank * 2;
+    for (int q = t; q < items; q += kMfThreads) {
+      const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
+      const int j = rem / 2, h = rem % 2;
+      const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
+      const bool ok = j < r && c8 < ncols;
+      uint4 v = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)j * V + col0 + c8 : 0));
+      if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      unsigned char* frag = lds_w + ((size_t)ti * kMfKSteps + j / 32) * 1024;
+      const int lbase = 8 * h + 16 * ((j % 32) / 8);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint16_t val = (uint16_t)(w4[c / 2] >> (16 * (c % 2)));
+        *reinterpret_cast<uint16_t*>(frag + (lbase + c) * 16 + 2 * (j % 8)) = val;
+      }
+    }
+  }
+
+  // ---- (2) VGPR M-tiles 8w..8w+7, staged through this wave's 4 KB of the (not yet
+  // used) E region, 16 rank rows at a time: lanes of quads 0,1 take rows 0..15 of a
+  // K-step, quads 2,3 rows 16..31
+  uint4 wf[kMfTilesPerWave][kMfKSteps];
+  {
+    unsigned char* stage = lds_e + (size_t)wv * 4096;   // [16 rows][128 columns] bf16
+    const int cbase = 128 * wv;                         // first column of the wave's tiles
+    const uint16_t* st16 = reinterpret_cast<const uint16_t*>(stage);
+#pragma unroll
+    for (int ks = 0; ks < kMfKSteps; ++ks) {
+      uint32_t d[kMfTilesPerWave][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 32 * ks + 16 * half + lane / 16 + 4 * q, c8 = cbase + 8 * (lane % 16);
+          const bool ok = row < r && c8 < ncols;
+          v[q] = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)row * V + col0 + c8 : 0));
+          if (!ok) v[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint4*>(stage + (lane / 16 + 4 * q) * 256 + 16 * (lane % 16)) = v[q];
+        if ((lq >> 1) == half) {
+#pragma unroll
+          for (int mt = 0; mt < kMfTilesPerWave; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rr = 8 * (lq & 1) + 2 * i;   // row within the staged half
+              const uint32_t lo = st16[rr * 128 + 16 * mt + lr];
+              const uint32_t hi = st16[(rr + 1) * 128 + 16 * mt + lr];
+              d[mt][i] = lo | (hi << 16);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int mt = 0; mt < kMfTilesPerWave; ++mt) wf[mt][ks] = make_uint4(d[mt][0], d[mt][1], d[mt][2], d[mt][3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- (3) the E rows of N-tiles 0 and 1 of position 0, prefetch of N-tile 2
+  ERow2 epre{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  mf_store_erow(lds_e, t, mf_load_erow(a, s_d, 0, t));
+  if (NT > 1) mf_store_erow(lds_e + 16 * kMfERow, t, mf_load_erow(a, s_d, 1, t));
+  if (NT > 2) epre = mf_load_erow(a, s_d, 2, t);
+
+  // the wave's tiles: i < 8 are VGPR tiles 8 wv + i; i >= 8 are LDS tiles 32 + wv + 4 (i - 8)
+  auto tile_m = [&](int i) {
+    return i < kMfTilesPerWave ? kMfTilesPerWave * wv + i : kMfRegTiles + wv + kMfWaves * (i - kMfTilesPerWave);
+  };
+  int n_mine = 0;   // tiles with columns in this slice
+  for (int i = 0; i < kMfTilesMax; ++i) {
+    const int m = tile_m(i);
+    if ((i < kMfTilesPerWave || m < kMfRegTiles + kMfLdsTiles) && 16 * m < ncols) n_mine = i + 1;
+  }
+
+  __syncthreads();
+
+  // combine the waves' partials of N-tile nt and publish each row's tagged word
+  auto publish = [&](int k, int nt) {
+    if (t < 16) {
+      const int b = 16 * nt + t;
+      uint64_t kk = s_rk[nt & 1][0][t];
+      Stat ss = s_rs[nt & 1][0][t];
+#pragma unroll
+      for (int w = 1; w < kMfWaves; ++w) {
+        kk = umax64(kk, s_rk[nt & 1][w][t]);
+        ss = stat_merge(ss, s_rs[nt & 1][w][t]);
+      }
+      if (b < B) {
+        a.stat_part[((size_t)k * B + b) * G + g] = ss;
+        const uint64_t idx = kk ? kResIdxMask - (uint64_t)key_token(kk) : 0ull;
+        const uint64_t word = ((uint64_t)(k + 1) << kResTagShift) | ((kk >> 32) << 18) | idx;
+        st_agent_u64(a.xrow + ((size_t)(k & 1) * G + g) * kMfRowsMax + b, word);
+      }
+    }
+  };
+
+  for (int k = 0; k < K; ++k) {
+    for (int nt = 0; nt < NT; ++nt) {
+      __syncthreads();   // E buffer nt & 1 is complete; s_rk[(nt - 1) & 1] is complete
+      if (nt > 0) publish(k, nt - 1);
+      if (nt > 0 && nt + 1 < NT) mf_store_erow(lds_e + ((nt + 1) & 1) * 16 * kMfERow, t, epre);
+      if (nt > 0 && nt + 2 < NT) epre = mf_load_erow(a, s_d, nt + 2, t);
+
+      // B operand of this N-tile: lane = row lr, rank rows 32 ks + 8 lq .. (rank
+      // rows >= r are zero in both operands, so all 8 K-steps always run)
+      uint4 ef[kMfKSteps];
+      const unsigned char* eb = lds_e + (nt & 1) * 16 * kMfERow + lr * kMfERow + 16 * lq;
+#pragma unroll
+      for (int ks = 0; ks < kMfKSteps; ++ks) ef[ks] = *reinterpret_cast<const uint4*>(eb + 64 * ks);
+
+      const int b = 16 * nt + lr;
+      const bool row_ok = b < B;
+      RowState rs{};
+      if (row_ok) {
+        const MfRow mr = s_row[b];
+        rs.invT = mr.invT;
+        rs.greedy = (mr.flags & 1u) != 0;
+        rs.pad = (mr.flags & 2u) != 0;
+        rs.key0 = mr.key0; rs.key1 = mr.key1; rs.ctr2 = mr.ctr2; rs.ctr3 = mr.ctr3;
+      }
+      const size_t row_off = ((size_t)b * K + k) * (size_t)V;
+      uint64_t best = 0;
+      Stat st{-INFINITY, 0.0f};
+
+      // base logits 4 tiles ahead, in rotating registers (no runtime-indexed arrays)
+      auto base_off = [&](int i) -> size_t {
+        const int c4 = 16 * tile_m(i) + 4 * lq;
+        return (row_ok && !rs.pad && i < n_mine && c4 < ncols) ? row_off + (size_t)(col0 + c4) : 0;
+      };
+      Base4<kBf16Base> b0, b1, b2, b3;
+      load_base4<kBf16Base>(b0, a.base, base_off(0));
+      load_base4<kBf16Base>(b1, a.base, base_off(1));
+      load_base4<kBf16Base>(b2, a.base, base_off(2));
+      load_base4<kBf16Base>(b3, a.base, base_off(3));
+
+#pragma unroll 1
+      for (int i = 0; i < n_mine; ++i) {
+        const int m = tile_m(i);
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (i < kMfTilesPerWave) {
+          // VGPR fragments need compile-time indices: one MFMA chain per case
+          switch (i) {
+#define DSPARK_MF_TILE(T)                                                          \
+  case T:                                                                          \
+    _Pragma("unroll") for (int ks = 0; ks < kMfKSteps; ++ks) acc = mfma_bf16(wf[T][ks], ef[ks], acc); \
+    break;
+            DSPARK_MF_TILE(0) DSPARK_MF_TILE(1) DSPARK_MF_TILE(2) DSPARK_MF_TILE(3)
+            DSPARK_MF_TILE(4) DSPARK_MF_TILE(5) DSPARK_MF_TILE(6) DSPARK_MF_TILE(7)
+#undef DSPARK_MF_TILE
+            default: break;
+          }
+        } else {
+          const unsigned char* fb = lds_w + (size_t)(m - kMfRegTiles) * kMfKSteps * 1024 + lane * 16;
+#pragma unroll
+          for (int ks = 0; ks < kMfKSteps; ++ks)
+            acc = mfma_bf16(*reinterpret_cast<const uint4*>(fb + ks * 1024), ef[ks], acc);
+        }
+        const int c4 = 16 * m + 4 * lq;              // column offset in the slice
+        if (row_ok && c4 < ncols) {
+          const uint32_t v0 = (uint32_t)(col0 + c4);
+          float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (!rs.pad) widen_base4<kBf16Base>(b0, base);
+          const float bias[4] = {acc[0], acc[1], acc[2], acc[3]};
+          epilogue4(rs, k, v0, base, bias, a.logits + row_off + v0, best, st);
+        }
+        b0 = b1;
+        b1 = b2;
+        b2 = b3;
+        load_base4<kBf16Base>(b3, a.base, base_off(i + 4));
+      }
+      // lanes of one row (equal lane % 16) combine; lanes 0..15 hold the wave's partials
+      for (int mask = 16; mask < 64; mask <<= 1) {
+        best = umax64(best, shfl_xor_u64(best, mask, 64));
+        Stat o;
+        o.m = __shfl_xor(st.m, mask, 64);
+        o.l = __shfl_xor(st.l, mask, 64);
+        st = stat_merge(st, o);
+      }
+      if (lane < 16) {
+        s_rk[nt & 1][wv][lane] = best;
+        s_rs[nt & 1][wv][lane] = st;
+      }
+    }
+    __syncthreads();
+    publish(k, NT - 1);
+
+    // ---- exchange level 2: the owner of row b (workgroup b, b + G, ...) reduces its G words
+    const uint64_t tag = (uint64_t)(k + 1);
+    uint64_t* xr = a.xrow + (size_t)(k & 1) * G * kMfRowsMax;
+    uint64_t* xw = a.xwin + (size_t)(k & 1) * kMfRowsMax;
+    bool failed = false;
+    for (int b = g; b < B; b += G) {
+      uint64_t x = 0;
+      for (int i = t; i < G; i += kMfThreads) {
+        const uint64_t* pw = xr + (size_t)i * kMfRowsMax + b;
+        uint64_t w = ld_agent_u64(pw);
+        unsigned spins = 0;
+        while ((w >> kResTagShift) != tag) {
+          if (++spins > a.spin_limit) { failed = true; break; }
+          __builtin_amdgcn_s_sleep(1);
+          w = ld_agent_u64(pw);
+        }
+        x = umax64(x, w);
+      }
+      for (int mask = 1; mask < 64; mask <<= 1) x = umax64(x, shfl_xor_u64(x, mask, 64));
+      __syncthreads();
+      if (lane == 0) s_rk[0][wv][0] = x;
+      __syncthreads();
+      if (t == 0) {
+        uint64_t y = s_rk[0][0][0];
+        for (int w = 1; w < kMfWaves; ++w) y = umax64(y, s_rk[0][w][0]);
+        st_agent_u64(xw + b, (tag << kResTagShift) | (y & ((1ull << kResTagShift) - 1)));
+      }
+    }
+    // ---- level 3: every workgroup reads the B winners
+    for (int b = t; b < B; b += kMfThreads) {
+      const uint64_t* pw = xw + b;
+      uint64_t w = ld_agent_u64(pw);
+      unsigned spins = 0;
+      while ((w >> kResTagShift) != tag) {
+        if (++spins > a.spin_limit) { failed = true; break; }
+        __builtin_amdgcn_s_sleep(1);
+        w = ld_agent_u64(pw);
+      }
+      const uint64_t low = w & ((1ull << kResTagShift) - 1);
+      s_d[b] = low ? clamp_token((int)(kResIdxMask - (low & kResIdxMask)), V) : 0;
+    }
+    if (failed) {
+      s_fail = 1;
+      atomicExch(a.fail, 1);
+    }
+    __syncthreads();
+    if (s_fail) {
+      if (g == 0)
+        for (int b = t; b < B; b += kMfThreads)
+          for (int kk = k; kk < K; ++kk) a.tokens[(size_t)b * K + kk] = -1;
+      return;
+    }
+    if (g == 0)
+      for (int b = t; b < B; b += kMfThreads) a.tokens[(size_t)b * K + k] = s_d[b];
+    if (k + 1 < K) {
+      // E rows of the next position's N-tiles 0 and 1, and the prefetch of N-tile 2
+      mf_store_erow(lds_e, t, mf_load_erow(a, s_d, 0, t));
+      if (NT > 1) mf_store_erow(lds_e + 16 * kMfERow, t, mf_load_erow(a, s_d, 1, t));
+      if (NT > 2) epre = mf_load_erow(a, s_d, 2, t);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Workspace {
@@ -1133,15 +1505,16 @@ struct Workspace {
   Stat* part_stat[2];
   Stat* row_stat;
   uint16_t* e_buf;
-  uint64_t* xkey;          // resident path: [2][kResMaxCUs][kResRowsMax]
-  Stat* stat_part;         // resident path: [K][B][kResMaxCUs]
+  uint64_t* xkey;          // resident paths: per-workgroup exchange words
+  uint64_t* xwin;          // resident MFMA path: [2][kMfRowsMax] row winners (follows xkey)
+  Stat* stat_part;         // resident paths: [K][B][kResMaxCUs]
   int* fail;               // resident path: bounded-wait failure flag
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Layout for the largest chunk count (chunk = 128 columns), plus the resident
-// path's exchange words and per-workgroup statistics when B <= 4.
+// paths' exchange words and per-workgroup statistics when B <= 128.
 inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* base) {
   const size_t max_chunks = (size_t)(V + kTile - 1) / kTile;
   size_t off = 0;
@@ -1152,9 +1525,12 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
   }
   const size_t o_rst = off; off = align_up(off + (size_t)B * K * sizeof(Stat), 256);
   const size_t o_e = off;   off = align_up(off + (size_t)B * r * sizeof(uint16_t), 256);
-  size_t o_x = 0, o_sp = 0, o_f = 0;
-  if (B <= kResRowsMax) {
-    o_x = off;  off = align_up(off + (size_t)2 * kResMaxCUs * kResRowsMax * sizeof(uint64_t), 256);
+  size_t o_x = 0, o_w = 0, o_sp = 0, o_f = 0;
+  const bool resident_ws = B <= kMfRowsMax;
+  if (resident_ws) {
+    // exchange words of both resident kernels: [2][CUs][rows] then [2][rows] winners
+    o_x = off;  off += (size_t)2 * kResMaxCUs * kMfRowsMax * sizeof(uint64_t);
+    o_w = off;  off = align_up(off + (size_t)2 * kMfRowsMax * sizeof(uint64_t), 256);
     o_sp = off; off = align_up(off + (size_t)K * B * kResMaxCUs * sizeof(Stat), 256);
     o_f = off;  off = align_up(off + sizeof(int), 256);
   }
@@ -1165,9 +1541,10 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
     }
     ws->row_stat = reinterpret_cast<Stat*>(base + o_rst);
     ws->e_buf = reinterpret_cast<uint16_t*>(base + o_e);
-    ws->xkey = B <= kResRowsMax ? reinterpret_cast<uint64_t*>(base + o_x) : nullptr;
-    ws->stat_part = B <= kResRowsMax ? reinterpret_cast<Stat*>(base + o_sp) : nullptr;
-    ws->fail = B <= kResRowsMax ? reinterpret_cast<int*>(base + o_f) : nullptr;
+    ws->xkey = resident_ws ? reinterpret_cast<uint64_t*>(base + o_x) : nullptr;
+    ws->xwin = resident_ws ? reinterpret_cast<uint64_t*>(base + o_w) : nullptr;
+    ws->stat_part = resident_ws ? reinterpret_cast<Stat*>(base + o_sp) : nullptr;
+    ws->fail = resident_ws ? reinterpret_cast<int*>(base + o_f) : nullptr;
   }
   return off;
 }
@@ -1176,6 +1553,7 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
 struct DeviceInfo {
   bool ready;
   bool resident_ok;   // one 512-thread workgroup with kResLdsBytes of LDS fits on every CU
+  bool mfma_ok;       // the same for the MFMA resident kernel
   int cus;
 };
 constexpr int kMaxDevices = 64;
@@ -1193,6 +1571,18 @@ bool prepare_resident_kernel() {
   return occ >= 1;
 }
 
+template <bool kBf16>
+bool prepare_mfma_kernel() {
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) != hipSuccess)
+    return false;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16>,
+                                                   kMfThreads, kMfLdsBytes) != hipSuccess)
+    return false;
+  return occ >= 1;
+}
+
 int init_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_HIP;
@@ -1205,8 +1595,11 @@ int init_device() {
   ok = ok && prepare_resident_kernel<1, false>() && prepare_resident_kernel<1, true>();
   ok = ok && prepare_resident_kernel<2, false>() && prepare_resident_kernel<2, true>();
   ok = ok && prepare_resident_kernel<4, false>() && prepare_resident_kernel<4, true>();
+  bool mok = cus > 0 && cus <= kResMaxCUs;
+  mok = mok && prepare_mfma_kernel<false>() && prepare_mfma_kernel<true>();
   info.cus = cus;
   info.resident_ok = ok;
+  info.mfma_ok = mok;
   info.ready = true;
   return DSPARK_OK;
 }
@@ -1241,6 +1634,7 @@ hipError_t launch_fused(const StepArgs& sa, bool in_kernel_pick, hipStream_t str
 // Which kernels one call enqueues, in order.
 struct Plan {
   bool resident;
+  bool resident_mfma;
   bool in_kernel_pick;
   int n_chunks;
   int chunk_cols;
@@ -1262,6 +1656,9 @@ int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
   // resident path: all positions in one persistent launch with W kept on chip
   plan->resident = !explicit_chunk && info.resident_ok && B <= kResRowsMax && r <= kResRank &&
                    V <= (int)kResIdxMask + 1 && plan->slice <= kResSlice;
+  plan->resident_mfma = !plan->resident && !explicit_chunk && info.mfma_ok && B > kResRowsMax &&
+                        B <= kMfRowsMax && r <= kResRank && V <= (int)kResIdxMask + 1 &&
+                        plan->slice <= kResSlice;
   plan->chunk_cols = chunk_cols;
   plan->n_chunks = (V + chunk_cols - 1) / chunk_cols;
   // one row: every workgroup picks the previous token itself (no pick launch)
@@ -1293,7 +1690,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   Plan plan;
   rc = make_plan(B, K, V, r, explicit_chunk ? chunk_cols : 0, &plan);
   if (rc != DSPARK_OK) return rc;
-  const bool resident = plan.resident;
+  const bool resident = plan.resident || plan.resident_mfma;
   const bool in_kernel_pick = plan.in_kernel_pick;
   const int n_chunks = plan.n_chunks;
   const int G = plan.G;
@@ -1313,24 +1710,39 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   const bool bf16 = base_dtype == DSPARK_BF16;
 
   if (resident) {
-    hipLaunchKernelGGL(res_clear, dim3(1), dim3(kThreads), 0, stream, ws.xkey, 2 * G * kResRowsMax, ws.fail);
+    const int n_clear = plan.resident_mfma ? 2 * G * kMfRowsMax + 2 * kMfRowsMax : 2 * G * kResRowsMax;
+    hipLaunchKernelGGL(res_clear, dim3((n_clear + 4095) / 4096), dim3(kThreads), 0, stream, ws.xkey, n_clear,
+                       ws.fail);
     if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
-    ResArgs ra;
-    ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
-    ra.temperature = temperature; ra.n_real = n_real; ra.logits = logits; ra.tokens = tokens;
-    ra.xkey = ws.xkey; ra.stat_part = ws.stat_part; ra.fail = ws.fail;
-    ra.B = B; ra.K = K; ra.V = V; ra.r = r; ra.slice = slice;
-    ra.spin_limit = 1u << 20;
-    const dim3 grid(G), block(kResThreads);
-    if (B == 1) {
-      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, true>), grid, block, kResLdsBytes, stream, ra);
-      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, false>), grid, block, kResLdsBytes, stream, ra);
-    } else if (B == 2) {
-      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, true>), grid, block, kResLdsBytes, stream, ra);
-      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, false>), grid, block, kResLdsBytes, stream, ra);
+    const dim3 grid(G);
+    if (plan.resident_mfma) {
+      MfArgs ma;
+      ma.base = base; ma.E = E; ma.W = W; ma.prev_token = prev_token; ma.seed = seed; ma.offset = offset;
+      ma.temperature = temperature; ma.n_real = n_real; ma.logits = logits; ma.tokens = tokens;
+      ma.xrow = ws.xkey; ma.xwin = ws.xkey + (size_t)2 * G * kMfRowsMax; ma.stat_part = ws.stat_part;
+      ma.fail = ws.fail;
+      ma.B = B; ma.K = K; ma.V = V; ma.r = r; ma.slice = slice;
+      ma.spin_limit = 1u << 20;
+      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true>), grid, dim3(kMfThreads), kMfLdsBytes, stream, ma);
+      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false>), grid, dim3(kMfThreads), kMfLdsBytes, stream, ma);
     } else {
-      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, true>), grid, block, kResLdsBytes, stream, ra);
-      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, false>), grid, block, kResLdsBytes, stream, ra);
+      ResArgs ra;
+      ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
+      ra.temperature = temperature; ra.n_real = n_real; ra.logits = logits; ra.tokens = tokens;
+      ra.xkey = ws.xkey; ra.stat_part = ws.stat_part; ra.fail = ws.fail;
+      ra.B = B; ra.K = K; ra.V = V; ra.r = r; ra.slice = slice;
+      ra.spin_limit = 1u << 20;
+      const dim3 block(kResThreads);
+      if (B == 1) {
+        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, true>), grid, block, kResLdsBytes, stream, ra);
+        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, false>), grid, block, kResLdsBytes, stream, ra);
+      } else if (B == 2) {
+        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, true>), grid, block, kResLdsBytes, stream, ra);
+        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, false>), grid, block, kResLdsBytes, stream, ra);
+      } else {
+        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, true>), grid, block, kResLdsBytes, stream, ra);
+        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, false>), grid, block, kResLdsBytes, stream, ra);
+      }
     }
     if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
   }
@@ -1395,6 +1807,8 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax),
       reinterpret_cast<const void*>(&res_clear),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true>),
   };
   for (const void* kfn : kernels)
     if (hipFuncGetAttributes(&attr, kfn) != hipSuccess) return DSPARK_ERR_HIP;
@@ -1451,7 +1865,7 @@ int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds) {
     if (kinds && n < max_kinds) kinds[n] = kind;
     ++n;
   };
-  if (plan.resident) {
+  if (plan.resident || plan.resident_mfma) {
     put(DSPARK_LAUNCH_CLEAR);
     put(DSPARK_LAUNCH_RESIDENT_BLOCK);
   } else {
