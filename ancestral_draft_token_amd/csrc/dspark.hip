@@ -1181,6 +1181,7 @@ struct MfArgs {
   uint64_t* xwin;      // [2][kMfRowsMax] tagged row winners
   Stat* stat_part;     // [K][B][G]
   int* fail;
+  float* sink;         // [64][4] stores of lanes without a real row or column
   int B, K, V, r, slice;
   unsigned spin_limit;
 };
@@ -1194,26 +1195,105 @@ struct MfRow {
 
 // Stage the embedding rows of N-tile nt (16 rows x 512 bytes) into an LDS
 // buffer: thread t copies 32 bytes (row t / 16, bytes 32 (t % 16) ..) of E[d[row]].
+// Rows beyond the batch and rank rows beyond r load a valid address and are
+// zeroed when stored (not when loaded: overwriting a register with a load in
+// flight would make the wave wait for it).
 struct ERow2 {
   uint4 lo, hi;
+  bool ok;
 };
+
+// Running argmax of one lane's perturbed scores, visited in increasing column
+// order: only a strictly larger score replaces the best, so ties keep the
+// lowest column, and NaN (never larger) never wins. kNoCol marks "empty"; the
+// first ordered score (even -inf) fills it.
+constexpr uint32_t kNoCol = 0xFFFFFFFFu;
+struct Best {
+  float z;
+  uint32_t v;
+};
+
+__device__ __forceinline__ void best_update4(Best& b, const float z[4], uint32_t v0) {
+  const float m = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));   // NaN only if all four are
+  const uint32_t j = z[0] == m ? 0u : (z[1] == m ? 1u : (z[2] == m ? 2u : 3u));
+  const bool take = m > b.z || (b.v == kNoCol && m == m);
+  b.z = take ? m : b.z;
+  b.v = take ? v0 + j : b.v;
+}
+
+__device__ __forceinline__ uint64_t best_key(const Best& b) { return b.v == kNoCol ? 0ull : score_key(b.z, b.v); }
+
+// Online softmax statistics of one lane: after each group of 4 scores,
+// l = sum over the lane's scores of exp(s - m) with m their running maximum.
+__device__ __forceinline__ void run_update4(Stat& st, const float s[4]) {
+  const float m4 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  const float mn = fmaxf(st.m, m4);
+  const float mr = mn == -INFINITY ? 0.0f : mn;   // nothing finite yet: every term is 0
+  float l = __fmul_rn(st.l, __expf(__fsub_rn(st.m, mr)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l = __fadd_rn(l, __expf(__fsub_rn(s[i], mr)));
+  st = Stat{mn, l};
+}
+
+// z = s + g for the Gumbel variate g of a Philox word x: u = ((x >> 9) + 1/2) 2^-23
+// (exact in float32), g = -ln(-ln u) = -ln2 * log2(-log2 u) - ln(ln 2), with the
+// hardware base-2 logarithm.
+__device__ __forceinline__ float perturb(float s, uint32_t x) {
+  const float u = __fmaf_rn((float)(x >> 9), 0x1p-23f, 0x1p-24f);
+  const float e2 = -__builtin_amdgcn_logf(u);
+  return __fmaf_rn(__builtin_amdgcn_logf(e2), -0.693147182f, __fadd_rn(s, 0.366512921f));
+}
+
+// Epilogue of one MFMA output fragment: columns v0..v0+3 of one row; returns
+// the float32 logits (the caller stores them). With kPartial, columns beyond
+// the slice (cols_ok false) take part as scores that never win (NaN) and
+// softmax terms that are 0.
+template <bool kBf16Base, bool kPartial>
+__device__ __forceinline__ float4 mf_epilogue(const RowState& rs, int k, uint32_t v0, const Base4<kBf16Base>& bv,
+                                              f32x4_t acc, bool cols_ok, Best& best, Stat& st) {
+  float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!rs.pad) widen_base4<kBf16Base>(bv, base);
+  float lg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(base[i], acc[i]);
+  const float4 out = make_float4(lg[0], lg[1], lg[2], lg[3]);
+  if (rs.greedy) {
+    if (kPartial && !cols_ok) lg[0] = lg[1] = lg[2] = lg[3] = __builtin_nanf("");
+    best_update4(best, lg, v0);
+    return out;
+  }
+  const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
+  const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+  float s[4], z[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = __fmul_rn(lg[i], rs.invT);
+    z[i] = perturb(s[i], xs[i]);
+    if (kPartial && !cols_ok) {
+      s[i] = -INFINITY;
+      z[i] = __builtin_nanf("");
+    }
+  }
+  best_update4(best, z, v0);
+  run_update4(st, s);
+  return out;
+}
 
 __device__ __forceinline__ ERow2 mf_load_erow(const MfArgs& a, const int* s_d, int nt, int t) {
   const int row = 16 * nt + t / 16, j16 = 16 * (t % 16);
   const bool ok = row < a.B && j16 < a.r;
   const uint16_t* src = a.E + (ok ? (size_t)s_d[row] * a.r + j16 : 0);
-  ERow2 v{*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8)};
-  if (!ok) v = ERow2{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-  return v;
+  return ERow2{*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8), ok};
 }
 
 __device__ __forceinline__ void mf_store_erow(unsigned char* ebuf, int t, const ERow2& v) {
+  const uint32_t m = v.ok ? ~0u : 0u;
   uint4* dst = reinterpret_cast<uint4*>(ebuf + (t / 16) * kMfERow + 32 * (t % 16));
-  dst[0] = v.lo;
-  dst[1] = v.hi;
+  dst[0] = make_uint4(v.lo.x & m, v.lo.y & m, v.lo.z & m, v.lo.w & m);
+  dst[1] = make_uint4(v.hi.x & m, v.hi.y & m, v.hi.z & m, v.hi.w & m);
 }
 
-template <bool kBf16Base>
+template <bool kBf16Base, bool kPartial>
 __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resident_mfma(MfArgs a) {
   extern __shared__ __align__(16) unsigned char mf_lds[];
   unsigned char* lds_w = mf_lds;                         // [17][8][64][16 B] fragments
@@ -1224,7 +1304,8 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   __shared__ int s_d[kMfRowsMax];                        // previous token per row
   __shared__ int s_fail;
 
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform
   const int g = blockIdx.x, G = gridDim.x;
   const int V = a.V, r = a.r, K = a.K, B = a.B;
   const int NT = (B + 15) / 16;
@@ -1306,11 +1387,14 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   }
   __syncthreads();
 
-  // ---- (3) the E rows of N-tiles 0 and 1 of position 0, prefetch of N-tile 2
-  ERow2 epre{make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+  // ---- (3) the E rows of N-tiles 0 and 1 of position 0. Every N-tile nt
+  // stores the rows of nt + 1 (held in epre) into the other buffer and
+  // prefetches nt + 2; rows past the batch are zeros, so the schedule has no
+  // branches. At a position start epre is stored at once as well, so no load
+  // is in flight in it when the first N-tile stores it again.
   mf_store_erow(lds_e, t, mf_load_erow(a, s_d, 0, t));
-  if (NT > 1) mf_store_erow(lds_e + 16 * kMfERow, t, mf_load_erow(a, s_d, 1, t));
-  if (NT > 2) epre = mf_load_erow(a, s_d, 2, t);
+  ERow2 epre = mf_load_erow(a, s_d, 1, t);
+  mf_store_erow(lds_e + 16 * kMfERow, t, epre);
 
   // the wave's tiles: i < 8 are VGPR tiles 8 wv + i; i >= 8 are LDS tiles 32 + wv + 4 (i - 8)
   auto tile_m = [&](int i) {
@@ -1321,6 +1405,48 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     const int m = tile_m(i);
     if ((i < kMfTilesPerWave || m < kMfRegTiles + kMfLdsTiles) && 16 * m < ncols) n_mine = i + 1;
   }
+
+  // this lane's row of (position k, N-tile nt): state, and the offset of (row, k, col0)
+  struct LaneRow {
+    RowState rs;
+    bool row_ok;   // a row of the batch
+    bool read;     // its base logits are read (not padding)
+    size_t off;
+  };
+  auto lane_row = [&](int k, int nt) {
+    LaneRow L{};
+    const int b = 16 * nt + lr;
+    if (k < K && b < B) {
+      const MfRow mr = s_row[b];
+      L.rs.invT = mr.invT;
+      L.rs.greedy = (mr.flags & 1u) != 0;
+      L.rs.pad = (mr.flags & 2u) != 0;
+      L.rs.key0 = mr.key0; L.rs.key1 = mr.key1; L.rs.ctr2 = mr.ctr2; L.rs.ctr3 = mr.ctr3;
+      L.row_ok = true;
+      L.read = !L.rs.pad;
+      L.off = ((size_t)b * K + k) * (size_t)V + col0;
+    }
+    return L;
+  };
+  // base offset of tile i of a lane row; 0 (a valid address, value unused) when there is none
+  auto base_at = [&](const LaneRow& L, int i) -> size_t {
+    const int c4 = 16 * tile_m(i) + 4 * lq;
+    return (L.read && i < n_mine && c4 < ncols) ? L.off + c4 : 0;
+  };
+  // the bias fragment of tile i (rank rows >= r are zero in both operands, so all 8 K-steps run)
+  auto tile_bias = [&](int i, const uint4 (&ef)[kMfKSteps]) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < kMfTilesPerWave) {
+#pragma unroll
+      for (int ks = 0; ks < kMfKSteps; ++ks) acc = mfma_bf16(wf[i][ks], ef[ks], acc);
+    } else {
+      const unsigned char* fb = lds_w + (size_t)(tile_m(i) - kMfRegTiles) * kMfKSteps * 1024 + lane * 16;
+#pragma unroll
+      for (int ks = 0; ks < kMfKSteps; ++ks)
+        acc = mfma_bf16(*reinterpret_cast<const uint4*>(fb + ks * 1024), ef[ks], acc);
+    }
+    return acc;
+  };
 
   __syncthreads();
 
@@ -1344,90 +1470,76 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     }
   };
 
+  // Base logits of each tile, one register set per tile (compile-time indices
+  // after unrolling, so nothing is copied while a load is in flight): tile
+  // i + 4 is loaded during tile i, and tiles 0..3 of the next N-tile (or of the
+  // next position's first N-tile, which does not depend on the token) during
+  // tiles 8..11.
+  Base4<kBf16Base> bq[kMfTilesMax];
+  {
+    const LaneRow L0 = lane_row(0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_base4<kBf16Base>(bq[i], a.base, base_at(L0, i));
+  }
+
   for (int k = 0; k < K; ++k) {
     for (int nt = 0; nt < NT; ++nt) {
       __syncthreads();   // E buffer nt & 1 is complete; s_rk[(nt - 1) & 1] is complete
       if (nt > 0) publish(k, nt - 1);
-      if (nt > 0 && nt + 1 < NT) mf_store_erow(lds_e + ((nt + 1) & 1) * 16 * kMfERow, t, epre);
-      if (nt > 0 && nt + 2 < NT) epre = mf_load_erow(a, s_d, nt + 2, t);
 
-      // B operand of this N-tile: lane = row lr, rank rows 32 ks + 8 lq .. (rank
-      // rows >= r are zero in both operands, so all 8 K-steps always run)
+      // B operand of this N-tile: lane = row lr, rank rows 32 ks + 8 lq ..
       uint4 ef[kMfKSteps];
       const unsigned char* eb = lds_e + (nt & 1) * 16 * kMfERow + lr * kMfERow + 16 * lq;
 #pragma unroll
       for (int ks = 0; ks < kMfKSteps; ++ks) ef[ks] = *reinterpret_cast<const uint4*>(eb + 64 * ks);
+      // the other buffer was last read in N-tile nt - 1, before the barrier above
+      mf_store_erow(lds_e + ((nt + 1) & 1) * 16 * kMfERow, t, epre);
+      epre = mf_load_erow(a, s_d, nt + 2, t);
 
-      const int b = 16 * nt + lr;
-      const bool row_ok = b < B;
-      RowState rs{};
-      if (row_ok) {
-        const MfRow mr = s_row[b];
-        rs.invT = mr.invT;
-        rs.greedy = (mr.flags & 1u) != 0;
-        rs.pad = (mr.flags & 2u) != 0;
-        rs.key0 = mr.key0; rs.key1 = mr.key1; rs.ctr2 = mr.ctr2; rs.ctr3 = mr.ctr3;
-      }
-      const size_t row_off = ((size_t)b * K + k) * (size_t)V;
-      uint64_t best = 0;
+      const LaneRow L = lane_row(k, nt);
+      const LaneRow Ln = nt + 1 < NT ? lane_row(k, nt + 1) : lane_row(k + 1, 0);
+      Best best{-INFINITY, kNoCol};
       Stat st{-INFINITY, 0.0f};
 
-      // base logits 4 tiles ahead, in rotating registers (no runtime-indexed arrays)
-      auto base_off = [&](int i) -> size_t {
-        const int c4 = 16 * tile_m(i) + 4 * lq;
-        return (row_ok && !rs.pad && i < n_mine && c4 < ncols) ? row_off + (size_t)(col0 + c4) : 0;
-      };
-      Base4<kBf16Base> b0, b1, b2, b3;
-      load_base4<kBf16Base>(b0, a.base, base_off(0));
-      load_base4<kBf16Base>(b1, a.base, base_off(1));
-      load_base4<kBf16Base>(b2, a.base, base_off(2));
-      load_base4<kBf16Base>(b3, a.base, base_off(3));
-
-#pragma unroll 1
-      for (int i = 0; i < n_mine; ++i) {
-        const int m = tile_m(i);
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (i < kMfTilesPerWave) {
-          // VGPR fragments need compile-time indices: one MFMA chain per case
-          switch (i) {
-#define DSPARK_MF_TILE(T)                                                          \
-  case T:                                                                          \
-    _Pragma("unroll") for (int ks = 0; ks < kMfKSteps; ++ks) acc = mfma_bf16(wf[T][ks], ef[ks], acc); \
-    break;
-            DSPARK_MF_TILE(0) DSPARK_MF_TILE(1) DSPARK_MF_TILE(2) DSPARK_MF_TILE(3)
-            DSPARK_MF_TILE(4) DSPARK_MF_TILE(5) DSPARK_MF_TILE(6) DSPARK_MF_TILE(7)
-#undef DSPARK_MF_TILE
-            default: break;
-          }
-        } else {
-          const unsigned char* fb = lds_w + (size_t)(m - kMfRegTiles) * kMfKSteps * 1024 + lane * 16;
+      // the bias of tile i + 1 is issued to the matrix cores before the epilogue of tile i
+      f32x4_t acc[2];
+      acc[0] = tile_bias(0, ef);
 #pragma unroll
-          for (int ks = 0; ks < kMfKSteps; ++ks)
-            acc = mfma_bf16(*reinterpret_cast<const uint4*>(fb + ks * 1024), ef[ks], acc);
+      for (int i = 0; i < kMfTilesMax; ++i) {
+        if (i + 4 < kMfTilesMax) load_base4<kBf16Base>(bq[i + 4], a.base, base_at(L, i + 4));
+        if (i >= 8 && i < 12) load_base4<kBf16Base>(bq[i - 8], a.base, base_at(Ln, i - 8));
+        if (i + 1 < kMfTilesMax && i + 1 < n_mine) acc[(i + 1) & 1] = tile_bias(i + 1, ef);
+        // One unconditional store per tile (to the sink when there is no
+        // tile, row or column) keeps the count of memory operations issued
+        // after each prefetch exact for the compiler's load waits; the base
+        // registers are consumed on both paths for the same reason.
+        float* out = a.sink + 4 * lane;
+        float4 lgv;
+        if (i < n_mine) {
+          const int c4 = 16 * tile_m(i) + 4 * lq;   // column offset in the slice
+          const bool cols_ok = !kPartial || c4 < ncols;
+          if (L.row_ok && cols_ok) out = a.logits + L.off + c4;
+          lgv = mf_epilogue<kBf16Base, kPartial>(L.rs, k, (uint32_t)(col0 + c4), bq[i], acc[i & 1], cols_ok,
+                                                 best, st);
+        } else {
+          float bw[4];
+          widen_base4<kBf16Base>(bq[i], bw);
+          lgv = make_float4(bw[0], bw[1], bw[2], bw[3]);
         }
-        const int c4 = 16 * m + 4 * lq;              // column offset in the slice
-        if (row_ok && c4 < ncols) {
-          const uint32_t v0 = (uint32_t)(col0 + c4);
-          float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (!rs.pad) widen_base4<kBf16Base>(b0, base);
-          const float bias[4] = {acc[0], acc[1], acc[2], acc[3]};
-          epilogue4(rs, k, v0, base, bias, a.logits + row_off + v0, best, st);
-        }
-        b0 = b1;
-        b1 = b2;
-        b2 = b3;
-        load_base4<kBf16Base>(b3, a.base, base_off(i + 4));
+        *reinterpret_cast<float4*>(out) = lgv;
+        __builtin_amdgcn_sched_barrier(0);
       }
       // lanes of one row (equal lane % 16) combine; lanes 0..15 hold the wave's partials
+      uint64_t key = best_key(best);
       for (int mask = 16; mask < 64; mask <<= 1) {
-        best = umax64(best, shfl_xor_u64(best, mask, 64));
+        key = umax64(key, shfl_xor_u64(key, mask, 64));
         Stat o;
         o.m = __shfl_xor(st.m, mask, 64);
         o.l = __shfl_xor(st.l, mask, 64);
         st = stat_merge(st, o);
       }
       if (lane < 16) {
-        s_rk[nt & 1][wv][lane] = best;
+        s_rk[nt & 1][wv][lane] = key;
         s_rs[nt & 1][wv][lane] = st;
       }
     }
@@ -1489,10 +1601,10 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     if (g == 0)
       for (int b = t; b < B; b += kMfThreads) a.tokens[(size_t)b * K + k] = s_d[b];
     if (k + 1 < K) {
-      // E rows of the next position's N-tiles 0 and 1, and the prefetch of N-tile 2
+      // E rows of the next position's N-tiles 0 and 1
       mf_store_erow(lds_e, t, mf_load_erow(a, s_d, 0, t));
-      if (NT > 1) mf_store_erow(lds_e + 16 * kMfERow, t, mf_load_erow(a, s_d, 1, t));
-      if (NT > 2) epre = mf_load_erow(a, s_d, 2, t);
+      epre = mf_load_erow(a, s_d, 1, t);
+      mf_store_erow(lds_e + 16 * kMfERow, t, epre);
     }
   }
 }
@@ -1509,6 +1621,7 @@ struct Workspace {
   uint64_t* xwin;          // resident MFMA path: [2][kMfRowsMax] row winners (follows xkey)
   Stat* stat_part;         // resident paths: [K][B][kResMaxCUs]
   int* fail;               // resident path: bounded-wait failure flag
+  float* sink;             // resident MFMA path: [64][4] discarded stores
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1525,7 +1638,7 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
   }
   const size_t o_rst = off; off = align_up(off + (size_t)B * K * sizeof(Stat), 256);
   const size_t o_e = off;   off = align_up(off + (size_t)B * r * sizeof(uint16_t), 256);
-  size_t o_x = 0, o_w = 0, o_sp = 0, o_f = 0;
+  size_t o_x = 0, o_w = 0, o_sp = 0, o_f = 0, o_s = 0;
   const bool resident_ws = B <= kMfRowsMax;
   if (resident_ws) {
     // exchange words of both resident kernels: [2][CUs][rows] then [2][rows] winners
@@ -1533,6 +1646,7 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
     o_w = off;  off = align_up(off + (size_t)2 * kMfRowsMax * sizeof(uint64_t), 256);
     o_sp = off; off = align_up(off + (size_t)K * B * kResMaxCUs * sizeof(Stat), 256);
     o_f = off;  off = align_up(off + sizeof(int), 256);
+    o_s = off;  off = align_up(off + 64 * 4 * sizeof(float), 256);
   }
   if (ws) {
     for (int i = 0; i < 2; ++i) {
@@ -1545,6 +1659,7 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
     ws->xwin = resident_ws ? reinterpret_cast<uint64_t*>(base + o_w) : nullptr;
     ws->stat_part = resident_ws ? reinterpret_cast<Stat*>(base + o_sp) : nullptr;
     ws->fail = resident_ws ? reinterpret_cast<int*>(base + o_f) : nullptr;
+    ws->sink = resident_ws ? reinterpret_cast<float*>(base + o_s) : nullptr;
   }
   return off;
 }
@@ -1571,13 +1686,13 @@ bool prepare_resident_kernel() {
   return occ >= 1;
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kPartial>
 bool prepare_mfma_kernel() {
-  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16>);
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16, kPartial>);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) != hipSuccess)
     return false;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kPartial>,
                                                    kMfThreads, kMfLdsBytes) != hipSuccess)
     return false;
   return occ >= 1;
@@ -1596,7 +1711,8 @@ int init_device() {
   ok = ok && prepare_resident_kernel<2, false>() && prepare_resident_kernel<2, true>();
   ok = ok && prepare_resident_kernel<4, false>() && prepare_resident_kernel<4, true>();
   bool mok = cus > 0 && cus <= kResMaxCUs;
-  mok = mok && prepare_mfma_kernel<false>() && prepare_mfma_kernel<true>();
+  mok = mok && prepare_mfma_kernel<false, false>() && prepare_mfma_kernel<true, false>();
+  mok = mok && prepare_mfma_kernel<false, true>() && prepare_mfma_kernel<true, true>();
   info.cus = cus;
   info.resident_ok = ok;
   info.mfma_ok = mok;
@@ -1656,9 +1772,11 @@ int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
   // resident path: all positions in one persistent launch with W kept on chip
   plan->resident = !explicit_chunk && info.resident_ok && B <= kResRowsMax && r <= kResRank &&
                    V <= (int)kResIdxMask + 1 && plan->slice <= kResSlice;
+  const int mf_slice = info.cus > 0 ? ((V + info.cus - 1) / info.cus + 15) / 16 * 16 : 0;
   plan->resident_mfma = !plan->resident && !explicit_chunk && info.mfma_ok && B > kResRowsMax &&
                         B <= kMfRowsMax && r <= kResRank && V <= (int)kResIdxMask + 1 &&
-                        plan->slice <= kResSlice;
+                        mf_slice <= kResSlice;
+  if (plan->resident_mfma) plan->slice = mf_slice;   // whole 16-column M-tiles
   plan->chunk_cols = chunk_cols;
   plan->n_chunks = (V + chunk_cols - 1) / chunk_cols;
   // one row: every workgroup picks the previous token itself (no pick launch)
@@ -1720,11 +1838,17 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
       ma.base = base; ma.E = E; ma.W = W; ma.prev_token = prev_token; ma.seed = seed; ma.offset = offset;
       ma.temperature = temperature; ma.n_real = n_real; ma.logits = logits; ma.tokens = tokens;
       ma.xrow = ws.xkey; ma.xwin = ws.xkey + (size_t)2 * G * kMfRowsMax; ma.stat_part = ws.stat_part;
-      ma.fail = ws.fail;
+      ma.fail = ws.fail; ma.sink = ws.sink;
       ma.B = B; ma.K = K; ma.V = V; ma.r = r; ma.slice = slice;
       ma.spin_limit = 1u << 20;
-      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true>), grid, dim3(kMfThreads), kMfLdsBytes, stream, ma);
-      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false>), grid, dim3(kMfThreads), kMfLdsBytes, stream, ma);
+      const dim3 mblock(kMfThreads);
+      if (V % 16 == 0) {
+        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, false>), grid, mblock, kMfLdsBytes, stream, ma);
+        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, false>), grid, mblock, kMfLdsBytes, stream, ma);
+      } else {
+        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, true>), grid, mblock, kMfLdsBytes, stream, ma);
+        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, true>), grid, mblock, kMfLdsBytes, stream, ma);
+      }
     } else {
       ResArgs ra;
       ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
@@ -1807,8 +1931,10 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax),
       reinterpret_cast<const void*>(&res_clear),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, true>),
   };
   for (const void* kfn : kernels)
     if (hipFuncGetAttributes(&attr, kfn) != hipSuccess) return DSPARK_ERR_HIP;
