@@ -597,12 +597,24 @@ __global__ __launch_bounds__(kThreads) void pick_and_gather(PickArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: proposal_softmax. Grid = (row, position) x column blocks; each
-// thread writes 4 consecutive entries of q. Sampling rows recompute
-// s = logit * invT exactly as the draw did; greedy rows get one-hot at d_k.
-// With last_from_partials (B == 1), the last position's token and (M, S) are
-// reduced here from its chunk partials; block 0 of that row stores them.
+// Kernel 3: proposal_softmax. Grid = (row, position) x column blocks of
+// kPropCols columns; thread t handles float4 j at column 4 (j * 256 + t) of
+// its block, so every load and store instruction of a wave is one contiguous
+// 1 KiB. All of a thread's logits loads are issued before the row's (M, S) is
+// merged, so the merge runs while they are in flight. Positions are visited
+// from last to first: the most recently written logits are read first, while
+// they may still be in the Infinity Cache. Logits are read and q written with
+// nontemporal hints (neither is touched again by this call). Sampling rows
+// recompute s = logit * invT exactly as the draw did; greedy rows get one-hot
+// at d_k. With last_from_partials (B == 1), the last position's token and
+// (M, S) are reduced here from its chunk partials; block 0 of that row stores
+// them.
 // ---------------------------------------------------------------------------
+constexpr int kPropVec = 8;                                 // float4 per thread
+constexpr int kPropCols = kThreads * 4 * kPropVec;          // 8192 columns per block
+
+typedef float fx4_t __attribute__((ext_vector_type(4)));
+
 struct PropArgs {
   const float* logits;
   const float* temperature;
@@ -618,39 +630,59 @@ struct PropArgs {
   int n_part;
 };
 
-__global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
-  __shared__ uint64_t s_key[kWaves];
-  __shared__ Stat s_stat[kWaves];
-  const int bk = blockIdx.x / a.blocks_per_row;
-  const int cb = blockIdx.x % a.blocks_per_row;
-  const int b = bk / a.K;
-  const int k = bk % a.K;
-  const int v0 = (cb * kThreads + threadIdx.x) * 4;
+// One block of proposal_softmax; kChecked: the row's last block, whose
+// accesses are bounds-checked (all others are unconditional, so the
+// compiler's waits for the loads stay exact).
+template <bool kChecked>
+__device__ __forceinline__ void proposal_block(const PropArgs& a, int b, int k, int cb, uint64_t* s_key,
+                                               Stat* s_stat) {
+  const int t = threadIdx.x;
+  const int bk = b * a.K + k;
   const float T = a.temperature[b];
   const bool greedy = !(T > 0.0f);
+  const size_t row = (size_t)bk * a.V;
+  const int c0 = cb * kPropCols + 4 * t;
+  auto in_row = [&](int v) { return !kChecked || v < a.V; };
+
+  // the first statistics partial of this thread is loaded before the logits,
+  // so the merge waits for it alone (loads complete in order)
+  const bool parts = a.n_part > 0 && !(a.last_from_partials && k == a.K - 1);
+  const Stat* ps = a.part_stat + ((size_t)k * a.B + b) * a.n_part;
+  Stat p0{-INFINITY, 0.0f};
+  fx4_t lg[kPropVec];
+  if (!greedy) {
+    if (parts) {
+      if (t < a.n_part) p0 = ps[t];
+      for (int i = t + kThreads; i < a.n_part; i += kThreads) p0 = stat_merge(p0, ps[i]);   // > 256 CUs
+    }
+#pragma unroll
+    for (int j = 0; j < kPropVec; ++j) {
+      const int v = c0 + j * kThreads * 4;
+      lg[j] = in_row(v) ? __builtin_nontemporal_load(reinterpret_cast<const fx4_t*>(a.logits + row + v))
+                        : fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
 
   Stat st;
   int tok;
   if (a.last_from_partials && k == a.K - 1) {
     uint64_t best = 0;
     Stat sst{-INFINITY, 0.0f};
-    for (int c = threadIdx.x; c < a.n_chunks; c += kThreads) {
+    for (int c = t; c < a.n_chunks; c += kThreads) {
       best = umax64(best, a.last_key[(size_t)b * a.n_chunks + c]);
       sst = stat_merge(sst, a.last_stat[(size_t)b * a.n_chunks + c]);
     }
     wg_reduce(best, sst, s_key, s_stat);
     st = sst;
     tok = clamp_token((int)key_token(best), a.V);
-    if (cb == 0 && threadIdx.x == 0) {
+    if (cb == 0 && t == 0) {
       a.tokens[bk] = tok;
       a.row_stat[bk] = st;
     }
-  } else if (a.n_part > 0) {
-    // the resident kernel leaves one statistics partial per workgroup
-    Stat sst{-INFINITY, 0.0f};
+  } else if (parts) {
+    // the resident kernels leave one statistics partial per workgroup
+    Stat sst = p0;
     uint64_t unused = 0;
-    const Stat* ps = a.part_stat + ((size_t)k * a.B + b) * a.n_part;
-    for (int i = threadIdx.x; i < a.n_part; i += kThreads) sst = stat_merge(sst, ps[i]);
     wg_reduce(unused, sst, s_key, s_stat);
     st = sst;
     tok = a.tokens[bk];
@@ -658,22 +690,46 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
     st = a.row_stat[bk];
     tok = a.tokens[bk];
   }
-  if (v0 >= a.V) return;
-  const size_t off = (size_t)bk * a.V + v0;
-  float4 out;
+
   if (greedy) {
-    out = make_float4(v0 == tok ? 1.0f : 0.0f, v0 + 1 == tok ? 1.0f : 0.0f,
-                      v0 + 2 == tok ? 1.0f : 0.0f, v0 + 3 == tok ? 1.0f : 0.0f);
-  } else {
-    const float invT = __fdiv_rn(1.0f, T);
-    const float invS = __fdiv_rn(1.0f, st.l);
-    const float4 lg = *reinterpret_cast<const float4*>(a.logits + off);
-    out.x = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg.x, invT), st.m)), invS);
-    out.y = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg.y, invT), st.m)), invS);
-    out.z = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg.z, invT), st.m)), invS);
-    out.w = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg.w, invT), st.m)), invS);
+#pragma unroll
+    for (int j = 0; j < kPropVec; ++j) {
+      const int v = c0 + j * kThreads * 4;
+      if (in_row(v)) {
+        const fx4_t out{v == tok ? 1.0f : 0.0f, v + 1 == tok ? 1.0f : 0.0f, v + 2 == tok ? 1.0f : 0.0f,
+                        v + 3 == tok ? 1.0f : 0.0f};
+        __builtin_nontemporal_store(out, reinterpret_cast<fx4_t*>(a.q + row + v));
+      }
+    }
+    return;
   }
-  *reinterpret_cast<float4*>(a.q + off) = out;
+  const float invT = __fdiv_rn(1.0f, T);
+  const float invS = __fdiv_rn(1.0f, st.l);
+#pragma unroll
+  for (int j = 0; j < kPropVec; ++j) {
+    const int v = c0 + j * kThreads * 4;
+    if (in_row(v)) {
+      fx4_t out;
+      out.x = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].x, invT), st.m)), invS);
+      out.y = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].y, invT), st.m)), invS);
+      out.z = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].z, invT), st.m)), invS);
+      out.w = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].w, invT), st.m)), invS);
+      __builtin_nontemporal_store(out, reinterpret_cast<fx4_t*>(a.q + row + v));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
+  __shared__ uint64_t s_key[kWaves];
+  __shared__ Stat s_stat[kWaves];
+  const int rk = blockIdx.x / a.blocks_per_row;
+  const int cb = blockIdx.x % a.blocks_per_row;
+  const int k = a.K - 1 - rk / a.B;
+  const int b = rk % a.B;
+  if ((cb + 1) * kPropCols <= a.V)
+    proposal_block<false>(a, b, k, cb, s_key, s_stat);
+  else
+    proposal_block<true>(a, b, k, cb, s_key, s_stat);
 }
 
 // ---------------------------------------------------------------------------
@@ -1901,7 +1957,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   pr.last_from_partials = (in_kernel_pick && !resident) ? 1 : 0;
   pr.part_stat = resident ? ws.stat_part : nullptr;
   pr.n_part = resident ? G : 0;
-  pr.blocks_per_row = (V + kThreads * 4 - 1) / (kThreads * 4);
+  pr.blocks_per_row = (V + kPropCols - 1) / kPropCols;
   const long long n_blocks = (long long)pr.blocks_per_row * B * K;
   if (n_blocks >= (1LL << 31)) return DSPARK_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(proposal_softmax, dim3((unsigned)n_blocks), dim3(kThreads), 0, stream, pr);
