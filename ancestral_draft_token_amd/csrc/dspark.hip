@@ -1208,6 +1208,8 @@ constexpr int kMfLdsTiles = kResSlice / 16 - kMfRegTiles;  // 17
 constexpr int kMfLdsPerWave = (kMfLdsTiles + kMfWaves - 1) / kMfWaves;   // 5
 constexpr int kMfTilesMax = kMfTilesPerWave + kMfLdsPerWave;            // 13
 constexpr int kMfKSteps = kResRank / 32;                   // 8
+constexpr int kMfAhead = 4;                                // base logits loaded this many tiles ahead
+constexpr int kMfNextAt = kMfTilesMax - 1 - kMfAhead;      // first tile loading the next N-tile's bases
 constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
 constexpr int kMfERow = 520;                               // bytes per staged E row (512 + pad)
 constexpr size_t kMfLdsW = (size_t)kMfLdsTiles * kMfKSteps * 64 * 16;   // 139,264 bytes
@@ -1269,12 +1271,24 @@ struct Best {
   uint32_t v;
 };
 
+// c ? a : b as a bit select (v_bfi), which the compiler keeps as straight-line
+// code instead of turning it into a branch around the costlier operand
+__device__ __forceinline__ uint32_t usel(bool c, uint32_t a, uint32_t b) {
+  const uint32_t m = 0u - (uint32_t)c;
+  return (a & m) | (b & ~m);
+}
+__device__ __forceinline__ float fsel(bool c, float a, float b) {
+  return __uint_as_float(usel(c, __float_as_uint(a), __float_as_uint(b)));
+}
+
 __device__ __forceinline__ void best_update4(Best& b, const float z[4], uint32_t v0) {
   const float m = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));   // NaN only if all four are
-  const uint32_t j = z[0] == m ? 0u : (z[1] == m ? 1u : (z[2] == m ? 2u : 3u));
-  const bool take = m > b.z || (b.v == kNoCol && m == m);
-  b.z = take ? m : b.z;
-  b.v = take ? v0 + j : b.v;
+  uint32_t j = usel(z[2] == m, 2u, 3u);
+  j = usel(z[1] == m, 1u, j);
+  j = usel(z[0] == m, 0u, j);
+  const bool take = (m > b.z) | ((b.v == kNoCol) & (m == m));
+  b.z = fsel(take, m, b.z);
+  b.v = usel(take, v0 + j, b.v);
 }
 
 __device__ __forceinline__ uint64_t best_key(const Best& b) { return b.v == kNoCol ? 0ull : score_key(b.z, b.v); }
@@ -1301,38 +1315,33 @@ __device__ __forceinline__ float perturb(float s, uint32_t x) {
 }
 
 // Epilogue of one MFMA output fragment: columns v0..v0+3 of one row; returns
-// the float32 logits (the caller stores them). With kPartial, columns beyond
-// the slice (cols_ok false) take part as scores that never win (NaN) and
-// softmax terms that are 0.
-template <bool kBf16Base, bool kPartial>
+// the float32 logits (the caller stores them). Straight-line code (no branch
+// on the row kind or on validity), so the whole tile is one basic block that
+// the scheduler can interleave with the matrix instructions of the next tile:
+// greedy rows rank the logits themselves; fragments without real columns
+// (ok false) take part as scores that never win (NaN) and softmax terms that
+// are 0. The statistics of greedy rows are not used.
+template <bool kBf16Base>
 __device__ __forceinline__ float4 mf_epilogue(const RowState& rs, int k, uint32_t v0, const Base4<kBf16Base>& bv,
-                                              f32x4_t acc, bool cols_ok, Best& best, Stat& st) {
-  float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (!rs.pad) widen_base4<kBf16Base>(bv, base);
+                                              f32x4_t acc, bool ok, Best& best, Stat& st) {
+  float base[4];
+  widen_base4<kBf16Base>(bv, base);
   float lg[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(base[i], acc[i]);
-  const float4 out = make_float4(lg[0], lg[1], lg[2], lg[3]);
-  if (rs.greedy) {
-    if (kPartial && !cols_ok) lg[0] = lg[1] = lg[2] = lg[3] = __builtin_nanf("");
-    best_update4(best, lg, v0);
-    return out;
-  }
+  for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(fsel(rs.pad, 0.0f, base[i]), acc[i]);
   const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
   const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
   float s[4], z[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     s[i] = __fmul_rn(lg[i], rs.invT);
-    z[i] = perturb(s[i], xs[i]);
-    if (kPartial && !cols_ok) {
-      s[i] = -INFINITY;
-      z[i] = __builtin_nanf("");
-    }
+    z[i] = fsel(rs.greedy, lg[i], perturb(s[i], xs[i]));
+    z[i] = fsel(ok, z[i], __builtin_nanf(""));
+    s[i] = fsel(ok, s[i], -INFINITY);
   }
   best_update4(best, z, v0);
   run_update4(st, s);
-  return out;
+  return make_float4(lg[0], lg[1], lg[2], lg[3]);
 }
 
 __device__ __forceinline__ ERow2 mf_load_erow(const MfArgs& a, const int* s_d, int nt, int t) {
@@ -1349,7 +1358,7 @@ __device__ __forceinline__ void mf_store_erow(unsigned char* ebuf, int t, const 
   dst[1] = make_uint4(v.hi.x & m, v.hi.y & m, v.hi.z & m, v.hi.w & m);
 }
 
-template <bool kBf16Base, bool kPartial>
+template <bool kBf16Base>
 __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resident_mfma(MfArgs a) {
   extern __shared__ __align__(16) unsigned char mf_lds[];
   unsigned char* lds_w = mf_lds;                         // [17][8][64][16 B] fragments
@@ -1496,7 +1505,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 #pragma unroll
       for (int ks = 0; ks < kMfKSteps; ++ks) acc = mfma_bf16(wf[i][ks], ef[ks], acc);
     } else {
-      const unsigned char* fb = lds_w + (size_t)(tile_m(i) - kMfRegTiles) * kMfKSteps * 1024 + lane * 16;
+      // a tile this wave does not have reads a valid one; its results are masked
+      const int ml = tile_m(i) < kMfRegTiles + kMfLdsTiles ? tile_m(i) - kMfRegTiles : 0;
+      const unsigned char* fb = lds_w + (size_t)ml * kMfKSteps * 1024 + lane * 16;
 #pragma unroll
       for (int ks = 0; ks < kMfKSteps; ++ks)
         acc = mfma_bf16(*reinterpret_cast<const uint4*>(fb + ks * 1024), ef[ks], acc);
@@ -1535,7 +1546,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   {
     const LaneRow L0 = lane_row(0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_base4<kBf16Base>(bq[i], a.base, base_at(L0, i));
+    for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base>(bq[i], a.base, base_at(L0, i));
   }
 
   for (int k = 0; k < K; ++k) {
@@ -1562,21 +1573,37 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       acc[0] = tile_bias(0, ef);
 #pragma unroll
       for (int i = 0; i < kMfTilesMax; ++i) {
-        if (i + 4 < kMfTilesMax) load_base4<kBf16Base>(bq[i + 4], a.base, base_at(L, i + 4));
-        if (i >= 8 && i < 12) load_base4<kBf16Base>(bq[i - 8], a.base, base_at(Ln, i - 8));
-        if (i + 1 < kMfTilesMax && i + 1 < n_mine) acc[(i + 1) & 1] = tile_bias(i + 1, ef);
-        // One unconditional store per tile (to the sink when there is no
-        // tile, row or column) keeps the count of memory operations issued
-        // after each prefetch exact for the compiler's load waits; the base
-        // registers are consumed on both paths for the same reason.
+        if (i + kMfAhead < kMfTilesMax) load_base4<kBf16Base>(bq[i + kMfAhead], a.base, base_at(L, i + kMfAhead));
+        if (i >= kMfNextAt && i < kMfNextAt + kMfAhead)
+          load_base4<kBf16Base>(bq[i - kMfNextAt], a.base, base_at(Ln, i - kMfNextAt));
+        // One store per tile, after the branch (to the sink when there is no
+        // tile, row or column), keeps the compiler's count of memory
+        // operations issued after each prefetch exact; the base registers are
+        // consumed on both paths for the same reason. Inside the branch the
+        // matrix instructions of tile i + 1 and the epilogue of tile i form
+        // one basic block (the epilogue has no branches), so the scheduler
+        // can interleave them.
         float* out = a.sink + 4 * lane;
         float4 lgv;
         if (i < n_mine) {
+          if (i + 1 < kMfTilesMax) acc[(i + 1) & 1] = tile_bias(i + 1, ef);
           const int c4 = 16 * tile_m(i) + 4 * lq;   // column offset in the slice
-          const bool cols_ok = !kPartial || c4 < ncols;
-          if (L.row_ok && cols_ok) out = a.logits + L.off + c4;
-          lgv = mf_epilogue<kBf16Base, kPartial>(L.rs, k, (uint32_t)(col0 + c4), bq[i], acc[i & 1], cols_ok,
-                                                 best, st);
+          const bool ok = c4 < ncols;
+          if (L.row_ok && ok) out = a.logits + L.off + c4;
+          lgv = mf_epilogue<kBf16Base>(L.rs, k, (uint32_t)(col0 + c4), bq[i], acc[i & 1], ok, best, st);
+          if (i + 1 < kMfTilesMax) {
+            // 8 x (one matrix instruction, 18 VALU): the chain of tile i + 1
+            // runs on the matrix cores while the epilogue of tile i issues
+            const bool from_lds = i + 1 >= kMfTilesPerWave;
+            if (from_lds) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#define DSPARK_MF_GROUP(n)                                                               \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
+  __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);                                    \
+  if (from_lds && (n) < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            DSPARK_MF_GROUP(0) DSPARK_MF_GROUP(1) DSPARK_MF_GROUP(2) DSPARK_MF_GROUP(3)
+            DSPARK_MF_GROUP(4) DSPARK_MF_GROUP(5) DSPARK_MF_GROUP(6) DSPARK_MF_GROUP(7)
+#undef DSPARK_MF_GROUP
+          }
         } else {
           float bw[4];
           widen_base4<kBf16Base>(bq[i], bw);
@@ -1742,13 +1769,13 @@ bool prepare_resident_kernel() {
   return occ >= 1;
 }
 
-template <bool kBf16, bool kPartial>
+template <bool kBf16>
 bool prepare_mfma_kernel() {
-  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16, kPartial>);
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16>);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) != hipSuccess)
     return false;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kPartial>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16>,
                                                    kMfThreads, kMfLdsBytes) != hipSuccess)
     return false;
   return occ >= 1;
@@ -1767,8 +1794,7 @@ int init_device() {
   ok = ok && prepare_resident_kernel<2, false>() && prepare_resident_kernel<2, true>();
   ok = ok && prepare_resident_kernel<4, false>() && prepare_resident_kernel<4, true>();
   bool mok = cus > 0 && cus <= kResMaxCUs;
-  mok = mok && prepare_mfma_kernel<false, false>() && prepare_mfma_kernel<true, false>();
-  mok = mok && prepare_mfma_kernel<false, true>() && prepare_mfma_kernel<true, true>();
+  mok = mok && prepare_mfma_kernel<false>() && prepare_mfma_kernel<true>();
   info.cus = cus;
   info.resident_ok = ok;
   info.mfma_ok = mok;
@@ -1898,13 +1924,8 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
       ma.B = B; ma.K = K; ma.V = V; ma.r = r; ma.slice = slice;
       ma.spin_limit = 1u << 20;
       const dim3 mblock(kMfThreads);
-      if (V % 16 == 0) {
-        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, false>), grid, mblock, kMfLdsBytes, stream, ma);
-        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, false>), grid, mblock, kMfLdsBytes, stream, ma);
-      } else {
-        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, true>), grid, mblock, kMfLdsBytes, stream, ma);
-        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, true>), grid, mblock, kMfLdsBytes, stream, ma);
-      }
+      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true>), grid, mblock, kMfLdsBytes, stream, ma);
+      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false>), grid, mblock, kMfLdsBytes, stream, ma);
     } else {
       ResArgs ra;
       ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
@@ -1987,10 +2008,8 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax),
       reinterpret_cast<const void*>(&res_clear),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true>),
   };
   for (const void* kfn : kernels)
     if (hipFuncGetAttributes(&attr, kfn) != hipSuccess) return DSPARK_ERR_HIP;
