@@ -184,12 +184,23 @@ struct Base4 {
   float4 f;
 };
 
+// Nontemporal: base logits are read once, and not letting them displace the
+// just-written logits in the Infinity Cache lets the proposal pass re-read
+// more of those from the cache instead of HBM.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
 template <bool kBf16Base>
 __device__ __forceinline__ void load_base4(Base4<kBf16Base>& bv, const void* base, size_t off) {
-  if (kBf16Base)
-    bv.h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
-  else
-    bv.f = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+  if (kBf16Base) {
+    const u32x2_t x =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(base) + off));
+    bv.h = make_uint2(x.x, x.y);
+  } else {
+    const f32x4v_t x =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(static_cast<const float*>(base) + off));
+    bv.f = make_float4(x.x, x.y, x.z, x.w);
+  }
 }
 
 template <bool kBf16Base>
@@ -1517,18 +1528,24 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 
   __syncthreads();
 
-  // combine the waves' partials of N-tile nt and publish each row's tagged word
+  // Combine the waves' partials of N-tile nt and publish each row's tagged
+  // word. Wave 1 does it (wave 0 may own one more tile than the others):
+  // lane = row (lane % 16) x wave (lane / 16), merged over the 4 lanes of a
+  // row in a fixed xor order.
   auto publish = [&](int k, int nt) {
-    if (t < 16) {
-      const int b = 16 * nt + t;
-      uint64_t kk = s_rk[nt & 1][0][t];
-      Stat ss = s_rs[nt & 1][0][t];
-#pragma unroll
-      for (int w = 1; w < kMfWaves; ++w) {
-        kk = umax64(kk, s_rk[nt & 1][w][t]);
-        ss = stat_merge(ss, s_rs[nt & 1][w][t]);
+    if (wv == 1) {
+      const int row = lane & 15, w = lane >> 4;
+      uint64_t kk = s_rk[nt & 1][w][row];
+      Stat ss = s_rs[nt & 1][w][row];
+      for (int mask = 16; mask < 64; mask <<= 1) {
+        kk = umax64(kk, shfl_xor_u64(kk, mask, 64));
+        Stat o;
+        o.m = __shfl_xor(ss.m, mask, 64);
+        o.l = __shfl_xor(ss.l, mask, 64);
+        ss = stat_merge(ss, o);
       }
-      if (b < B) {
+      const int b = 16 * nt + row;
+      if (lane < 16 && b < B) {
         a.stat_part[((size_t)k * B + b) * G + g] = ss;
         const uint64_t idx = kk ? kResIdxMask - (uint64_t)key_token(kk) : 0ull;
         const uint64_t word = ((uint64_t)(k + 1) << kResTagShift) | ((kk >> 32) << 18) | idx;
