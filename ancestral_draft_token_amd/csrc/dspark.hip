@@ -1355,11 +1355,23 @@ __device__ __forceinline__ float4 mf_epilogue(const RowState& rs, int k, uint32_
   return make_float4(lg[0], lg[1], lg[2], lg[3]);
 }
 
-__device__ __forceinline__ ERow2 mf_load_erow(const MfArgs& a, const int* s_d, int nt, int t) {
+struct ERowSrc {
+  const uint16_t* src;
+  bool ok;
+};
+
+__device__ __forceinline__ ERowSrc mf_erow_src(const MfArgs& a, const int* s_d, int nt, int t) {
   const int row = 16 * nt + t / 16, j16 = 16 * (t % 16);
   const bool ok = row < a.B && j16 < a.r;
-  const uint16_t* src = a.E + (ok ? (size_t)s_d[row] * a.r + j16 : 0);
-  return ERow2{*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 8), ok};
+  return ERowSrc{a.E + (ok ? (size_t)s_d[row] * a.r + j16 : 0), ok};
+}
+
+__device__ __forceinline__ ERow2 mf_load_erow(const ERowSrc& es) {
+  return ERow2{*reinterpret_cast<const uint4*>(es.src), *reinterpret_cast<const uint4*>(es.src + 8), es.ok};
+}
+
+__device__ __forceinline__ ERow2 mf_load_erow(const MfArgs& a, const int* s_d, int nt, int t) {
+  return mf_load_erow(mf_erow_src(a, s_d, nt, t));
 }
 
 __device__ __forceinline__ void mf_store_erow(unsigned char* ebuf, int t, const ERow2& v) {
@@ -1560,14 +1572,15 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // next position's first N-tile, which does not depend on the token) during
   // tiles 8..11.
   Base4<kBf16Base> bq[kMfTilesMax];
-  {
-    const LaneRow L0 = lane_row(0, 0);
+  LaneRow L = lane_row(0, 0);   // this N-tile's row of the lane (carried from the previous N-tile)
 #pragma unroll
-    for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base>(bq[i], a.base, base_at(L0, i));
-  }
+  for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base>(bq[i], a.base, base_at(L, i));
 
   for (int k = 0; k < K; ++k) {
     for (int nt = 0; nt < NT; ++nt) {
+      // source of the E rows of N-tile nt + 2 (tokens are fixed within a position),
+      // read before the barrier so its latency overlaps the wait
+      const ERowSrc es = mf_erow_src(a, s_d, nt + 2, t);
       __syncthreads();   // E buffer nt & 1 is complete; s_rk[(nt - 1) & 1] is complete
       if (nt > 0) publish(k, nt - 1);
 
@@ -1578,9 +1591,8 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       for (int ks = 0; ks < kMfKSteps; ++ks) ef[ks] = *reinterpret_cast<const uint4*>(eb + 64 * ks);
       // the other buffer was last read in N-tile nt - 1, before the barrier above
       mf_store_erow(lds_e + ((nt + 1) & 1) * 16 * kMfERow, t, epre);
-      epre = mf_load_erow(a, s_d, nt + 2, t);
+      epre = mf_load_erow(es);
 
-      const LaneRow L = lane_row(k, nt);
       const LaneRow Ln = nt + 1 < NT ? lane_row(k, nt + 1) : lane_row(k + 1, 0);
       Best best{-INFINITY, kNoCol};
       Stat st{-INFINITY, 0.0f};
@@ -1642,6 +1654,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
         s_rk[nt & 1][wv][lane] = key;
         s_rs[nt & 1][wv][lane] = st;
       }
+      L = Ln;
     }
     __syncthreads();
     publish(k, NT - 1);
