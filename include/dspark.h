@@ -152,12 +152,13 @@ typedef enum {
  * sizes, in order: writes up to max_kinds dspark_launch_kind_t values to
  * `kinds` (host memory, may be NULL) and returns the launch count, or a
  * negative status. Three plans exist:
- *   - resident (B <= 4, r <= 256, V <= 2^18 and V <= 784 x the device's CU
- *     count): CLEAR, RESIDENT_BLOCK, PROPOSAL. One persistent launch runs all K
- *     positions; each workgroup keeps its slice of W on chip for the block.
- *     It needs every workgroup resident at once (one per compute unit); its
- *     device-side waits are bounded, and if one expires the call's tokens are
- *     -1 instead of hanging.
+ *   - resident (r <= 256, V <= 2^18, V <= 784 x the device's CU count, and
+ *     B <= 128): CLEAR, RESIDENT_BLOCK, PROPOSAL. One persistent launch runs
+ *     all K positions; each workgroup keeps its slice of W on chip for the
+ *     block (B <= 4: a VALU GEMV with 512 threads; 4 < B <= 128: bf16 MFMA
+ *     tiles with 256 threads). It needs every workgroup resident at once (one
+ *     per compute unit); its device-side waits are bounded, and if one
+ *     expires the call's tokens are -1 instead of hanging.
  *   - B == 1 otherwise: K x FUSED_POSITION, PROPOSAL (each fused kernel picks
  *     the previous position's token itself).
  *   - otherwise: K x (FUSED_POSITION, PICK), PROPOSAL.
