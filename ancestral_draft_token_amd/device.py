@@ -17,7 +17,8 @@ from .inputs import Workload
 
 
 class DeviceProblem:
-    def __init__(self, w: Workload, device: str = "cuda:0", chunk_cols: Optional[int] = None):
+    def __init__(self, w: Workload, device: str = "cuda:0", chunk_cols: Optional[int] = None,
+                 workspace: Optional[torch.Tensor] = None):
         self.w = w
         self.device = torch.device(device)
         self.chunk_cols = chunk_cols
@@ -42,7 +43,13 @@ class DeviceProblem:
         self.logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
         self.q = torch.empty((B, K, V), dtype=torch.float32, device=dev)
         self.ws_bytes = dspark_workspace_bytes(B, K, V, r)
-        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            # a workspace shared by several problems (calls run one at a time)
+            if workspace.numel() * workspace.element_size() < self.ws_bytes:
+                raise ValueError("shared workspace is too small")
+            self.workspace = workspace
+        else:
+            self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def enqueue(self, stream=None, **overrides) -> int:
         """Enqueue one block on ``stream`` (torch stream / raw handle / None = current)."""

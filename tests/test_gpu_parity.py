@@ -161,3 +161,36 @@ def test_resident_and_streaming_plans_agree():
     assert bool((a.tokens == b.tokens).all())
     assert float((a.logits - b.logits).abs().max()) <= parity.LOGIT_ATOL
     assert float((a.q - b.q).abs().max()) <= parity.Q_ATOL
+
+
+def test_one_workspace_across_calls():
+    """One workspace serves calls of different B and K in turn (each call clears
+    the exchange words it uses, so nothing left by an earlier call with other
+    sizes can be taken for a current word); every call matches the oracle on
+    sampled rows."""
+    import torch
+    from ancestral_draft_token_amd import dspark_workspace_bytes
+    from ancestral_draft_token_amd.device import DeviceProblem
+    cases = [
+        ("b96", dict(make=inputs.large_padded, kw={}), [0, 95]),
+        ("b8_k1", dict(make=inputs.small_batch, kw=dict(K=1)), [0, 7]),
+        ("b40_k3", dict(make=inputs.small_batch, kw=dict(B=40, K=3)), [1, 39]),
+        ("b2", dict(make=inputs.small_batch, kw=dict(B=2)), [0, 1]),
+        ("b4_k1", dict(make=inputs.small_batch, kw=dict(B=4, K=1)), [2, 3]),
+        ("b3", dict(make=inputs.small_batch, kw=dict(B=3)), [0, 2]),
+        ("b96_again", dict(make=inputs.large_padded, kw={}), [3, 88]),
+    ]
+    ws_bytes = max(dspark_workspace_bytes(96, 7, 200064, 256), dspark_workspace_bytes(40, 7, 200064, 256))
+    shared = torch.full((ws_bytes,), 0x5A, dtype=torch.uint8, device="cuda:0")   # not zeroed
+    for name, c, rows in cases:
+        w = c["make"](**c["kw"])
+        say(f"shared workspace: {name} B={w.B} K={w.K}")
+        p = DeviceProblem(w, workspace=shared)
+        p.enqueue()
+        torch.cuda.synchronize()
+        assert bool((p.tokens >= 0).all()), name
+        sub, order = w.subset_rows(rows)
+        t, l, q = rows_to_host(p, order)
+        rep = parity.check(sub, t, l, q)
+        say(f"parity ok {name} {rep.as_dict()}")
+        del p
