@@ -1230,7 +1230,19 @@ constexpr size_t kMfLdsBytes = kMfLdsW + kMfLdsE;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4_t mfma_bf16(uint4 a, uint4 b, f32x4_t c) {
+// Register-resident W fragments are defined in AGPRs by an empty asm whose
+// output is tied to its input with the AGPR constraint. The instruction reads
+// its A operand from either register file, so the builtin then takes them
+// straight from AGPRs; without this the register allocator parks them in
+// AGPRs on its own and copies each one back to VGPRs before every use (four
+// VALU moves per instruction).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t in_agpr(u32x4_t v) {
+  u32x4_t r;
+  asm volatile("; W fragment kept in AGPRs %0" : "=a"(r) : "0"(v));
+  return r;
+}
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
@@ -1435,7 +1447,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // ---- (2) VGPR M-tiles 8w..8w+7, staged through this wave's 4 KB of the (not yet
   // used) E region, 16 rank rows at a time: lanes of quads 0,1 take rows 0..15 of a
   // K-step, quads 2,3 rows 16..31
-  uint4 wf[kMfTilesPerWave][kMfKSteps];
+  u32x4_t wf[kMfTilesPerWave][kMfKSteps];   // A fragments, kept in AGPRs
   {
     unsigned char* stage = lds_e + (size_t)wv * 4096;   // [16 rows][128 columns] bf16
     const int cbase = 128 * wv;                         // first column of the wave's tiles
@@ -1470,7 +1482,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int mt = 0; mt < kMfTilesPerWave; ++mt) wf[mt][ks] = make_uint4(d[mt][0], d[mt][1], d[mt][2], d[mt][3]);
+      for (int mt = 0; mt < kMfTilesPerWave; ++mt) wf[mt][ks] = in_agpr(u32x4_t{d[mt][0], d[mt][1], d[mt][2], d[mt][3]});
     }
   }
   __syncthreads();
@@ -1533,7 +1545,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       const unsigned char* fb = lds_w + (size_t)ml * kMfKSteps * 1024 + lane * 16;
 #pragma unroll
       for (int ks = 0; ks < kMfKSteps; ++ks)
-        acc = mfma_bf16(*reinterpret_cast<const uint4*>(fb + ks * 1024), ef[ks], acc);
+        acc = mfma_bf16(*reinterpret_cast<const u32x4_t*>(fb + ks * 1024), ef[ks], acc);
     }
     return acc;
   };
