@@ -60,8 +60,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     // full 64-bit products: one v_mad_u64_u32 each instead of a mul_lo/mul_hi pair
     const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c.x;
     const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
-    c = make_uint4((uint32_t)(pb >> 32) ^ c.y ^ k0, (uint32_t)pb, (uint32_t)(pa >> 32) ^ c.w ^ k1,
-                   (uint32_t)pa);
+    // three-input exclusive or in one instruction (v_bitop3_b32, truth table 0x96)
+    c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c.y, k0, 0x96), (uint32_t)pb,
+                   __builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c.w, k1, 0x96), (uint32_t)pa);
   }
   return c;
 }
