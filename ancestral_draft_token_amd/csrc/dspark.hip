@@ -1224,6 +1224,8 @@ constexpr int kMfAhead = 4;                                // base logits loaded
 constexpr int kMfNextAt = kMfTilesMax - 1 - kMfAhead;      // first tile loading the next N-tile's bases
 constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
 constexpr int kMfERow = 520;                               // bytes per staged E row (512 + pad)
+constexpr int kMfSinkFloats = 1024;                        // sink: stores of lanes without a row or column
+constexpr int kMfZeroWords = 512;                          // 4 KB of zeros: base logits of rows that have none
 constexpr size_t kMfLdsW = (size_t)kMfLdsTiles * kMfKSteps * 64 * 16;   // 139,264 bytes
 constexpr size_t kMfLdsE = (size_t)2 * 16 * kMfERow;                    // 16,640 bytes
 constexpr size_t kMfLdsBytes = kMfLdsW + kMfLdsE;
@@ -1263,14 +1265,15 @@ struct MfArgs {
   uint64_t* xwin;      // [2][kMfRowsMax] tagged row winners
   Stat* stat_part;     // [K][B][G]
   int* fail;
-  float* sink;         // [64][4] stores of lanes without a real row or column
+  float* sink;         // [kMfSinkFloats] stores of lanes without a real row or column
+  const void* zeros;   // [kMfZeroWords] zeroed words: the base logits of padding rows
   int B, K, V, r, slice;
   unsigned spin_limit;
 };
 
 // Row state kept in LDS for the whole launch (temperature, slot, padding).
 struct MfRow {
-  float invT;
+  float invT;            // 1/T; 1 for greedy rows
   uint32_t flags;        // bit 0: greedy, bit 1: padding
   uint32_t key0, key1, ctr2, ctr3;
 };
@@ -1329,39 +1332,56 @@ __device__ __forceinline__ void run_update4(Stat& st, const float s[4]) {
   st = Stat{mn, l};
 }
 
-// z = s + g for the Gumbel variate g of a Philox word x: u = ((x >> 9) + 1/2) 2^-23
-// (exact in float32), g = -ln(-ln u) = -ln2 * log2(-log2 u) - ln(ln 2), with the
-// hardware base-2 logarithm.
-__device__ __forceinline__ float perturb(float s, uint32_t x) {
-  const float u = __fmaf_rn((float)(x >> 9), 0x1p-23f, 0x1p-24f);
-  const float e2 = -__builtin_amdgcn_logf(u);
-  return __fmaf_rn(__builtin_amdgcn_logf(e2), -0.693147182f, __fadd_rn(s, 0.366512921f));
+// log2(-log2 u) for u = ((x >> 9) + 1/2) 2^-23 of a Philox word x, with the
+// hardware base-2 logarithm; the Gumbel variate is g = -ln(-ln u) =
+// -ln2 * log2(-log2 u) - ln(ln 2). u is formed from bits: the float with
+// exponent 0 and mantissa x >> 9 (one alignbit) is 1 + (x >> 9) 2^-23, and
+// subtracting 1 - 2^-24 from it is exact, giving the same u as the integer
+// conversion.
+__device__ __forceinline__ float gumbel_log2(uint32_t x) {
+  const float f = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, x, 9));
+  const float u = __fsub_rn(f, 0x1.fffffep-1f);
+  return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
 }
+
+// This lane's row of one (position, N-tile): its Philox slot, the scale 1/T and
+// the Gumbel coefficient (greedy rows: 1 and 0, which makes the perturbed
+// score the logit itself), where its base logits are read (a zeroed region
+// for padding rows and for rows past the batch) and where its logits go (the
+// sink for rows past the batch).
+struct MfLane {
+  float invT, gco;
+  uint32_t key0, key1, ctr2, ctr3;
+  const unsigned char* bp;   // base logits of (row, position, first column of the slice)
+  float* op;                 // logits of the same
+};
 
 // Epilogue of one MFMA output fragment: columns v0..v0+3 of one row; returns
 // the float32 logits (the caller stores them). Straight-line code (no branch
-// on the row kind or on validity), so the whole tile is one basic block that
-// the scheduler can interleave with the matrix instructions of the next tile:
-// greedy rows rank the logits themselves; fragments without real columns
-// (ok false) take part as scores that never win (NaN) and softmax terms that
-// are 0. The statistics of greedy rows are not used.
-template <bool kBf16Base>
-__device__ __forceinline__ float4 mf_epilogue(const RowState& rs, int k, uint32_t v0, const Base4<kBf16Base>& bv,
+// on the row kind), so the whole tile is one basic block that the scheduler
+// can interleave with the matrix instructions of the next tile. The ranked
+// score is z = s + gco * log2(-log2 u): with gco = -ln 2 that is s + g + ln(ln 2)
+// for the Gumbel variate g, a shift by one constant for the whole row, so the
+// argmax is that of s + g. kRagged (a vocabulary that is not a multiple of 16):
+// fragments without real columns (ok false) take part as scores that never win
+// (NaN) and softmax terms that are 0. The statistics of greedy rows are not used.
+template <bool kBf16Base, bool kRagged>
+__device__ __forceinline__ float4 mf_epilogue(const MfLane& L, int k, uint32_t v0, const Base4<kBf16Base>& bv,
                                               f32x4_t acc, bool ok, Best& best, Stat& st) {
   float base[4];
   widen_base4<kBf16Base>(bv, base);
-  float lg[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(fsel(rs.pad, 0.0f, base[i]), acc[i]);
-  const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
+  const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, L.ctr2, L.ctr3), L.key0, L.key1);
   const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-  float s[4], z[4];
+  float lg[4], s[4], z[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s[i] = __fmul_rn(lg[i], rs.invT);
-    z[i] = fsel(rs.greedy, lg[i], perturb(s[i], xs[i]));
-    z[i] = fsel(ok, z[i], __builtin_nanf(""));
-    s[i] = fsel(ok, s[i], -INFINITY);
+    lg[i] = __fadd_rn(base[i], acc[i]);
+    s[i] = __fmul_rn(lg[i], L.invT);
+    z[i] = __fmaf_rn(gumbel_log2(xs[i]), L.gco, s[i]);
+    if (kRagged) {
+      z[i] = fsel(ok, z[i], __builtin_nanf(""));
+      s[i] = fsel(ok, s[i], -INFINITY);
+    }
   }
   best_update4(best, z, v0);
   run_update4(st, s);
@@ -1394,7 +1414,7 @@ __device__ __forceinline__ void mf_store_erow(unsigned char* ebuf, int t, const 
   dst[1] = make_uint4(v.hi.x & m, v.hi.y & m, v.hi.z & m, v.hi.w & m);
 }
 
-template <bool kBf16Base>
+template <bool kBf16Base, bool kRagged>
 __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resident_mfma(MfArgs a) {
   extern __shared__ __align__(16) unsigned char mf_lds[];
   unsigned char* lds_w = mf_lds;                         // [17][8][64][16 B] fragments
@@ -1419,7 +1439,8 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   if (t == 0) s_fail = 0;
   for (int b = t; b < B; b += kMfThreads) {
     const RowState rs = row_state(a.temperature, a.seed, a.offset, b, n_real);
-    s_row[b] = MfRow{rs.invT, (rs.greedy ? 1u : 0u) | (rs.pad ? 2u : 0u), rs.key0, rs.key1, rs.ctr2, rs.ctr3};
+    s_row[b] = MfRow{rs.greedy ? 1.0f : rs.invT, (rs.greedy ? 1u : 0u) | (rs.pad ? 2u : 0u), rs.key0, rs.key1,
+                     rs.ctr2, rs.ctr3};
     s_d[b] = clamp_token(a.prev_token[b], V);
   }
 
@@ -1507,35 +1528,36 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     if ((i < kMfTilesPerWave || m < kMfRegTiles + kMfLdsTiles) && 16 * m < ncols) n_mine = i + 1;
   }
 
-  // this lane's row of (position k, N-tile nt): state, and the offset of (row, k, col0)
-  struct LaneRow {
-    RowState rs;
-    bool row_ok;   // a row of the batch
-    bool read;     // its base logits are read (not padding)
-    size_t off;
-  };
-  auto lane_row = [&](int k, int nt) {
-    LaneRow L{};
+  // this lane's row of (position k, N-tile nt)
+  constexpr int kEsz = kBf16Base ? 2 : 4;   // bytes per base logit
+  auto lane_base = [&](int k, int nt) -> const unsigned char* {
     const int b = 16 * nt + lr;
-    if (k < K && b < B) {
-      const MfRow mr = s_row[b];
-      L.rs.invT = mr.invT;
-      L.rs.greedy = (mr.flags & 1u) != 0;
-      L.rs.pad = (mr.flags & 2u) != 0;
-      L.rs.key0 = mr.key0; L.rs.key1 = mr.key1; L.rs.ctr2 = mr.ctr2; L.rs.ctr3 = mr.ctr3;
-      L.row_ok = true;
-      L.read = !L.rs.pad;
-      L.off = ((size_t)b * K + k) * (size_t)V + col0;
-    }
+    const bool read = k < K && b < B && !(s_row[b].flags & 2u);
+    return read ? static_cast<const unsigned char*>(a.base) + (((size_t)b * K + k) * (size_t)V + col0) * kEsz
+                : static_cast<const unsigned char*>(a.zeros);
+  };
+  auto lane_row = [&](int k, int nt, const unsigned char* bp) {
+    MfLane L;
+    const int b = 16 * nt + lr;
+    const bool real = b < B;
+    const MfRow mr = s_row[real ? b : 0];
+    L.invT = mr.invT;
+    L.gco = (mr.flags & 1u) ? 0.0f : -0.693147182f;
+    L.key0 = mr.key0; L.key1 = mr.key1; L.ctr2 = mr.ctr2; L.ctr3 = mr.ctr3;
+    L.bp = bp;
+    L.op = real ? a.logits + ((size_t)b * K + k) * (size_t)V + col0 : a.sink;
     return L;
   };
-  // base offset of tile i of a lane row; 0 (a valid address, value unused) when there is none
-  auto base_at = [&](const LaneRow& L, int i) -> size_t {
+  // base logits of tile i of a lane row (its first column when the tile has
+  // none here: a valid address, the value unused)
+  auto base_at = [&](const unsigned char* bp, int i) -> const void* {
     const int c4 = 16 * tile_m(i) + 4 * lq;
-    return (L.read && i < n_mine && c4 < ncols) ? L.off + c4 : 0;
+    const bool has = i < n_mine && (!kRagged || c4 < ncols);
+    return bp + (has ? c4 : 0) * kEsz;
   };
-  // the bias fragment of tile i (rank rows >= r are zero in both operands, so all 8 K-steps run)
-  auto tile_bias = [&](int i, const uint4 (&ef)[kMfKSteps]) {
+  // the bias fragment of tile i (rank rows >= r are zero in both operands, so all 8 K-steps run);
+  // an LDS tile also returns its last A fragment in `last` (see the keep-alive below)
+  auto tile_bias = [&](int i, const uint4 (&ef)[kMfKSteps], u32x4_t& last) {
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (i < kMfTilesPerWave) {
 #pragma unroll
@@ -1545,8 +1567,10 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       const int ml = tile_m(i) < kMfRegTiles + kMfLdsTiles ? tile_m(i) - kMfRegTiles : 0;
       const unsigned char* fb = lds_w + (size_t)ml * kMfKSteps * 1024 + lane * 16;
 #pragma unroll
-      for (int ks = 0; ks < kMfKSteps; ++ks)
-        acc = mfma_bf16(*reinterpret_cast<const u32x4_t*>(fb + ks * 1024), ef[ks], acc);
+      for (int ks = 0; ks < kMfKSteps; ++ks) {
+        last = *reinterpret_cast<const u32x4_t*>(fb + ks * 1024);
+        acc = mfma_bf16(last, ef[ks], acc);
+      }
     }
     return acc;
   };
@@ -1585,9 +1609,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // next position's first N-tile, which does not depend on the token) during
   // tiles 8..11.
   Base4<kBf16Base> bq[kMfTilesMax];
-  LaneRow L = lane_row(0, 0);   // this N-tile's row of the lane (carried from the previous N-tile)
+  const unsigned char* bp = lane_base(0, 0);   // base logits of this N-tile's row of the lane
 #pragma unroll
-  for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base>(bq[i], a.base, base_at(L, i));
+  for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base>(bq[i], base_at(bp, i), 0);
 
   for (int k = 0; k < K; ++k) {
     for (int nt = 0; nt < NT; ++nt) {
@@ -1606,18 +1630,21 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       mf_store_erow(lds_e + ((nt + 1) & 1) * 16 * kMfERow, t, epre);
       epre = mf_load_erow(es);
 
-      const LaneRow Ln = nt + 1 < NT ? lane_row(k, nt + 1) : lane_row(k + 1, 0);
+      // the lane's row here; only the base pointer of the next one is kept (for its prefetch)
+      const MfLane L = lane_row(k, nt, bp);
+      const unsigned char* bpn = nt + 1 < NT ? lane_base(k, nt + 1) : lane_base(k + 1, 0);
       Best best{-INFINITY, kNoCol};
       Stat st{-INFINITY, 0.0f};
 
       // the bias of tile i + 1 is issued to the matrix cores before the epilogue of tile i
       f32x4_t acc[2];
-      acc[0] = tile_bias(0, ef);
+      u32x4_t afrag;   // last A fragment of an LDS tile's chain
+      acc[0] = tile_bias(0, ef, afrag);
 #pragma unroll
       for (int i = 0; i < kMfTilesMax; ++i) {
-        if (i + kMfAhead < kMfTilesMax) load_base4<kBf16Base>(bq[i + kMfAhead], a.base, base_at(L, i + kMfAhead));
+        if (i + kMfAhead < kMfTilesMax) load_base4<kBf16Base>(bq[i + kMfAhead], base_at(bp, i + kMfAhead), 0);
         if (i >= kMfNextAt && i < kMfNextAt + kMfAhead)
-          load_base4<kBf16Base>(bq[i - kMfNextAt], a.base, base_at(Ln, i - kMfNextAt));
+          load_base4<kBf16Base>(bq[i - kMfNextAt], base_at(bpn, i - kMfNextAt), 0);
         // One store per tile, after the branch (to the sink when there is no
         // tile, row or column), keeps the compiler's count of memory
         // operations issued after each prefetch exact; the base registers are
@@ -1628,15 +1655,30 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
         float* out = a.sink + 4 * lane;
         float4 lgv;
         if (i < n_mine) {
-          if (i + 1 < kMfTilesMax) acc[(i + 1) & 1] = tile_bias(i + 1, ef);
+          if (i + 1 < kMfTilesMax) acc[(i + 1) & 1] = tile_bias(i + 1, ef, afrag);
           const int c4 = 16 * tile_m(i) + 4 * lq;   // column offset in the slice
-          const bool ok = c4 < ncols;
-          if (L.row_ok && ok) out = a.logits + L.off + c4;
-          lgv = mf_epilogue<kBf16Base>(L.rs, k, (uint32_t)(col0 + c4), bq[i], acc[i & 1], ok, best, st);
+          const bool ok = !kRagged || c4 < ncols;
+          out = ok ? L.op + c4 : a.sink + c4;
+          lgv = mf_epilogue<kBf16Base, kRagged>(L, k, (uint32_t)(col0 + c4), bq[i], acc[i & 1], ok, best, st);
           if (i + 1 < kMfTilesMax) {
             // 8 x (one matrix instruction, 18 VALU): the chain of tile i + 1
             // runs on the matrix cores while the epilogue of tile i issues
             const bool from_lds = i + 1 >= kMfTilesPerWave;
+            if (from_lds) {
+              // Keep-alive: the last A fragment of the chain (and, after the
+              // N-tile's last chain, the B fragments of its last K-steps) stay
+              // allocated until the epilogue's result exists, so no VALU
+              // result of the epilogue is written into those registers right
+              // after the matrix instructions that read them.
+              float lx = lgv.x;
+              asm volatile("; A fragment live until here %1" : "+v"(lx) : "v"(afrag));
+              if (i + 2 == kMfTilesMax) {
+                auto v4 = [](uint4 e) { return u32x4_t{e.x, e.y, e.z, e.w}; };
+                asm volatile("; B fragments live until here %1 %2 %3 %4"
+                             : "+v"(lx) : "v"(v4(ef[4])), "v"(v4(ef[5])), "v"(v4(ef[6])), "v"(v4(ef[7])));
+              }
+              lgv.x = lx;
+            }
             if (from_lds) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #define DSPARK_MF_GROUP(n)                                                               \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
@@ -1667,7 +1709,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
         s_rk[nt & 1][wv][lane] = key;
         s_rs[nt & 1][wv][lane] = st;
       }
-      L = Ln;
+      bp = bpn;
     }
     __syncthreads();
     publish(k, NT - 1);
@@ -1747,7 +1789,7 @@ struct Workspace {
   uint64_t* xwin;          // resident MFMA path: [2][kMfRowsMax] row winners (follows xkey)
   Stat* stat_part;         // resident paths: [K][B][kResMaxCUs]
   int* fail;               // resident path: bounded-wait failure flag
-  float* sink;             // resident MFMA path: [64][4] discarded stores
+  float* sink;             // resident MFMA path: [kMfSinkFloats] discarded stores
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1769,10 +1811,12 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
   if (resident_ws) {
     // exchange words of both resident kernels: [2][CUs][rows] then [2][rows] winners
     o_x = off;  off += (size_t)2 * kResMaxCUs * kMfRowsMax * sizeof(uint64_t);
-    o_w = off;  off = align_up(off + (size_t)2 * kMfRowsMax * sizeof(uint64_t), 256);
+    // (the MFMA kernel's winners follow the G workgroups' words it uses, and
+    // its zeroed words follow the winners, inside this region and the next)
+    o_w = off;  off = align_up(off + (size_t)(2 * kMfRowsMax + kMfZeroWords) * sizeof(uint64_t), 256);
     o_sp = off; off = align_up(off + (size_t)K * B * kResMaxCUs * sizeof(Stat), 256);
     o_f = off;  off = align_up(off + sizeof(int), 256);
-    o_s = off;  off = align_up(off + 64 * 4 * sizeof(float), 256);
+    o_s = off;  off = align_up(off + kMfSinkFloats * sizeof(float), 256);
   }
   if (ws) {
     for (int i = 0; i < 2; ++i) {
@@ -1812,13 +1856,13 @@ bool prepare_resident_kernel() {
   return occ >= 1;
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kRagged>
 bool prepare_mfma_kernel() {
-  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16>);
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) != hipSuccess)
     return false;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>,
                                                    kMfThreads, kMfLdsBytes) != hipSuccess)
     return false;
   return occ >= 1;
@@ -1837,7 +1881,8 @@ int init_device() {
   ok = ok && prepare_resident_kernel<2, false>() && prepare_resident_kernel<2, true>();
   ok = ok && prepare_resident_kernel<4, false>() && prepare_resident_kernel<4, true>();
   bool mok = cus > 0 && cus <= kResMaxCUs;
-  mok = mok && prepare_mfma_kernel<false>() && prepare_mfma_kernel<true>();
+  mok = mok && prepare_mfma_kernel<false, false>() && prepare_mfma_kernel<true, false>();
+  mok = mok && prepare_mfma_kernel<false, true>() && prepare_mfma_kernel<true, true>();
   info.cus = cus;
   info.resident_ok = ok;
   info.mfma_ok = mok;
@@ -1953,7 +1998,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   const bool bf16 = base_dtype == DSPARK_BF16;
 
   if (resident) {
-    const int n_clear = plan.resident_mfma ? 2 * G * kMfRowsMax + 2 * kMfRowsMax : 2 * G * kResRowsMax;
+    const int n_clear = plan.resident_mfma ? 2 * G * kMfRowsMax + 2 * kMfRowsMax + kMfZeroWords : 2 * G * kResRowsMax;
     hipLaunchKernelGGL(res_clear, dim3((n_clear + 4095) / 4096), dim3(kThreads), 0, stream, ws.xkey, n_clear,
                        ws.fail);
     if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
@@ -1963,12 +2008,20 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
       ma.base = base; ma.E = E; ma.W = W; ma.prev_token = prev_token; ma.seed = seed; ma.offset = offset;
       ma.temperature = temperature; ma.n_real = n_real; ma.logits = logits; ma.tokens = tokens;
       ma.xrow = ws.xkey; ma.xwin = ws.xkey + (size_t)2 * G * kMfRowsMax; ma.stat_part = ws.stat_part;
-      ma.fail = ws.fail; ma.sink = ws.sink;
+      ma.fail = ws.fail; ma.sink = ws.sink; ma.zeros = ma.xwin + 2 * kMfRowsMax;
       ma.B = B; ma.K = K; ma.V = V; ma.r = r; ma.slice = slice;
       ma.spin_limit = 1u << 20;
       const dim3 mblock(kMfThreads);
-      if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true>), grid, mblock, kMfLdsBytes, stream, ma);
-      else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false>), grid, mblock, kMfLdsBytes, stream, ma);
+      // columns come in whole tiles of 16 unless the vocabulary is ragged
+      const bool ragged = V % 16 != 0;
+      if (bf16 && !ragged)
+        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, false>), grid, mblock, kMfLdsBytes, stream, ma);
+      else if (!ragged)
+        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, false>), grid, mblock, kMfLdsBytes, stream, ma);
+      else if (bf16)
+        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, true>), grid, mblock, kMfLdsBytes, stream, ma);
+      else
+        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, true>), grid, mblock, kMfLdsBytes, stream, ma);
     } else {
       ResArgs ra;
       ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
@@ -2051,8 +2104,10 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax),
       reinterpret_cast<const void*>(&res_clear),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, true>),
   };
   for (const void* kfn : kernels)
     if (hipFuncGetAttributes(&attr, kfn) != hipSuccess) return DSPARK_ERR_HIP;
