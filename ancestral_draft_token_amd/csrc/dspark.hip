@@ -1223,11 +1223,11 @@ constexpr int kMfKSteps = kResRank / 32;                   // 8
 constexpr int kMfAhead = 4;                                // base logits loaded this many tiles ahead
 constexpr int kMfNextAt = kMfTilesMax - 1 - kMfAhead;      // first tile loading the next N-tile's bases
 constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
-constexpr int kMfERow = 520;                               // bytes per staged E row (512 + pad)
+constexpr int kMfERow = 528;                               // bytes per staged E row: 512 + 16 (16-byte aligned rows; 16 lanes of one 128-bit read cover all banks)
 constexpr int kMfSinkFloats = 1024;                        // sink: stores of lanes without a row or column
 constexpr int kMfZeroWords = 512;                          // 4 KB of zeros: base logits of rows that have none
 constexpr size_t kMfLdsW = (size_t)kMfLdsTiles * kMfKSteps * 64 * 16;   // 139,264 bytes
-constexpr size_t kMfLdsE = (size_t)2 * 16 * kMfERow;                    // 16,640 bytes
+constexpr size_t kMfLdsE = (size_t)2 * 16 * kMfERow;                    // 16,896 bytes
 constexpr size_t kMfLdsBytes = kMfLdsW + kMfLdsE;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -1847,25 +1847,27 @@ DeviceInfo g_devices[kMaxDevices];
 template <int RB, bool kBf16>
 bool prepare_resident_kernel() {
   const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident<RB, kBf16>);
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResLdsBytes) != hipSuccess)
-    return false;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident<RB, kBf16>,
-                                                   kResThreads, kResLdsBytes) != hipSuccess)
-    return false;
-  return occ >= 1;
+  const bool ok =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResLdsBytes) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident<RB, kBf16>,
+                                                   kResThreads, kResLdsBytes) == hipSuccess;
+  // a probe that fails only rules the plan out: clear the error it leaves
+  // behind, or the caller's next HIP call would report it
+  if (!ok) (void)hipGetLastError();
+  return ok && occ >= 1;
 }
 
 template <bool kBf16, bool kRagged>
 bool prepare_mfma_kernel() {
   const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>);
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) != hipSuccess)
-    return false;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>,
-                                                   kMfThreads, kMfLdsBytes) != hipSuccess)
-    return false;
-  return occ >= 1;
+  const bool ok =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>,
+                                                   kMfThreads, kMfLdsBytes) == hipSuccess;
+  if (!ok) (void)hipGetLastError();
+  return ok && occ >= 1;
 }
 
 int init_device() {
