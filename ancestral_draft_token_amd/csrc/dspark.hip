@@ -1332,6 +1332,28 @@ __device__ __forceinline__ void run_update4(Stat& st, const float s[4]) {
   st = Stat{mn, l};
 }
 
+// Merge of (key, statistics) partials over the four 16-lane rows of a wave
+// (lane l with l ^ 16, then with l ^ 32), with the gfx950 lane-swap
+// instructions instead of LDS-routed shuffles. Swapping a register with itself
+// hands every lane the pair {lower row's value, upper row's value} in that
+// order, so all lanes of a pair compute the same merge (max and stat_merge are
+// symmetric in any case).
+__device__ __forceinline__ void row_merge4(uint64_t& key, Stat& st) {
+#define DSPARK_SWAP_MERGE(swap)                                                                   \
+  {                                                                                              \
+    const auto lo = swap((uint32_t)key, (uint32_t)key, false, false);                            \
+    const auto hi = swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);            \
+    const auto mm = swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);            \
+    const auto ll = swap(__float_as_uint(st.l), __float_as_uint(st.l), false, false);            \
+    key = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);               \
+    st = stat_merge(Stat{__uint_as_float(mm[0]), __uint_as_float(ll[0])},                         \
+                    Stat{__uint_as_float(mm[1]), __uint_as_float(ll[1])});                        \
+  }
+  DSPARK_SWAP_MERGE(__builtin_amdgcn_permlane16_swap)
+  DSPARK_SWAP_MERGE(__builtin_amdgcn_permlane32_swap)
+#undef DSPARK_SWAP_MERGE
+}
+
 // log2(-log2 u) for u = ((x >> 9) + 1/2) 2^-23 of a Philox word x, with the
 // hardware base-2 logarithm; the Gumbel variate is g = -ln(-ln u) =
 // -ln2 * log2(-log2 u) - ln(ln 2). u is formed from bits: the float with
@@ -1579,20 +1601,13 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 
   // Combine the waves' partials of N-tile nt and publish each row's tagged
   // word. Wave 1 does it (wave 0 may own one more tile than the others):
-  // lane = row (lane % 16) x wave (lane / 16), merged over the 4 lanes of a
-  // row in a fixed xor order.
+  // lane = row (lane % 16) x wave (lane / 16), merged over the 4 rows of lanes.
   auto publish = [&](int k, int nt) {
     if (wv == 1) {
       const int row = lane & 15, w = lane >> 4;
       uint64_t kk = s_rk[nt & 1][w][row];
       Stat ss = s_rs[nt & 1][w][row];
-      for (int mask = 16; mask < 64; mask <<= 1) {
-        kk = umax64(kk, shfl_xor_u64(kk, mask, 64));
-        Stat o;
-        o.m = __shfl_xor(ss.m, mask, 64);
-        o.l = __shfl_xor(ss.l, mask, 64);
-        ss = stat_merge(ss, o);
-      }
+      row_merge4(kk, ss);
       const int b = 16 * nt + row;
       if (lane < 16 && b < B) {
         a.stat_part[((size_t)k * B + b) * G + g] = ss;
@@ -1698,13 +1713,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       }
       // lanes of one row (equal lane % 16) combine; lanes 0..15 hold the wave's partials
       uint64_t key = best_key(best);
-      for (int mask = 16; mask < 64; mask <<= 1) {
-        key = umax64(key, shfl_xor_u64(key, mask, 64));
-        Stat o;
-        o.m = __shfl_xor(st.m, mask, 64);
-        o.l = __shfl_xor(st.l, mask, 64);
-        st = stat_merge(st, o);
-      }
+      row_merge4(key, st);
       if (lane < 16) {
         s_rk[nt & 1][wv][lane] = key;
         s_rs[nt & 1][wv][lane] = st;
