@@ -50,21 +50,50 @@ constexpr int kPickPerThread = 8;    // in-kernel pick: at most 8 x 256 = 2048 p
 // as 1, 2, 3", SC'11, section 3): ten rounds of the 4x32 bijection; the key is
 // bumped by the Weyl increments between rounds.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int round = 0; round < 10; ++round) {
-    if (round) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
-    // full 64-bit products: one v_mad_u64_u32 each instead of a mul_lo/mul_hi pair
-    const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c.x;
-    const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
-    // three-input exclusive or in one instruction (v_bitop3_b32, truth table 0x96)
-    c = make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c.y, k0, 0x96), (uint32_t)pb,
-                   __builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c.w, k1, 0x96), (uint32_t)pa);
-  }
+// One Philox4x32 round: the two products as full 64-bit results (one
+// v_mad_u64_u32 each instead of a mul_lo/mul_hi pair) and the three-input
+// exclusive or as one v_bitop3_b32 (truth table 0x96).
+__device__ __forceinline__ uint4 philox_round(uint4 c, uint32_t k0, uint32_t k1) {
+  const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c.x;
+  const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c.z;
+  return make_uint4(__builtin_amdgcn_bitop3_b32((uint32_t)(pb >> 32), c.y, k0, 0x96), (uint32_t)pb,
+                    __builtin_amdgcn_bitop3_b32((uint32_t)(pa >> 32), c.w, k1, 0x96), (uint32_t)pa);
+}
+
+// A hook with nothing to do (see philox4x32_10_hooked).
+struct NoHook {
+  template <int J>
+  __device__ __forceinline__ void step() {}
+};
+
+// Philox4x32-10 with hook.step<J>() after rounds 2J + 1 (J = 0..4): a place to
+// issue unrelated work between the rounds (the large-batch kernel issues its
+// next matrix chain there). The step index is a template argument so that
+// whatever it indexes stays in registers.
+template <class Hook>
+__device__ __forceinline__ uint4 philox4x32_10_hooked(uint4 c, uint32_t k0, uint32_t k1, Hook& hook) {
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  c = philox_round(c, k0, k1);
+  c = philox_round(c, k0 + W0, k1 + W1);
+  hook.template step<0>();
+  c = philox_round(c, k0 + 2 * W0, k1 + 2 * W1);
+  c = philox_round(c, k0 + 3 * W0, k1 + 3 * W1);
+  hook.template step<1>();
+  c = philox_round(c, k0 + 4 * W0, k1 + 4 * W1);
+  c = philox_round(c, k0 + 5 * W0, k1 + 5 * W1);
+  hook.template step<2>();
+  c = philox_round(c, k0 + 6 * W0, k1 + 6 * W1);
+  c = philox_round(c, k0 + 7 * W0, k1 + 7 * W1);
+  hook.template step<3>();
+  c = philox_round(c, k0 + 8 * W0, k1 + 8 * W1);
+  c = philox_round(c, k0 + 9 * W0, k1 + 9 * W1);
+  hook.template step<4>();
   return c;
+}
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+  NoHook none;
+  return philox4x32_10_hooked(c, k0, k1, none);
 }
 
 // Standard Gumbel variate from the top 23 bits of a Philox word:
@@ -1250,6 +1279,31 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, uint4 b, f32x4_t c) {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// The bias chain of one LDS M-tile, issued from the epilogue's hooks: step J
+// runs the matrix instruction of K-step J and reads the A fragment of K-step
+// J + 1, so each read has a stretch of VALU work to arrive in while one
+// fragment register set suffices. Fences keep the scheduler from gathering
+// the reads and multiplies back into one read-wait-multiply run ahead of the
+// epilogue (the register pressure here leaves it no room to overlap them).
+struct LdsChain {
+  const unsigned char* fb;   // this lane's fragment of K-step 0; K-steps are 1 KB apart
+  uint4 e[kMfKSteps];        // B fragments
+  u32x4_t fr;                // A fragment in flight
+  f32x4_t an;
+  __device__ __forceinline__ u32x4_t frag(int ks) const { return *reinterpret_cast<const u32x4_t*>(fb + ks * 1024); }
+  __device__ __forceinline__ void start() {
+    fr = frag(0);
+    an = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  template <int J>
+  __device__ __forceinline__ void step() {
+    __builtin_amdgcn_sched_barrier(0);
+    an = mfma_bf16(fr, e[J], an);
+    if constexpr (J + 1 < kMfKSteps) fr = frag(J + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
 struct MfArgs {
   const void* base;
   const uint16_t* E;
@@ -1387,12 +1441,13 @@ struct MfLane {
 // argmax is that of s + g. kRagged (a vocabulary that is not a multiple of 16):
 // fragments without real columns (ok false) take part as scores that never win
 // (NaN) and softmax terms that are 0. The statistics of greedy rows are not used.
-template <bool kBf16Base, bool kRagged>
+// hook.step<J>(), J = 0..7, runs at eight points spread over the epilogue's work.
+template <bool kBf16Base, bool kRagged, class Hook>
 __device__ __forceinline__ float4 mf_epilogue(const MfLane& L, int k, uint32_t v0, const Base4<kBf16Base>& bv,
-                                              f32x4_t acc, bool ok, Best& best, Stat& st) {
+                                              f32x4_t acc, bool ok, Best& best, Stat& st, Hook& hook) {
   float base[4];
   widen_base4<kBf16Base>(bv, base);
-  const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, L.ctr2, L.ctr3), L.key0, L.key1);
+  const uint4 x = philox4x32_10_hooked(make_uint4(v0 >> 2, (uint32_t)k, L.ctr2, L.ctr3), L.key0, L.key1, hook);
   const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
   float lg[4], s[4], z[4];
 #pragma unroll
@@ -1404,8 +1459,11 @@ __device__ __forceinline__ float4 mf_epilogue(const MfLane& L, int k, uint32_t v
       z[i] = fsel(ok, z[i], __builtin_nanf(""));
       s[i] = fsel(ok, s[i], -INFINITY);
     }
+    if (i == 1) hook.template step<5>();
   }
+  hook.template step<6>();
   best_update4(best, z, v0);
+  hook.template step<7>();
   run_update4(st, s);
   return make_float4(lg[0], lg[1], lg[2], lg[3]);
 }
@@ -1577,23 +1635,12 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     const bool has = i < n_mine && (!kRagged || c4 < ncols);
     return bp + (has ? c4 : 0) * kEsz;
   };
-  // the bias fragment of tile i (rank rows >= r are zero in both operands, so all 8 K-steps run);
-  // an LDS tile also returns its last A fragment in `last` (see the keep-alive below)
-  auto tile_bias = [&](int i, const uint4 (&ef)[kMfKSteps], u32x4_t& last) {
+  // the bias fragment of VGPR tile i < 8 (rank rows >= r are zero in both operands, so all
+  // 8 K-steps run); the chains of LDS tiles are issued from the epilogue's hooks
+  auto tile_bias = [&](int i, const uint4 (&ef)[kMfKSteps]) {
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (i < kMfTilesPerWave) {
 #pragma unroll
-      for (int ks = 0; ks < kMfKSteps; ++ks) acc = mfma_bf16(wf[i][ks], ef[ks], acc);
-    } else {
-      // a tile this wave does not have reads a valid one; its results are masked
-      const int ml = tile_m(i) < kMfRegTiles + kMfLdsTiles ? tile_m(i) - kMfRegTiles : 0;
-      const unsigned char* fb = lds_w + (size_t)ml * kMfKSteps * 1024 + lane * 16;
-#pragma unroll
-      for (int ks = 0; ks < kMfKSteps; ++ks) {
-        last = *reinterpret_cast<const u32x4_t*>(fb + ks * 1024);
-        acc = mfma_bf16(last, ef[ks], acc);
-      }
-    }
+    for (int ks = 0; ks < kMfKSteps; ++ks) acc = mfma_bf16(wf[i][ks], ef[ks], acc);
     return acc;
   };
 
@@ -1653,8 +1700,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 
       // the bias of tile i + 1 is issued to the matrix cores before the epilogue of tile i
       f32x4_t acc[2];
-      u32x4_t afrag;   // last A fragment of an LDS tile's chain
-      acc[0] = tile_bias(0, ef, afrag);
+      acc[0] = tile_bias(0, ef);
 #pragma unroll
       for (int i = 0; i < kMfTilesMax; ++i) {
         if (i + kMfAhead < kMfTilesMax) load_base4<kBf16Base>(bq[i + kMfAhead], base_at(bp, i + kMfAhead), 0);
@@ -1670,38 +1716,40 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
         float* out = a.sink + 4 * lane;
         float4 lgv;
         if (i < n_mine) {
-          if (i + 1 < kMfTilesMax) acc[(i + 1) & 1] = tile_bias(i + 1, ef, afrag);
           const int c4 = 16 * tile_m(i) + 4 * lq;   // column offset in the slice
           const bool ok = !kRagged || c4 < ncols;
           out = ok ? L.op + c4 : a.sink + c4;
-          lgv = mf_epilogue<kBf16Base, kRagged>(L, k, (uint32_t)(col0 + c4), bq[i], acc[i & 1], ok, best, st);
-          if (i + 1 < kMfTilesMax) {
-            // 8 x (one matrix instruction, 18 VALU): the chain of tile i + 1
-            // runs on the matrix cores while the epilogue of tile i issues
-            const bool from_lds = i + 1 >= kMfTilesPerWave;
-            if (from_lds) {
-              // Keep-alive: the last A fragment of the chain (and, after the
-              // N-tile's last chain, the B fragments of its last K-steps) stay
-              // allocated until the epilogue's result exists, so no VALU
-              // result of the epilogue is written into those registers right
-              // after the matrix instructions that read them.
-              float lx = lgv.x;
-              asm volatile("; A fragment live until here %1" : "+v"(lx) : "v"(afrag));
-              if (i + 2 == kMfTilesMax) {
-                auto v4 = [](uint4 e) { return u32x4_t{e.x, e.y, e.z, e.w}; };
-                asm volatile("; B fragments live until here %1 %2 %3 %4"
-                             : "+v"(lx) : "v"(v4(ef[4])), "v"(v4(ef[5])), "v"(v4(ef[6])), "v"(v4(ef[7])));
-              }
-              lgv.x = lx;
+          const uint32_t v0 = (uint32_t)(col0 + c4);
+          if (i + 1 < kMfTilesPerWave) {
+            // the chain of tile i + 1 (W in AGPRs) runs on the matrix cores
+            // while the epilogue of tile i issues: 8 x (one matrix
+            // instruction, 18 VALU)
+            acc[(i + 1) & 1] = tile_bias(i + 1, ef);
+            NoHook none;
+            lgv = mf_epilogue<kBf16Base, kRagged>(L, k, v0, bq[i], acc[i & 1], ok, best, st, none);
+#pragma unroll
+            for (int n = 0; n < kMfKSteps; ++n) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);
             }
-            if (from_lds) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#define DSPARK_MF_GROUP(n)                                                               \
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                     \
-  __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);                                    \
-  if (from_lds && (n) < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            DSPARK_MF_GROUP(0) DSPARK_MF_GROUP(1) DSPARK_MF_GROUP(2) DSPARK_MF_GROUP(3)
-            DSPARK_MF_GROUP(4) DSPARK_MF_GROUP(5) DSPARK_MF_GROUP(6) DSPARK_MF_GROUP(7)
-#undef DSPARK_MF_GROUP
+          } else if (i + 1 < kMfTilesMax) {
+            // the chain of LDS tile i + 1 (a tile this wave does not have reads
+            // a valid one; its results are not used), placed by hand: the
+            // epilogue issues one matrix instruction at each of its eight
+            // hooks and the next fragment read after it (the scheduler would
+            // otherwise run read, wait, multiply eight times in a row before
+            // the epilogue)
+            const int ml = tile_m(i + 1) < kMfRegTiles + kMfLdsTiles ? tile_m(i + 1) - kMfRegTiles : 0;
+            LdsChain ch;
+            ch.fb = lds_w + (size_t)ml * kMfKSteps * 1024 + lane * 16;
+#pragma unroll
+            for (int ks = 0; ks < kMfKSteps; ++ks) ch.e[ks] = ef[ks];
+            ch.start();
+            lgv = mf_epilogue<kBf16Base, kRagged>(L, k, v0, bq[i], acc[i & 1], ok, best, st, ch);
+            acc[(i + 1) & 1] = ch.an;
+          } else {
+            NoHook none;
+            lgv = mf_epilogue<kBf16Base, kRagged>(L, k, v0, bq[i], acc[i & 1], ok, best, st, none);
           }
         } else {
           float bw[4];

@@ -1,20 +1,21 @@
 """Checks on the gfx950 assembly of the large-batch (MFMA) kernel.
 
-The compiler's hazard model for matrix instructions covers a late read of the
-accumulator input, not of the A and B operands. A build in which a reloaded A
-operand was rewritten by the very next VALU instruction produced bias values
-that changed from run to run, so the kernel is written to keep that pattern
-out, and this test holds it out:
+The kernel keeps W resident in registers: 62 of its 64 A-operand fragments
+per lane live in AGPRs for the whole launch, read there by the matrix
+instructions. A build in which the register allocator spilled some of those
+fragments to scratch memory gave bias values that changed from run to run.
+There the spill store of an AGPR tuple was followed two instructions later by
+an AGPR write of the same registers, and the fragments were reloaded inside
+the N-tile loop. This test keeps that configuration out:
 
-* no VALU instruction writes a register that a matrix instruction read as its
-  A or B operand among the first 8 VALU instructions after it (each takes at
-  least 4 cycles on a 16-lane SIMD, so that is 32 cycles or more: at least the
-  whole duration of a 16x16x32 bf16 matrix instruction). A matrix instruction
-  that accumulates onto an earlier one's result ends that one's window (it
-  cannot start before the earlier one has read its operands). Loads from LDS
-  or memory are exempt: their results arrive a memory latency after issue;
+* no AGPR is spilled (no scratch store with AGPR data) anywhere in the kernel;
 * no scratch (spill) access sits inside the kernel's inner loops, where the W
-  fragments and the per-tile state live.
+  fragments and the per-tile state live (a spill there would also stall every
+  tile on the scratch round trip).
+
+A VALU write to a matrix instruction's A or B registers right after it issues
+does not change its result. This was checked on gfx950 with the matrix pipe
+idle and busy, over 5e8 results each, so this test does not restrict it.
 
 The assembly is generated here with the library's own flags (device code only,
 about 15 s); no GPU is needed.
@@ -30,20 +31,8 @@ import pytest
 
 from ancestral_draft_token_amd import _build
 
-WINDOW = 8   # VALU instructions
 KERNEL = "markov_bias_gumbel_argmax_resident_mfma"
 VARIANTS = ["ILb0ELb0EE", "ILb1ELb0EE", "ILb0ELb1EE", "ILb1ELb1EE"]   # <bf16 base, ragged vocabulary>
-_REG = re.compile(r"\b([av])\[(\d+):(\d+)\]|\b([av])(\d+)\b")
-
-
-def _regs(text: str) -> set:
-    out = set()
-    for m in _REG.finditer(text):
-        if m.group(1):
-            out.update((m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1))
-        else:
-            out.add((m.group(4), int(m.group(5))))
-    return out
 
 
 @pytest.fixture(scope="module")
@@ -64,63 +53,49 @@ def _function(asm: str, variant: str) -> list:
     return asm[start:end].splitlines()
 
 
-def _operand_overwrites(lines: list) -> list:
-    """(VALU distance, mfma line, writer line, opcode) for VALU writes of A/B
-    operands; the distance counts the VALU instructions after the MFMA, the
-    writer included (scalar instructions and s_nop count as none)."""
-    pending, hits = [], []   # (A/B registers, destination, line, distance)
-    for ln, line in enumerate(lines):
+def _scratch_by_depth(lines: list) -> list:
+    """(loop depth, instruction) of every scratch access, the depth taken from
+    the compiler's basic-block comments."""
+    depth, out = 0, []
+    for line in lines:
+        if line.startswith(".LBB") or line.startswith("; %bb"):
+            m = re.search(r"Depth=(\d+)", line)
+            depth = int(m.group(1)) if m else 0
         s = line.strip()
-        if not s or s.startswith(";") or s.startswith(".") or s.endswith(":"):
-            continue
-        op = s.split()[0]
-        parts = [p.strip() for p in s[len(op):].split(";")[0].split(",")]
-        if op.startswith("v_mfma"):
-            src_c = _regs(parts[3]) if len(parts) > 3 else set()
-            pending = [e for e in pending if not (e[1] & src_c)]
-            pending.append((_regs(parts[1]) | _regs(parts[2]), _regs(parts[0]), ln, 0))
-        elif op.startswith("v_"):
-            pending = [(ab, dst, i, d + 1) for ab, dst, i, d in pending]
-            written = _regs(parts[0]) if parts[0] else set()
-            hits += [(d, i, ln, op) for ab, dst, i, d in pending if ab & written]
-            pending = [e for e in pending if e[3] < WINDOW]
-    return hits
+        if s.startswith("scratch_"):
+            out.append((depth, s))
+    return out
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_mfma_operands_not_rewritten_soon_after(asm, variant):
+def test_matrix_kernel_is_a_full_mfma_kernel(asm, variant):
     lines = _function(asm, variant)
-    assert any("v_mfma" in l for l in lines)
-    hits = _operand_overwrites(lines)
-    assert not hits, [(d, lines[i].strip(), lines[j].strip()) for d, i, j, _ in hits[:5]]
+    assert sum(1 for l in lines if "v_mfma_f32_16x16x32_bf16" in l) >= 8 * 13
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_no_agpr_spill(asm, variant):
+    bad = [s for _, s in _scratch_by_depth(_function(asm, variant)) if s.startswith("scratch_store") and " a[" in s]
+    assert not bad, bad[:5]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_no_spill_in_inner_loops(asm, variant):
-    depth, bad = 0, []
-    for line in _function(asm, variant):
-        m = re.search(r"Depth=(\d+)", line)
-        if line.startswith(".LBB") or line.startswith("; %bb"):
-            depth = int(m.group(1)) if m else 0
-        if "scratch_" in line and depth >= 2:
-            bad.append(line.strip())
+    bad = [s for d, s in _scratch_by_depth(_function(asm, variant)) if d >= 2]
     assert not bad, bad[:5]
 
 
-def test_scanner_flags_a_planted_overwrite():
-    """The scanner itself: A and B operands rewritten within the window are found
-    (nops and scalar instructions do not widen it); one rewritten after 8 VALU
-    instructions, or by an LDS load, is not."""
-    mfma = "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], 0"
-    add = "\tv_add_f32_e32 v1, v2, v3"
-    write_a = "\tv_bitop3_b32 v5, v1, v2, v3 bitop3:0x96"
-    write_b = "\tv_mad_u64_u32 v[10:11], s[0:1], v1, s38, 0"
-    assert [h[3] for h in _operand_overwrites([mfma, add, write_a])] == ["v_bitop3_b32"]
-    assert [h[0] for h in _operand_overwrites([mfma, "\ts_nop 7", "\ts_mov_b32 s0, 0", write_b])] == [1]
-    assert _operand_overwrites([mfma] + [add] * 7 + [write_a]) != []
-    assert _operand_overwrites([mfma] + [add] * 8 + [write_a]) == []
-    assert _operand_overwrites([mfma, "\tds_read_b128 v[4:7], v12 offset:1024"]) == []
-    chained = "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[12:15], v[16:19], a[0:3]"
-    assert _operand_overwrites([mfma, chained, write_a]) == []
-    assert [h[3] for h in _operand_overwrites([mfma, chained, "\tv_mov_b32_e32 v13, 0"])] == ["v_mov_b32_e32"]
-
+def test_depth_parser():
+    lines = [
+        ".LBB4_312:                              ; =>This Loop Header: Depth=1",
+        "\tscratch_load_dwordx2 v[16:17], off, off offset:8",
+        "; %bb.348:                              ;   in Loop: Header=BB4_315 Depth=2",
+        "\tscratch_store_dwordx4 off, a[4:7], off",
+        ".LBB4_400:",
+        "\tscratch_store_dword off, v1, off",
+    ]
+    assert _scratch_by_depth(lines) == [
+        (1, "scratch_load_dwordx2 v[16:17], off, off offset:8"),
+        (2, "scratch_store_dwordx4 off, a[4:7], off"),
+        (0, "scratch_store_dword off, v1, off"),
+    ]
