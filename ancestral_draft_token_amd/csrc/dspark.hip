@@ -1269,6 +1269,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // AGPRs on its own and copies each one back to VGPRs before every use (four
 // VALU moves per instruction).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void* lds_gptr_t;   // global source of an LDS-direct load
+typedef __attribute__((address_space(3))) void* lds_lptr_t;   // its LDS destination
 __device__ __forceinline__ u32x4_t in_agpr(u32x4_t v) {
   u32x4_t r;
   asm volatile("; W fragment kept in AGPRs %0" : "=a"(r) : "0"(v));
@@ -1524,69 +1526,102 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     s_d[b] = clamp_token(a.prev_token[b], V);
   }
 
-  // ---- (1) LDS M-tiles 32..48: each 16-byte load (8 columns of one rank row)
-  // is scattered into the fragment layout (element e of lane l at byte l*16 + 2e)
+  // ---- (1) VGPR M-tiles 8w..8w+7, in two rounds of four K-steps. In each,
+  // rank rows 128 h .. 128 h + 127 of the slice's first 512 columns are copied
+  // into the (not yet used) LDS-tile region by LDS-direct loads (one 1 KB row
+  // per wave instruction, lane i's 16 bytes at 16 i; no registers hold the
+  // data), rows past the rank and columns past the slice from the zeroed
+  // region; then every wave gathers its A fragments from there (lane l:
+  // column l % 16 of the tile, rank rows 8 (l / 16) .. + 7).
+  u32x4_t wf[kMfTilesPerWave][kMfKSteps];   // A fragments, kept in AGPRs
   {
-    const int items = kMfLdsTiles * kResRank * 2;
-    for (int q = t; q < items; q += kMfThreads) {
-      const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
-      const int j = rem / 2, h = rem % 2;
-      const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
-      const bool ok = j < r && c8 < ncols;
-      uint4 v = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)j * V + col0 + c8 : 0));
-      if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      unsigned char* frag = lds_w + ((size_t)ti * kMfKSteps + j / 32) * 1024;
-      const int lbase = 8 * h + 16 * ((j % 32) / 8);
+    constexpr int kStageRow = 2 * 16 * kMfRegTiles + 16;       // bytes per staged row (1 KB + pad)
+    constexpr int kRoundRows = kResRank / 2;                   // 128
+    constexpr int kRowsPerWave = kRoundRows / kMfWaves;        // 32
+    static_assert((size_t)kRoundRows * kStageRow <= kMfLdsW, "staging fits the LDS-tile region");
+    const uint16_t* st16 = reinterpret_cast<const uint16_t*>(lds_w);
+    const int c8 = 8 * lane;                                   // this lane's 8 columns of a staged row
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint16_t val = (uint16_t)(w4[c / 2] >> (16 * (c % 2)));
-        *reinterpret_cast<uint16_t*>(frag + (lbase + c) * 16 + 2 * (j % 8)) = val;
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll 8
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int rl = kRowsPerWave * wv + i, row = kRoundRows * h + rl;
+        const bool ok = row < r && c8 < ncols;
+        const uint16_t* src = ok ? a.W + (size_t)row * V + col0 + c8
+                                 : static_cast<const uint16_t*>(a.zeros) + c8;
+        __builtin_amdgcn_global_load_lds((lds_gptr_t)src, (lds_lptr_t)(lds_w + (size_t)rl * kStageRow), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) (expcnt, lgkmcnt not waited): every row of this wave has landed
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kMfKSteps / 2; ++kk) {
+        const int ks = (kMfKSteps / 2) * h + kk;
+#pragma unroll
+        for (int mt = 0; mt < kMfTilesPerWave; ++mt) {
+          const int col = 16 * (kMfTilesPerWave * wv + mt) + lr;
+          uint32_t d[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rr = 32 * kk + 8 * lq + 2 * e;   // staged row of rank row 32 ks + 8 lq + 2 e
+            const uint32_t lo = st16[(rr * kStageRow) / 2 + col];
+            const uint32_t hi = st16[((rr + 1) * kStageRow) / 2 + col];
+            d[e] = lo | (hi << 16);
+          }
+          // 62 fragments and the two 4-register accumulators fill the 256
+          // AGPRs exactly; the last two fragments stay ordinary VGPR values
+          // (left to the allocator, it moves two of its own choosing and has
+          // at times spilled one to scratch instead)
+          const u32x4_t f = u32x4_t{d[0], d[1], d[2], d[3]};
+          wf[mt][ks] = (mt == kMfTilesPerWave - 1 && ks >= kMfKSteps - 2) ? f : in_agpr(f);
+        }
+      }
+      __syncthreads();   // the staging area is overwritten next
+    }
+  }
+
+  // ---- (2) LDS M-tiles 32..48: each 16-byte load (8 columns of one rank row)
+  // is scattered into the fragment layout (element e of lane l at byte l*16 + 2e).
+  // Consecutive threads take consecutive rank rows (so the 2-byte stores of a
+  // wave spread over the LDS banks); each thread issues its loads in batches
+  // of 17 before storing any (one memory latency per batch, not per item).
+  // Beyond the rank or the slice a valid address is read and the value zeroed
+  // when stored.
+  {
+    constexpr int kItems = kMfLdsTiles * kResRank * 2;         // 8704
+    constexpr int kPerThread = kItems / kMfThreads;            // 34
+    constexpr int kBatch = 17;
+    static_assert(kItems % kMfThreads == 0 && kPerThread % kBatch == 0, "item split");
+#pragma unroll
+    for (int b0 = 0; b0 < kPerThread; b0 += kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int q = t + (b0 + u) * kMfThreads;
+        const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
+        const int j = rem / 2, h = rem % 2;
+        const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
+        const bool ok = j < r && c8 < ncols;
+        v[u] = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)j * V + col0 + c8 : 0));
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int q = t + (b0 + u) * kMfThreads;
+        const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
+        const int j = rem / 2, h = rem % 2;
+        const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
+        const uint32_t m = (j < r && c8 < ncols) ? ~0u : 0u;
+        const uint32_t w4[4] = {v[u].x & m, v[u].y & m, v[u].z & m, v[u].w & m};
+        unsigned char* frag = lds_w + ((size_t)ti * kMfKSteps + j / 32) * 1024;
+        const int lbase = 8 * h + 16 * ((j % 32) / 8);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint16_t val = (uint16_t)(w4[c / 2] >> (16 * (c % 2)));
+          *reinterpret_cast<uint16_t*>(frag + (lbase + c) * 16 + 2 * (j % 8)) = val;
+        }
       }
     }
   }
 
-  // ---- (2) VGPR M-tiles 8w..8w+7, staged through this wave's 4 KB of the (not yet
-  // used) E region, 16 rank rows at a time: lanes of quads 0,1 take rows 0..15 of a
-  // K-step, quads 2,3 rows 16..31
-  u32x4_t wf[kMfTilesPerWave][kMfKSteps];   // A fragments, kept in AGPRs
-  {
-    unsigned char* stage = lds_e + (size_t)wv * 4096;   // [16 rows][128 columns] bf16
-    const int cbase = 128 * wv;                         // first column of the wave's tiles
-    const uint16_t* st16 = reinterpret_cast<const uint16_t*>(stage);
-#pragma unroll
-    for (int ks = 0; ks < kMfKSteps; ++ks) {
-      uint32_t d[kMfTilesPerWave][4];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint4 v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = 32 * ks + 16 * half + lane / 16 + 4 * q, c8 = cbase + 8 * (lane % 16);
-          const bool ok = row < r && c8 < ncols;
-          v[q] = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)row * V + col0 + c8 : 0));
-          if (!ok) v[q] = make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint4*>(stage + (lane / 16 + 4 * q) * 256 + 16 * (lane % 16)) = v[q];
-        if ((lq >> 1) == half) {
-#pragma unroll
-          for (int mt = 0; mt < kMfTilesPerWave; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int rr = 8 * (lq & 1) + 2 * i;   // row within the staged half
-              const uint32_t lo = st16[rr * 128 + 16 * mt + lr];
-              const uint32_t hi = st16[(rr + 1) * 128 + 16 * mt + lr];
-              d[mt][i] = lo | (hi << 16);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int mt = 0; mt < kMfTilesPerWave; ++mt) wf[mt][ks] = in_agpr(u32x4_t{d[mt][0], d[mt][1], d[mt][2], d[mt][3]});
-    }
-  }
   __syncthreads();
 
   // ---- (3) the E rows of N-tiles 0 and 1 of position 0. Every N-tile nt
