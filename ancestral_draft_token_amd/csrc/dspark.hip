@@ -1629,9 +1629,13 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // prefetches nt + 2; rows past the batch are zeros, so the schedule has no
   // branches. At a position start epre is stored at once as well, so no load
   // is in flight in it when the first N-tile stores it again.
-  mf_store_erow(lds_e, t, mf_load_erow(a, s_d, 0, t));
-  ERow2 epre = mf_load_erow(a, s_d, 1, t);
-  mf_store_erow(lds_e + 16 * kMfERow, t, epre);
+  ERow2 epre;
+  {
+    const ERow2 e0 = mf_load_erow(a, s_d, 0, t);   // both loads in flight before either store
+    epre = mf_load_erow(a, s_d, 1, t);
+    mf_store_erow(lds_e, t, e0);
+    mf_store_erow(lds_e + 16 * kMfERow, t, epre);
+  }
 
   // the wave's tiles: i < 8 are VGPR tiles 8 wv + i; i >= 8 are LDS tiles 32 + wv + 4 (i - 8)
   auto tile_m = [&](int i) {
@@ -1686,7 +1690,13 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // lane = row (lane % 16) x wave (lane / 16), merged over the 4 rows of lanes.
   auto publish = [&](int k, int nt) {
     if (wv == 1) {
-      const int row = lane & 15, w = lane >> 4;
+      // the lane's row is taken through an opaque instruction, so the address
+      // arithmetic below is done here rather than hoisted out of the loops
+      // (held across them it was spilled, and the reloads waited for every
+      // logit store still in flight)
+      int row;
+      asm volatile("v_and_b32 %0, 15, %1" : "=v"(row) : "v"(lane));
+      const int w = lane >> 4;
       uint64_t kk = s_rk[nt & 1][w][row];
       Stat ss = s_rs[nt & 1][w][row];
       row_merge4(kk, ss);
@@ -1861,9 +1871,11 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     if (g == 0)
       for (int b = t; b < B; b += kMfThreads) a.tokens[(size_t)b * K + k] = s_d[b];
     if (k + 1 < K) {
-      // E rows of the next position's N-tiles 0 and 1
-      mf_store_erow(lds_e, t, mf_load_erow(a, s_d, 0, t));
+      // E rows of the next position's N-tiles 0 and 1 (both loads in flight
+      // before either store)
+      const ERow2 e0 = mf_load_erow(a, s_d, 0, t);
       epre = mf_load_erow(a, s_d, 1, t);
+      mf_store_erow(lds_e, t, e0);
       mf_store_erow(lds_e + 16 * kMfERow, t, epre);
     }
   }
