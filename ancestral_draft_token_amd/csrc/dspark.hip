@@ -1410,6 +1410,34 @@ __device__ __forceinline__ void row_merge4(uint64_t& key, Stat& st) {
 #undef DSPARK_SWAP_MERGE
 }
 
+// Maximum of a 64-bit value over the 64 lanes of a wave, every lane getting
+// it, without LDS: DPP within quads (xor 1, xor 2), then the half-row and row
+// mirrors (which pair quad 0 with quad 1 and half 0 with half 1), then the
+// lane swaps across 16-lane rows.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#define DSPARK_DPP_MAX(ctrl)                                                                           \
+  {                                                                                                    \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, ctrl, 0xF, 0xF, false); \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), ctrl, 0xF, 0xF, false); \
+    x = umax64(x, ((uint64_t)hi << 32) | lo);                                                          \
+  }
+  DSPARK_DPP_MAX(0xB1)    // quad_perm(1,0,3,2): lane ^ 1
+  DSPARK_DPP_MAX(0x4E)    // quad_perm(2,3,0,1): lane ^ 2
+  DSPARK_DPP_MAX(0x141)   // row_half_mirror
+  DSPARK_DPP_MAX(0x140)   // row_mirror
+#undef DSPARK_DPP_MAX
+#define DSPARK_SWAP_MAX(swap)                                                                  \
+  {                                                                                            \
+    const auto lo = swap((uint32_t)x, (uint32_t)x, false, false);                              \
+    const auto hi = swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);              \
+    x = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);               \
+  }
+  DSPARK_SWAP_MAX(__builtin_amdgcn_permlane16_swap)
+  DSPARK_SWAP_MAX(__builtin_amdgcn_permlane32_swap)
+#undef DSPARK_SWAP_MAX
+  return x;
+}
+
 // log2(-log2 u) for u = ((x >> 9) + 1/2) 2^-23 of a Philox word x, with the
 // hardware base-2 logarithm; the Gumbel variate is g = -ln(-ln u) =
 // -ln2 * log2(-log2 u) - ln(ln 2). u is formed from bits: the float with
@@ -1816,32 +1844,39 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     __syncthreads();
     publish(k, NT - 1);
 
-    // ---- exchange level 2: the owner of row b (workgroup b, b + G, ...) reduces its G words
+    // ---- exchange level 2: the owner of row b (workgroup b, b + G, ...) reduces its G
+    // words in wave 0 alone (each lane polls G / 64 of them, the first loads of a
+    // group of four in flight together; no LDS, no barrier) and publishes the winner
     const uint64_t tag = (uint64_t)(k + 1);
     uint64_t* xr = a.xrow + (size_t)(k & 1) * G * kMfRowsMax;
     uint64_t* xw = a.xwin + (size_t)(k & 1) * kMfRowsMax;
     bool failed = false;
-    for (int b = g; b < B; b += G) {
-      uint64_t x = 0;
-      for (int i = t; i < G; i += kMfThreads) {
-        const uint64_t* pw = xr + (size_t)i * kMfRowsMax + b;
-        uint64_t w = ld_agent_u64(pw);
-        unsigned spins = 0;
-        while ((w >> kResTagShift) != tag) {
-          if (++spins > a.spin_limit) { failed = true; break; }
-          __builtin_amdgcn_s_sleep(1);
-          w = ld_agent_u64(pw);
+    if (wv == 0) {
+      for (int b = g; b < B; b += G) {
+        uint64_t x = 0;
+        for (int i0 = lane; i0 < G; i0 += 4 * 64) {
+          // the words still missing are reloaded together: one round trip per pass
+          uint64_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            w[j] = i0 + 64 * j < G ? ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kMfRowsMax + b) : (tag << kResTagShift);
+          unsigned spins = 0;
+          for (;;) {
+            bool all = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) all = all && (w[j] >> kResTagShift) == tag;
+            if (all) break;
+            if (++spins > a.spin_limit) { failed = true; break; }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if ((w[j] >> kResTagShift) != tag) w[j] = ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kMfRowsMax + b);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x = umax64(x, w[j]);
         }
-        x = umax64(x, w);
-      }
-      for (int mask = 1; mask < 64; mask <<= 1) x = umax64(x, shfl_xor_u64(x, mask, 64));
-      __syncthreads();
-      if (lane == 0) s_rk[0][wv][0] = x;
-      __syncthreads();
-      if (t == 0) {
-        uint64_t y = s_rk[0][0][0];
-        for (int w = 1; w < kMfWaves; ++w) y = umax64(y, s_rk[0][w][0]);
-        st_agent_u64(xw + b, (tag << kResTagShift) | (y & ((1ull << kResTagShift) - 1)));
+        x = wave_max_u64(x);
+        if (lane == 0) st_agent_u64(xw + b, (tag << kResTagShift) | (x & ((1ull << kResTagShift) - 1)));
       }
     }
     // ---- level 3: every workgroup reads the B winners
