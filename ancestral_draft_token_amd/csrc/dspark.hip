@@ -1376,16 +1376,30 @@ __device__ __forceinline__ void best_update4(Best& b, const float z[4], uint32_t
 
 __device__ __forceinline__ uint64_t best_key(const Best& b) { return b.v == kNoCol ? 0ull : score_key(b.z, b.v); }
 
-// Online softmax statistics of one lane: after each group of 4 scores,
-// l = sum over the lane's scores of exp(s - m) with m their running maximum.
+// Online softmax statistics of one lane, accumulated in base 2: after each
+// group of 4 scores, l = sum over the lane's scores of 2^(s L - M) with m
+// their running maximum, L = log2(e) rounded to float and M = fl(m L); each
+// term is one fma and one v_exp. stat_to_natural turns (m, l) into the usual
+// form sum exp(s - m) = l 2^(M - m L), exactly up to a few ulp.
+constexpr float kLog2e = 1.44269504f;
 __device__ __forceinline__ void run_update4(Stat& st, const float s[4]) {
   const float m4 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   const float mn = fmaxf(st.m, m4);
   const float mr = mn == -INFINITY ? 0.0f : mn;   // nothing finite yet: every term is 0
-  float l = __fmul_rn(st.l, __expf(__fsub_rn(st.m, mr)));
+  const float Mr = __fmul_rn(mr, kLog2e);
+  float l = __fmul_rn(st.l, __builtin_amdgcn_exp2f(__fsub_rn(__fmul_rn(st.m, kLog2e), Mr)));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l = __fadd_rn(l, __expf(__fsub_rn(s[i], mr)));
+  for (int i = 0; i < 4; ++i) l = __fadd_rn(l, __builtin_amdgcn_exp2f(__fmaf_rn(s[i], kLog2e, -Mr)));
   st = Stat{mn, l};
+}
+
+// d = m L - M is the rounding error of M (found exactly by the fma); 2^-d is
+// 1 - d ln2 to far below float precision (|d| <= ulp(M) / 2).
+__device__ __forceinline__ Stat stat_to_natural(Stat st) {
+  if (!(st.l > 0.0f)) return st;
+  const float M = __fmul_rn(st.m, kLog2e);
+  const float d = __fmaf_rn(st.m, kLog2e, -M);
+  return Stat{st.m, __fmaf_rn(st.l, __fmul_rn(-d, 0.693147182f), st.l)};
 }
 
 // Merge of (key, statistics) partials over the four 16-lane rows of a wave
@@ -1834,6 +1848,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       }
       // lanes of one row (equal lane % 16) combine; lanes 0..15 hold the wave's partials
       uint64_t key = best_key(best);
+      st = stat_to_natural(st);
       row_merge4(key, st);
       if (lane < 16) {
         s_rk[nt & 1][wv][lane] = key;
