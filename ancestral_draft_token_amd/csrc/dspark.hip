@@ -1250,7 +1250,7 @@ constexpr int kMfLdsPerWave = (kMfLdsTiles + kMfWaves - 1) / kMfWaves;   // 5
 constexpr int kMfTilesMax = kMfTilesPerWave + kMfLdsPerWave;            // 13
 constexpr int kMfKSteps = kResRank / 32;                   // 8
 constexpr int kMfAhead = 4;                                // base logits loaded this many tiles ahead
-constexpr int kMfNextAt = kMfTilesMax - 1 - kMfAhead;      // first tile loading the next N-tile's bases
+constexpr int kMfNextAt = kMfTilesMax - kMfAhead;          // the last kMfAhead tiles load the next N-tile's first bases
 constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
 constexpr int kMfERow = 528;                               // bytes per staged E row: 512 + 16 (16-byte aligned rows; 16 lanes of one 128-bit read cover all banks)
 constexpr int kMfSinkFloats = 1024;                        // sink: stores of lanes without a row or column
@@ -1283,25 +1283,33 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, uint4 b, f32x4_t c) {
 
 // The bias chain of one LDS M-tile, issued from the epilogue's hooks: step J
 // runs the matrix instruction of K-step J and reads the A fragment of K-step
-// J + 1, so each read has a stretch of VALU work to arrive in while one
-// fragment register set suffices. Fences keep the scheduler from gathering
-// the reads and multiplies back into one read-wait-multiply run ahead of the
+// J + 2. Two fragments are in flight, so each read has two stretches of VALU
+// work to arrive in (with one in flight a tile carrying an LDS chain took
+// ~1150 cycles against ~780 for a tile whose chain reads registers; with two,
+// ~940). Fences keep the scheduler from gathering the
+// reads and multiplies back into one read-wait-multiply run ahead of the
 // epilogue (the register pressure here leaves it no room to overlap them).
 struct LdsChain {
   const unsigned char* fb;   // this lane's fragment of K-step 0; K-steps are 1 KB apart
   uint4 e[kMfKSteps];        // B fragments
-  u32x4_t fr;                // A fragment in flight
+  u32x4_t fr0, fr1;          // A fragments in flight: even and odd K-steps
   f32x4_t an;
   __device__ __forceinline__ u32x4_t frag(int ks) const { return *reinterpret_cast<const u32x4_t*>(fb + ks * 1024); }
   __device__ __forceinline__ void start() {
-    fr = frag(0);
+    fr0 = frag(0);
+    fr1 = frag(1);
     an = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
   template <int J>
   __device__ __forceinline__ void step() {
     __builtin_amdgcn_sched_barrier(0);
-    an = mfma_bf16(fr, e[J], an);
-    if constexpr (J + 1 < kMfKSteps) fr = frag(J + 1);
+    if constexpr ((J & 1) == 0) {
+      an = mfma_bf16(fr0, e[J], an);
+      if constexpr (J + 2 < kMfKSteps) fr0 = frag(J + 2);
+    } else {
+      an = mfma_bf16(fr1, e[J], an);
+      if constexpr (J + 2 < kMfKSteps) fr1 = frag(J + 2);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 };
@@ -1517,7 +1525,13 @@ struct ERowSrc {
   bool ok;
 };
 
-__device__ __forceinline__ ERowSrc mf_erow_src(const MfArgs& a, const int* s_d, int nt, int t) {
+__device__ __forceinline__ ERowSrc mf_erow_src(const MfArgs& a, const int* s_d, int nt, int t_in) {
+  // Row and LDS addresses are recomputed from an opaque copy of the thread
+  // index at every use. Kept live across the position loop they were spilled
+  // to scratch, and the reload's wait (vmcnt 0) at the start of every
+  // position also waited for all logit stores still in flight.
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(t_in));
   const int row = 16 * nt + t / 16, j16 = 16 * (t % 16);
   const bool ok = row < a.B && j16 < a.r;
   return ERowSrc{a.E + (ok ? (size_t)s_d[row] * a.r + j16 : 0), ok};
