@@ -156,6 +156,108 @@ __device__ __forceinline__ void reduce_lanes(uint64_t& key, Stat& st, int width)
   }
 }
 
+// Merge of (key, statistics) partials over the four 16-lane rows of a wave
+// (lane l with l ^ 16, then with l ^ 32), with the gfx950 lane-swap
+// instructions instead of LDS-routed shuffles. Swapping a register with itself
+// hands every lane the pair {lower row's value, upper row's value} in that
+// order, so all lanes of a pair compute the same merge (max and stat_merge are
+// symmetric in any case).
+__device__ __forceinline__ void row_merge4(uint64_t& key, Stat& st) {
+#define DSPARK_SWAP_MERGE(swap)                                                                   \
+  {                                                                                              \
+    const auto lo = swap((uint32_t)key, (uint32_t)key, false, false);                            \
+    const auto hi = swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);            \
+    const auto mm = swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);            \
+    const auto ll = swap(__float_as_uint(st.l), __float_as_uint(st.l), false, false);            \
+    key = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);               \
+    st = stat_merge(Stat{__uint_as_float(mm[0]), __uint_as_float(ll[0])},                         \
+                    Stat{__uint_as_float(mm[1]), __uint_as_float(ll[1])});                        \
+  }
+  DSPARK_SWAP_MERGE(__builtin_amdgcn_permlane16_swap)
+  DSPARK_SWAP_MERGE(__builtin_amdgcn_permlane32_swap)
+#undef DSPARK_SWAP_MERGE
+}
+
+// Maximum of a 64-bit value over the 64 lanes of a wave, every lane getting
+// it, without LDS: DPP within quads (xor 1, xor 2), then the half-row and row
+// mirrors (which pair quad 0 with quad 1 and half 0 with half 1), then the
+// lane swaps across 16-lane rows.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#define DSPARK_DPP_MAX(ctrl)                                                                           \
+  {                                                                                                    \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, ctrl, 0xF, 0xF, false); \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), ctrl, 0xF, 0xF, false); \
+    x = umax64(x, ((uint64_t)hi << 32) | lo);                                                          \
+  }
+  DSPARK_DPP_MAX(0xB1)    // quad_perm(1,0,3,2): lane ^ 1
+  DSPARK_DPP_MAX(0x4E)    // quad_perm(2,3,0,1): lane ^ 2
+  DSPARK_DPP_MAX(0x141)   // row_half_mirror
+  DSPARK_DPP_MAX(0x140)   // row_mirror
+#undef DSPARK_DPP_MAX
+#define DSPARK_SWAP_MAX(swap)                                                                  \
+  {                                                                                            \
+    const auto lo = swap((uint32_t)x, (uint32_t)x, false, false);                              \
+    const auto hi = swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);              \
+    x = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);               \
+  }
+  DSPARK_SWAP_MAX(__builtin_amdgcn_permlane16_swap)
+  DSPARK_SWAP_MAX(__builtin_amdgcn_permlane32_swap)
+#undef DSPARK_SWAP_MAX
+  return x;
+}
+
+// Merge of (key, statistics) over the 64 lanes of a wave, every lane getting
+// the result: DPP within 16-lane rows (lane ^ 1, lane ^ 2, then the half-row
+// and row mirrors, which pair the quads and the halves of a row), then the
+// lane swaps across rows. Each step merges two partials of the same shape, and
+// max and stat_merge are symmetric, so every lane computes the same merge.
+__device__ __forceinline__ void wave_merge_key_stat(uint64_t& key, Stat& st) {
+#define DSPARK_DPP_MERGE(ctrl)                                                                            \
+  {                                                                                                       \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)key, ctrl, 0xF, 0xF, false); \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(key >> 32), ctrl, 0xF, 0xF, false); \
+    const int om = __builtin_amdgcn_update_dpp(0, __float_as_int(st.m), ctrl, 0xF, 0xF, false);          \
+    const int ol = __builtin_amdgcn_update_dpp(0, __float_as_int(st.l), ctrl, 0xF, 0xF, false);          \
+    key = umax64(key, ((uint64_t)hi << 32) | lo);                                                         \
+    st = stat_merge(st, Stat{__int_as_float(om), __int_as_float(ol)});                                    \
+  }
+  DSPARK_DPP_MERGE(0xB1)    // quad_perm(1,0,3,2): lane ^ 1
+  DSPARK_DPP_MERGE(0x4E)    // quad_perm(2,3,0,1): lane ^ 2
+  DSPARK_DPP_MERGE(0x141)   // row_half_mirror
+  DSPARK_DPP_MERGE(0x140)   // row_mirror
+#undef DSPARK_DPP_MERGE
+  row_merge4(key, st);
+}
+
+// Maximum of a 64-bit value over the lanes of a wave with equal lane % RB
+// (RB = 1, 2 or 4), every lane getting its class's maximum: rotations within
+// 16-lane rows by RB, 2 RB, ... (which keep the class), then the lane swaps
+// across rows.
+template <int RB>
+__device__ __forceinline__ uint64_t wave_max_u64_class(uint64_t x) {
+  if constexpr (RB == 1) {
+    return wave_max_u64(x);
+  } else {
+#define DSPARK_ROR_MAX(n)                                                                                    \
+  {                                                                                                          \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, 0x120 + (n), 0xF, 0xF, false); \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), 0x120 + (n), 0xF, 0xF, false); \
+    x = umax64(x, ((uint64_t)hi << 32) | lo);                                                                \
+  }
+    if constexpr (RB <= 2) DSPARK_ROR_MAX(2)   // row_ror:2
+    DSPARK_ROR_MAX(4)                           // row_ror:4
+    DSPARK_ROR_MAX(8)                           // row_ror:8
+#undef DSPARK_ROR_MAX
+    const auto l16 = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    const auto h16 = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    x = umax64(((uint64_t)h16[0] << 32) | l16[0], ((uint64_t)h16[1] << 32) | l16[1]);
+    const auto l32 = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    const auto h32 = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+    x = umax64(((uint64_t)h32[0] << 32) | l32[0], ((uint64_t)h32[1] << 32) | l32[1]);
+    return x;
+  }
+}
+
 __device__ __forceinline__ int clamp_token(int d, int V) { return d < 0 ? 0 : (d > V - 1 ? V - 1 : d); }
 
 struct StepArgs {
@@ -851,9 +953,25 @@ __device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Value of lane partner(l) within its group of 8 lanes, by DPP: the half-row
+// mirror (l <-> 7 - l, pairing the lanes that differ in bit 2), lane ^ 2 and
+// lane ^ 1. No LDS round trip, unlike a lane shuffle.
+__device__ __forceinline__ float dpp_mirror8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
 // Reduce-scatter of acc[RB][8] over the 8 rank-slice lanes of a column group
 // (lanes differing in bits 0..2): lane js ends with the sums of 4 columns
 // (4 * (js & 1) ..) of row er (RB = 4: js >> 1; RB = 2: js >> 2; RB = 1: 0).
+// The three exchange steps pair lanes of opposite bit 2 (by the mirror),
+// then of opposite bit 1, then of opposite bit 0; the mirror pairs 0-7, 1-6,
+// 2-5, 3-4, and the three steps still add every slice exactly once.
 template <int RB>
 __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js, float bias[4]) {
   const int b0 = js & 1, b1 = (js >> 1) & 1, b2 = (js >> 2) & 1;
@@ -866,13 +984,13 @@ __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js
       for (int c = 0; c < 8; ++c) {
         const float keep = b2 ? acc[(2 + r0) % RB][c] : acc[r0 % RB][c];
         const float send = b2 ? acc[r0 % RB][c] : acc[(2 + r0) % RB][c];
-        h[r0][c] = __fadd_rn(keep, __shfl_xor(send, 4, 64));
+        h[r0][c] = __fadd_rn(keep, dpp_mirror8(send));
       }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float keep = b1 ? h[1][c] : h[0][c];
       const float send = b1 ? h[0][c] : h[1][c];
-      h2[c] = __fadd_rn(keep, __shfl_xor(send, 2, 64));
+      h2[c] = __fadd_rn(keep, dpp_xor2(send));
     }
   } else if (RB == 2) {
     float h[8];
@@ -880,22 +998,22 @@ __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js
     for (int c = 0; c < 8; ++c) {
       const float keep = b2 ? acc[1 % RB][c] : acc[0][c];
       const float send = b2 ? acc[0][c] : acc[1 % RB][c];
-      h[c] = __fadd_rn(keep, __shfl_xor(send, 4, 64));
+      h[c] = __fadd_rn(keep, dpp_mirror8(send));
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], __shfl_xor(h[c], 2, 64));
+    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], dpp_xor2(h[c]));
   } else {
     float h[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) h[c] = __fadd_rn(acc[0][c], __shfl_xor(acc[0][c], 4, 64));
+    for (int c = 0; c < 8; ++c) h[c] = __fadd_rn(acc[0][c], dpp_mirror8(acc[0][c]));
 #pragma unroll
-    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], __shfl_xor(h[c], 2, 64));
+    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], dpp_xor2(h[c]));
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float keep = b0 ? h2[4 + i] : h2[i];
     const float send = b0 ? h2[i] : h2[4 + i];
-    bias[i] = __fadd_rn(keep, __shfl_xor(send, 1, 64));
+    bias[i] = __fadd_rn(keep, dpp_xor1(send));
   }
 }
 
@@ -1141,7 +1259,7 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     for (int rr = 0; rr < RB; ++rr) {
       uint64_t kk = (er == rr) ? best : 0ull;
       Stat ss = (er == rr) ? st : Stat{-INFINITY, 0.0f};
-      reduce_lanes(kk, ss, 64);
+      wave_merge_key_stat(kk, ss);
       if (lane == 0) {
         s_key[wv][rr] = kk;
         s_stat[wv][rr] = ss;
@@ -1194,8 +1312,8 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       s_fail = 1;
       atomicExch(a.fail, 1);
     }
-    // lanes of the same row (equal t % RB) combine: xor over the bits above log2(RB)
-    for (int mask = RB; mask < 64; mask <<= 1) xb = umax64(xb, shfl_xor_u64(xb, mask, 64));
+    // lanes of the same row (equal t % RB) combine
+    xb = wave_max_u64_class<RB>(xb);
     if (lane < RB) s_x[wv][lane] = xb;
     __syncthreads();
     if (s_fail) {
@@ -1408,56 +1526,6 @@ __device__ __forceinline__ Stat stat_to_natural(Stat st) {
   const float M = __fmul_rn(st.m, kLog2e);
   const float d = __fmaf_rn(st.m, kLog2e, -M);
   return Stat{st.m, __fmaf_rn(st.l, __fmul_rn(-d, 0.693147182f), st.l)};
-}
-
-// Merge of (key, statistics) partials over the four 16-lane rows of a wave
-// (lane l with l ^ 16, then with l ^ 32), with the gfx950 lane-swap
-// instructions instead of LDS-routed shuffles. Swapping a register with itself
-// hands every lane the pair {lower row's value, upper row's value} in that
-// order, so all lanes of a pair compute the same merge (max and stat_merge are
-// symmetric in any case).
-__device__ __forceinline__ void row_merge4(uint64_t& key, Stat& st) {
-#define DSPARK_SWAP_MERGE(swap)                                                                   \
-  {                                                                                              \
-    const auto lo = swap((uint32_t)key, (uint32_t)key, false, false);                            \
-    const auto hi = swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);            \
-    const auto mm = swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);            \
-    const auto ll = swap(__float_as_uint(st.l), __float_as_uint(st.l), false, false);            \
-    key = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);               \
-    st = stat_merge(Stat{__uint_as_float(mm[0]), __uint_as_float(ll[0])},                         \
-                    Stat{__uint_as_float(mm[1]), __uint_as_float(ll[1])});                        \
-  }
-  DSPARK_SWAP_MERGE(__builtin_amdgcn_permlane16_swap)
-  DSPARK_SWAP_MERGE(__builtin_amdgcn_permlane32_swap)
-#undef DSPARK_SWAP_MERGE
-}
-
-// Maximum of a 64-bit value over the 64 lanes of a wave, every lane getting
-// it, without LDS: DPP within quads (xor 1, xor 2), then the half-row and row
-// mirrors (which pair quad 0 with quad 1 and half 0 with half 1), then the
-// lane swaps across 16-lane rows.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#define DSPARK_DPP_MAX(ctrl)                                                                           \
-  {                                                                                                    \
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, ctrl, 0xF, 0xF, false); \
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), ctrl, 0xF, 0xF, false); \
-    x = umax64(x, ((uint64_t)hi << 32) | lo);                                                          \
-  }
-  DSPARK_DPP_MAX(0xB1)    // quad_perm(1,0,3,2): lane ^ 1
-  DSPARK_DPP_MAX(0x4E)    // quad_perm(2,3,0,1): lane ^ 2
-  DSPARK_DPP_MAX(0x141)   // row_half_mirror
-  DSPARK_DPP_MAX(0x140)   // row_mirror
-#undef DSPARK_DPP_MAX
-#define DSPARK_SWAP_MAX(swap)                                                                  \
-  {                                                                                            \
-    const auto lo = swap((uint32_t)x, (uint32_t)x, false, false);                              \
-    const auto hi = swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);              \
-    x = umax64(((uint64_t)hi[0] << 32) | lo[0], ((uint64_t)hi[1] << 32) | lo[1]);               \
-  }
-  DSPARK_SWAP_MAX(__builtin_amdgcn_permlane16_swap)
-  DSPARK_SWAP_MAX(__builtin_amdgcn_permlane32_swap)
-#undef DSPARK_SWAP_MAX
-  return x;
 }
 
 // log2(-log2 u) for u = ((x >> 9) + 1/2) 2^-23 of a Philox word x, with the
