@@ -1295,15 +1295,19 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     if (xr < B) {
       for (int gg = t / RB; gg < G; gg += kResThreads / RB) {
         const uint64_t* pw = a.xkey + ((size_t)(k & 1) * G + gg) * kResRowsMax + xr;
-        uint64_t w = ld_agent_u64(pw);
-        unsigned spins = 0;
-        while ((int)(w >> kResTagShift) != k + 1) {
-          if (++spins > a.spin_limit) {
-            failed = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          w = ld_agent_u64(pw);
+        // two reads of the word in flight, staggered by ~1500 cycles and
+        // checked in turn, so a word that lands is seen about half a round trip
+        // later on average (three in flight were no better: more traffic)
+        uint64_t w0 = ld_agent_u64(pw);
+        __builtin_amdgcn_s_sleep(24);
+        uint64_t w1 = ld_agent_u64(pw);
+        uint64_t w = 0;
+        for (unsigned spins = 0;; ++spins) {
+          if ((int)(w0 >> kResTagShift) == k + 1) { w = w0; break; }
+          w0 = ld_agent_u64(pw);
+          if ((int)(w1 >> kResTagShift) == k + 1) { w = w1; break; }
+          w1 = ld_agent_u64(pw);
+          if (spins > a.spin_limit) { failed = true; break; }
         }
         xb = umax64(xb, w);
       }
