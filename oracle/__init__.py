@@ -72,6 +72,15 @@ def _load():
             P, ctypes.c_double, ctypes.c_int,
             P, P, P, P, P, P, P, ctypes.c_int]
         lib.dspark_oracle_draft_block.restype = ctypes.c_int
+        lib.dspark_oracle_verify_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32]
+        lib.dspark_oracle_verify_uniform.restype = ctypes.c_float
+        lib.dspark_oracle_verify_gumbel.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32,
+                                                    ctypes.c_uint32]
+        lib.dspark_oracle_verify_gumbel.restype = ctypes.c_float
+        lib.dspark_oracle_verify_standard.argtypes = [
+            P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+            P, P, P, P, P, P]
+        lib.dspark_oracle_verify_standard.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -160,3 +169,47 @@ def draft_block(w, *, forced: Optional[np.ndarray] = None, want_logits: bool = T
         raise RuntimeError(f"oracle draft_block failed with {rc}")
     return OracleResult(tokens=tokens, own_tokens=own, logits=logits, q=q, margin=margin,
                         ncand=ncand, cand=cand)
+
+
+@dataclasses.dataclass
+class VerifyResult:
+    n_accepted: np.ndarray      # [B] int32: drafts accepted
+    out_tokens: np.ndarray      # [B,K+1] int32: accepted drafts, the emitted token, then -1
+    margin: np.ndarray          # [B] float64: best minus runner-up score of the emitted draw
+    ncand: np.ndarray           # [B] int32: scores within tie_eps of the best
+    cand: np.ndarray            # [B,MAX_CAND] int32: those indices, ascending
+
+
+def verify_uniform(seed: int, offset: int, k: int) -> float:
+    return float(_load().dspark_oracle_verify_uniform(seed & (2**64 - 1), offset & (2**64 - 1), k))
+
+
+def verify_gumbel(seed: int, offset: int, j: int, v: int) -> float:
+    return float(_load().dspark_oracle_verify_gumbel(seed & (2**64 - 1), offset & (2**64 - 1), j, v))
+
+
+def verify_standard(draft_tokens, q, p, seed, offset, tie_eps: float = TIE_EPS) -> VerifyResult:
+    """Standard token-level verification of a draft block (rules and readings in
+    the header section of ``dspark_oracle.c``). ``q`` [B,K,V] and ``p``
+    [B,K+1,V] are float32 (other float types are rounded to float32 first)."""
+    lib = _load()
+    d = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    B, K = d.shape
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    V = p.shape[-1]
+    if q.shape != (B, K, V) or p.shape != (B, K + 1, V):
+        raise ValueError("shapes: q [B,K,V], p [B,K+1,V]")
+    sd = np.ascontiguousarray(seed, dtype=np.int64)
+    off = np.ascontiguousarray(offset, dtype=np.int64)
+    n = np.zeros(B, dtype=np.int32)
+    out = np.zeros((B, K + 1), dtype=np.int32)
+    margin = np.zeros(B, dtype=np.float64)
+    ncand = np.zeros(B, dtype=np.int32)
+    cand = np.full((B, MAX_CAND), -1, dtype=np.int32)
+    rc = lib.dspark_oracle_verify_standard(_ptr(q), _ptr(p), _ptr(d), _ptr(sd), _ptr(off), B, K, V,
+                                           float(tie_eps), MAX_CAND, _ptr(n), _ptr(out), None,
+                                           _ptr(margin), _ptr(ncand), _ptr(cand))
+    if rc != 0:
+        raise RuntimeError(f"oracle verify_standard failed with {rc}")
+    return VerifyResult(n_accepted=n, out_tokens=out, margin=margin, ncand=ncand, cand=cand)

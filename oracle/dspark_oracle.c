@@ -304,3 +304,128 @@ int dspark_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* ---- standard token-level verification ------------------------------------
+ *
+ * What the draft block feeds: its tokens d_k and proposals q_k are checked
+ * against target distributions p_k by the standard rule ("brb-nv/TensorRT-LLM
+ * pull 21", section "2. Golden sampling semantics": rejection_sample_method
+ * standard, token-level verification, the default). The pages name the rule
+ * and do not spell it out; this is the textbook rule of Leviathan, Kalman
+ * and Matias, "Fast Inference from Transformers via Speculative Decoding"
+ * (ICML 2023), section 2.3, and Chen et al., "Accelerating Large Language
+ * Model Decoding with Speculative Sampling" (2023), algorithm 2:
+ *   for k = 0 .. K-1: accept d_k with probability min(1, p_k(d_k) / q_k(d_k));
+ *   at the first rejection emit a token drawn from max(0, p_k - q_k)
+ *   (normalised) and stop; if all K are accepted emit a bonus token drawn
+ *   from p_K.
+ * Output per row: n (the number accepted) and K+1 tokens: d_0 .. d_{n-1},
+ * the emitted token, then -1.
+ *
+ * Readings (the pages are silent; each is listed in the design notes):
+ *  - ratio = float32(p_k(d_k) / q_k(d_k)), one IEEE division; accept iff
+ *    u_k < ratio (float32 compare). q = 0 < p gives +inf (accept); 0/0 gives
+ *    NaN (reject).
+ *  - u_k = ((x >> 9) + 1/2) 2^-23 for the Philox word x = word 0 of counter
+ *    (0xFFFFFFFF, 256 + k, lo32(offset), hi32(offset)) under key
+ *    (lo32(seed), hi32(seed)): the draft uses counter words y = k < 256, so
+ *    the streams never meet.
+ *  - The emitted token at position j (j < K: residual; j = K: bonus) is the
+ *    Gumbel-max draw over w_v = float32(p_j(v) - q_j(v)) where that is > 0
+ *    (residual) or w_v = p_j(v) (bonus), among v with w_v > 0: the lowest
+ *    index of the largest ln(w_v) + g_v, g_v = -ln(-ln u) of word (v & 3) of
+ *    counter (v >> 2, 512 + j, lo32(offset), hi32(offset)). Scores are
+ *    rounded to float32 before the argmax, as the kernel decides in float32.
+ *    A residual with no positive entry (possible only through rounding, as
+ *    p = q then) is replaced by p_j.
+ */
+
+static uint32_t verify_word(uint64_t seed, uint64_t offset, uint32_t x, uint32_t y, uint32_t w)
+{
+    uint32_t ctr[4] = { x, y, (uint32_t)offset, (uint32_t)(offset >> 32) };
+    uint32_t key[2] = { (uint32_t)seed, (uint32_t)(seed >> 32) };
+    uint32_t out[4];
+    dspark_oracle_philox4x32_10(ctr, key, out);
+    return out[w & 3u];
+}
+
+/* The acceptance uniform of position k, as float32 (exact). */
+float dspark_oracle_verify_uniform(uint64_t seed, uint64_t offset, uint32_t k)
+{
+    return (float)dspark_oracle_uniform(verify_word(seed, offset, 0xFFFFFFFFu, 256u + k, 0u));
+}
+
+/* Gumbel variate of column v for the token emitted at position j. */
+float dspark_oracle_verify_gumbel(uint64_t seed, uint64_t offset, uint32_t j, uint32_t v)
+{
+    return dspark_oracle_gumbel(verify_word(seed, offset, v >> 2, 512u + j, v));
+}
+
+int dspark_oracle_verify_standard(
+    const float* q, const float* p, const int32_t* draft, const int64_t* seed, const int64_t* offset,
+    int B, int K, int V, double tie_eps, int max_cand,
+    int32_t* n_accepted, int32_t* out_tokens, int32_t* emit_pos,
+    double* margin, int32_t* ncand, int32_t* cand)
+{
+    if (B < 0 || K < 0 || V <= 0) return -1;
+    if (!q || !p || !draft || !seed || !offset || !n_accepted || !out_tokens) return -1;
+    if (cand && max_cand <= 0) return -1;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int b = 0; b < B; ++b) {
+        const uint64_t sd = (uint64_t)seed[b], off = (uint64_t)offset[b];
+        int n = 0;
+        for (; n < K; ++n) {
+            int d = draft[(size_t)b * K + n];
+            if (d < 0) d = 0;
+            if (d > V - 1) d = V - 1;
+            const float pv = p[((size_t)b * (K + 1) + n) * V + d];
+            const float qv = q[((size_t)b * K + n) * V + d];
+            const float ratio = pv / qv;
+            const float u = dspark_oracle_verify_uniform(sd, off, (uint32_t)n);
+            if (!(u < ratio)) break;
+        }
+        /* the emitted token */
+        const float* pj = p + ((size_t)b * (K + 1) + n) * V;
+        const float* qj = n < K ? q + ((size_t)b * K + n) * V : NULL;
+        int use_p = (qj == NULL);
+        if (!use_p) {
+            int any = 0;
+            for (int v = 0; v < V && !any; ++v) any = (pj[v] - qj[v]) > 0.0f;
+            use_p = !any;
+        }
+        int best = -1;
+        float zbest = 0.0f;
+        for (int v = 0; v < V; ++v) {
+            const float w = use_p ? pj[v] : pj[v] - qj[v];
+            if (!(w > 0.0f)) continue;
+            const float z = (float)log((double)w) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            if (best < 0 || z > zbest) { best = v; zbest = z; }
+        }
+        double second = -INFINITY;
+        int n_near = 0;
+        for (int v = 0; v < V && best >= 0; ++v) {
+            const float w = use_p ? pj[v] : pj[v] - qj[v];
+            if (!(w > 0.0f)) continue;
+            const float z = (float)log((double)w) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            if (v != best && (double)z > second) second = (double)z;
+            if ((double)z >= (double)zbest - tie_eps) {
+                if (cand && n_near < max_cand) cand[(size_t)b * max_cand + n_near] = v;
+                ++n_near;
+            }
+        }
+        n_accepted[b] = n;
+        int32_t* out = out_tokens + (size_t)b * (K + 1);
+        for (int i = 0; i < n; ++i) {
+            int d = draft[(size_t)b * K + i];
+            out[i] = d < 0 ? 0 : (d > V - 1 ? V - 1 : d);
+        }
+        out[n] = best < 0 ? 0 : best;
+        for (int i = n + 1; i <= K; ++i) out[i] = -1;
+        if (emit_pos) emit_pos[b] = n;
+        if (margin) margin[b] = best < 0 ? INFINITY : (double)zbest - second;
+        if (ncand) ncand[b] = n_near;
+    }
+    return 0;
+}
