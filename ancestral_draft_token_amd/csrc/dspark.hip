@@ -2018,6 +2018,131 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 }
 
 // ---------------------------------------------------------------------------
+// Standard token-level verification of a draft block ("brb-nv/TensorRT-LLM
+// pull 21", section "2. Golden sampling semantics": rejection_sample_method
+// standard, the default). The rule is the textbook one (Leviathan, Kalman and
+// Matias, ICML 2023, section 2.3): accept d_k with probability
+// min(1, p_k(d_k) / q_k(d_k)); at the first rejection emit a draw from
+// max(0, p_k - q_k) normalised; if all K are accepted emit a bonus draw from
+// p_K. Conventions (ratio in float32, the Philox counters of the uniforms and
+// of the Gumbel noise, the fallback for an empty residual) are stated in
+// include/dspark.h.
+//
+// Two launches, no counters (the workspace needs no initialisation):
+// verify_partials, one block per (8192-column chunk, row), streams the row
+// the emitted token is drawn from (p_j and q_j, or p_K) once and leaves the
+// chunk's best Gumbel-max key; verify_finish, one wave per row, merges them.
+// Every wave finds the first rejected position itself: lane i tests position
+// i (64 at a time) and a ballot picks the first failure.
+// ---------------------------------------------------------------------------
+constexpr int kVerCols = 8192;   // columns per verify_partials block (32 per thread)
+
+struct VerArgs {
+  const int32_t* draft;    // [B,K]
+  const float* q;          // [B,K,V]
+  const float* p;          // [B,K+1,V]
+  const int64_t* seed;
+  const int64_t* offset;
+  uint64_t* part;          // [B][n_chunks][2]: best key of the draw's distribution, and of p_j
+  int32_t* n_accepted;     // [B]
+  int32_t* out_tokens;     // [B,K+1]
+  int B, K, V, n_chunks;
+};
+
+__device__ __forceinline__ uint4 verify_philox(uint64_t seed, uint64_t off, uint32_t x, uint32_t y) {
+  return philox4x32_10(make_uint4(x, y, (uint32_t)off, (uint32_t)(off >> 32)), (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+// The first rejected position of row b (K if every draft is accepted); every
+// lane of the wave gets it.
+__device__ __forceinline__ int verify_first_reject(const VerArgs& a, int b) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
+  for (int k0 = 0; k0 < a.K; k0 += 64) {
+    const int k = k0 + lane;
+    bool reject = false;
+    if (k < a.K) {
+      const int d = clamp_token(a.draft[(size_t)b * a.K + k], a.V);
+      const float pv = a.p[((size_t)b * (a.K + 1) + k) * a.V + d];
+      const float qv = a.q[((size_t)b * a.K + k) * a.V + d];
+      const float ratio = __fdiv_rn(pv, qv);
+      const uint32_t x = verify_philox(seed, off, 0xFFFFFFFFu, 256u + (uint32_t)k).x;
+      const float u = __fmul_rn(__fadd_rn((float)(x >> 9), 0.5f), 0x1p-23f);   // exact
+      reject = !(u < ratio);
+    }
+    const uint64_t m = __ballot(reject);
+    if (m) return k0 + __builtin_ctzll(m);
+  }
+  return a.K;
+}
+
+__global__ __launch_bounds__(kThreads) void verify_partials(VerArgs a) {
+  __shared__ uint64_t s_k[kWaves][2];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int j = verify_first_reject(a, b);
+  const bool residual = j < a.K;
+  const float* pj = a.p + ((size_t)b * (a.K + 1) + j) * a.V;
+  const float* qj = a.q + ((size_t)b * a.K + (residual ? j : 0)) * a.V;
+  const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
+  const int c0 = c * kVerCols;
+  uint64_t kw = 0, kp = 0;   // best key over w = max(0, p - q) (or p), and over p
+#pragma unroll 2
+  for (int i = 0; i < kVerCols / (4 * kThreads); ++i) {
+    const int v = c0 + 4 * t + i * 4 * kThreads;
+    if (v >= a.V) break;
+    const float4 pv = *reinterpret_cast<const float4*>(pj + v);
+    float4 qv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (residual) qv = *reinterpret_cast<const float4*>(qj + v);
+    const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)j);
+    const float pe[4] = {pv.x, pv.y, pv.z, pv.w};
+    const float qe[4] = {qv.x, qv.y, qv.z, qv.w};
+    const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // base-2 form of ln w + g: log2 w - log2(-log2 u) (the same order)
+      const float gl = gumbel_log2(xe[e]);
+      const float w = residual ? __fsub_rn(pe[e], qe[e]) : pe[e];
+      if (w > 0.0f) kw = umax64(kw, score_key(__fsub_rn(__builtin_amdgcn_logf(w), gl), (uint32_t)(v + e)));
+      if (pe[e] > 0.0f) kp = umax64(kp, score_key(__fsub_rn(__builtin_amdgcn_logf(pe[e]), gl), (uint32_t)(v + e)));
+    }
+  }
+  kw = wave_max_u64(kw);
+  kp = wave_max_u64(kp);
+  if (lane == 0) {
+    s_k[wv][0] = kw;
+    s_k[wv][1] = kp;
+  }
+  __syncthreads();
+  if (t < 2) {
+    uint64_t m = s_k[0][t];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = umax64(m, s_k[w][t]);
+    a.part[((size_t)b * a.n_chunks + c) * 2 + t] = m;
+  }
+}
+
+__global__ __launch_bounds__(64) void verify_finish(VerArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int n = verify_first_reject(a, b);
+  uint64_t kw = 0, kp = 0;
+  for (int c = lane; c < a.n_chunks; c += 64) {
+    kw = umax64(kw, a.part[((size_t)b * a.n_chunks + c) * 2]);
+    kp = umax64(kp, a.part[((size_t)b * a.n_chunks + c) * 2 + 1]);
+  }
+  kw = wave_max_u64(kw);
+  kp = wave_max_u64(kp);
+  // an empty residual (only through rounding) falls back to p_j; no positive
+  // entry at all gives token 0
+  const uint64_t key = kw ? kw : kp;
+  const int tok = key ? clamp_token((int)key_token(key), a.V) : 0;
+  int32_t* out = a.out_tokens + (size_t)b * (a.K + 1);
+  for (int i = lane; i <= a.K; i += 64)
+    out[i] = i < n ? clamp_token(a.draft[(size_t)b * a.K + i], a.V) : (i == n ? tok : -1);
+  if (lane == 0) a.n_accepted[b] = n;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Workspace {
@@ -2324,6 +2449,41 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   return DSPARK_OK;
 }
 
+inline int verify_chunks(int V) { return (V + kVerCols - 1) / kVerCols; }
+
+inline int verify_check(int B, int K, int V) {
+  if (B < 0 || K < 0 || V <= 0) return DSPARK_ERR_ARG;
+  if (K > kMaxK || V % 4 != 0 || B > 65535) return DSPARK_ERR_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
+inline size_t verify_workspace(int B, int V) {
+  return align_up((size_t)B * verify_chunks(V) * 2 * sizeof(uint64_t), 256);
+}
+
+int verify_standard_impl(const int32_t* draft, const float* q, const float* p, const int64_t* seed,
+                         const int64_t* offset, int B, int K, int V, int32_t* n_accepted,
+                         int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  int rc = verify_check(B, K, V);
+  if (rc != DSPARK_OK) return rc;
+  if (B == 0) return DSPARK_OK;
+  if ((K > 0 && (!draft || !q)) || !p || !seed || !offset || !n_accepted || !out_tokens) return DSPARK_ERR_ARG;
+  if ((K > 0 && !aligned16(q)) || !aligned16(p)) return DSPARK_ERR_ARG;
+  if (!workspace || workspace_bytes < verify_workspace(B, V) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return DSPARK_ERR_WORKSPACE;
+  VerArgs a;
+  a.draft = draft; a.q = q; a.p = p; a.seed = seed; a.offset = offset;
+  a.part = static_cast<uint64_t*>(workspace);
+  a.n_accepted = n_accepted; a.out_tokens = out_tokens;
+  a.B = B; a.K = K; a.V = V; a.n_chunks = verify_chunks(V);
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  hipLaunchKernelGGL(verify_partials, dim3(a.n_chunks, B), dim3(kThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
+  hipLaunchKernelGGL(verify_finish, dim3(B), dim3(64), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
 }  // namespace dspark
 
 extern "C" {
@@ -2346,6 +2506,8 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax),
       reinterpret_cast<const void*>(&res_clear),
+      reinterpret_cast<const void*>(&verify_partials),
+      reinterpret_cast<const void*>(&verify_finish),
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false>),
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false>),
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true>),
@@ -2359,6 +2521,19 @@ int dspark_init(void) {
 size_t dspark_workspace_bytes(int B, int K, int V, int r) {
   if (dspark::check_sizes(B, K, V, r) != DSPARK_OK) return 0;
   return dspark::workspace_layout(B, K, V, r, nullptr, nullptr);
+}
+
+size_t dspark_verify_workspace_bytes(int B, int K, int V) {
+  if (dspark::verify_check(B, K, V) != DSPARK_OK) return 0;
+  return dspark::verify_workspace(B, V);
+}
+
+int dspark_verify_standard(const int32_t* draft_tokens, const float* draft_probs, const float* target_probs,
+                           const int64_t* seed, const int64_t* offset, int B, int K, int V,
+                           int32_t* n_accepted, int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return dspark::verify_standard_impl(draft_tokens, draft_probs, target_probs, seed, offset, B, K, V, n_accepted,
+                                      out_tokens, workspace, workspace_bytes, stream);
 }
 
 int dspark_draft_block(const void* base_logits, int base_dtype, const uint16_t* E, const uint16_t* W,

@@ -165,6 +165,53 @@ typedef enum {
  * dspark_draft_block_chunked always uses the last two plans. */
 int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds);
 
+/* Standard token-level verification of a draft block ("brb-nv/TensorRT-LLM
+ * pull 21", section "2. Golden sampling semantics": rejection_sample_method
+ * standard, token-level verification). The pages name the rule; this is the
+ * textbook one (Leviathan, Kalman and Matias, "Fast Inference from
+ * Transformers via Speculative Decoding", ICML 2023, section 2.3): for
+ * k = 0 .. K-1 accept d_k with probability min(1, p_k(d_k) / q_k(d_k)); at the
+ * first rejection emit a token drawn from max(0, p_k - q_k) normalised and
+ * stop; if all K drafts are accepted, emit a bonus token drawn from p_K.
+ *
+ *   draft_tokens  [B,K]    int32 d_k (as dspark_draft_block writes them; clamped into [0,V))
+ *   draft_probs   [B,K,V]  float32 q_k (dspark_draft_block's draft_probs); may be NULL if K == 0
+ *   target_probs  [B,K+1,V] float32 p_k, the target's distributions
+ *   seed, offset  [B]      int64, the request's Philox slot (as for the draft)
+ *   B, K, V       B >= 0, 0 <= K <= 255, V > 0 and V % 4 == 0, B <= 65535
+ *   n_accepted    [B]      int32 out: the number n of drafts accepted (0..K)
+ *   out_tokens    [B,K+1]  int32 out: d_0 .. d_{n-1}, the emitted token, then -1
+ *   workspace     device scratch of at least dspark_verify_workspace_bytes(B,K,V)
+ *                 bytes, 8-byte aligned; contents need no initialisation
+ *
+ * Conventions (the pages leave them open):
+ *   - ratio = float32(p_k(d_k) / q_k(d_k)), one IEEE division; accept iff
+ *     u_k < ratio. q = 0 < p accepts; 0/0 (NaN) rejects.
+ *   - u_k = ((x >> 9) + 1/2) 2^-23 (exact in float32), x = output word 0 of
+ *     Philox4x32-10 at counter (0xFFFFFFFF, 256 + k, lo32(offset),
+ *     hi32(offset)) under key (lo32(seed), hi32(seed)). The draft block uses
+ *     counter word 1 = k < 256, so the two streams never meet.
+ *   - The emitted token at position j (j < K after a rejection, j = K for the
+ *     bonus) is the Gumbel-max draw over w_v = float32(p_j(v) - q_j(v)) (or
+ *     p_K(v)) among v with w_v > 0: the lowest index of the largest
+ *     ln w_v + g_v, g_v = -ln(-ln u) of output word (v & 3) of counter
+ *     (v >> 2, 512 + j, lo32(offset), hi32(offset)). A residual with no
+ *     positive entry (only through rounding) is replaced by p_j; a row with
+ *     no positive entry at all emits token 0.
+ *
+ * Two launches on `stream` (a partial pass per 8192-column chunk and row,
+ * then a merge per row); graph-capturable; nothing is allocated. Errors as
+ * for dspark_draft_block: DSPARK_ERR_ARG for null or misaligned pointers
+ * (q and p need 16-byte alignment), DSPARK_ERR_UNSUPPORTED for sizes outside
+ * the limits above, DSPARK_ERR_WORKSPACE, DSPARK_ERR_HIP. B == 0 enqueues
+ * nothing. */
+size_t dspark_verify_workspace_bytes(int B, int K, int V);
+int dspark_verify_standard(
+    const int32_t* draft_tokens, const float* draft_probs, const float* target_probs,
+    const int64_t* seed, const int64_t* offset, int B, int K, int V,
+    int32_t* n_accepted, int32_t* out_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* dspark_status_string(int status);
 

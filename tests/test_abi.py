@@ -123,3 +123,39 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(adt, "_lib", None)
     with pytest.raises(RuntimeError):
         adt.load_library(str(tmp_path / "nope.so"))
+
+
+# ---- standard verification: host checks (nothing is enqueued) ---------------
+
+def _verify(lib, **kw):
+    a = dict(draft=16, q=16, p=16, seed=16, offset=16, B=2, K=3, V=64, n=16, out=16, ws=16,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.dspark_verify_standard(a["draft"], a["q"], a["p"], a["seed"], a["offset"], a["B"], a["K"],
+                                      a["V"], a["n"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_verify_workspace_bytes(lib):
+    assert adt.dspark_verify_workspace_bytes(88, 7, 200064) >= 88 * 25 * 16
+    assert adt.dspark_verify_workspace_bytes(1, 7, 8) > 0
+    assert adt.dspark_verify_workspace_bytes(1, 256, 64) == 0      # K > 255
+    assert adt.dspark_verify_workspace_bytes(1, 7, 66) == 0        # V % 4 != 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=None), adt.DSPARK_ERR_ARG),
+    (dict(q=None), adt.DSPARK_ERR_ARG),
+    (dict(n=None), adt.DSPARK_ERR_ARG),
+    (dict(p=24), adt.DSPARK_ERR_ARG),                  # p not 16-byte aligned
+    (dict(V=66), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(K=256), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(B=-1), adt.DSPARK_ERR_ARG),
+    (dict(ws=None), adt.DSPARK_ERR_WORKSPACE),
+    (dict(ws_bytes=8), adt.DSPARK_ERR_WORKSPACE),
+])
+def test_verify_host_checks(lib, kw, status):
+    assert _verify(lib, **kw) == status
+
+
+def test_verify_empty_batch_enqueues_nothing(lib):
+    assert _verify(lib, B=0, draft=None, q=None, p=None) == adt.DSPARK_OK
