@@ -199,8 +199,9 @@ int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds);
  *     positive entry (only through rounding) is replaced by p_j; a row with
  *     no positive entry at all emits token 0.
  *
- * Two launches on `stream` (a partial pass per 8192-column chunk and row,
- * then a merge per row); graph-capturable; nothing is allocated. Errors as
+ * Two launches on `stream` (a partial pass per chunk of 1024 to 8192
+ * columns and row, then a merge per row); graph-capturable; nothing is
+ * allocated. Errors as
  * for dspark_draft_block: DSPARK_ERR_ARG for null or misaligned pointers
  * (q and p need 16-byte alignment), DSPARK_ERR_UNSUPPORTED for sizes outside
  * the limits above, DSPARK_ERR_WORKSPACE, DSPARK_ERR_HIP. B == 0 enqueues

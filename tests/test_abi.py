@@ -136,7 +136,7 @@ def _verify(lib, **kw):
 
 
 def test_verify_workspace_bytes(lib):
-    assert adt.dspark_verify_workspace_bytes(88, 7, 200064) >= 88 * 25 * 16
+    assert adt.dspark_verify_workspace_bytes(88, 7, 200064) >= 88 * 25 * 8
     assert adt.dspark_verify_workspace_bytes(1, 7, 8) > 0
     assert adt.dspark_verify_workspace_bytes(1, 256, 64) == 0      # K > 255
     assert adt.dspark_verify_workspace_bytes(1, 7, 66) == 0        # V % 4 != 0

@@ -161,3 +161,14 @@ def test_verify_full_size_after_the_draft_block():
     nn = n.cpu().numpy()
     assert ((nn >= 0) & (nn <= K)).all()
     say(f"accepted per row: mean {nn.mean():.2f}")
+
+
+def test_verify_empty_residual_falls_back_to_the_target():
+    """p_k = q_k / 2 (not normalised): the ratio is 1/2, so about half the
+    positions reject, and max(0, p - q) is empty everywhere: both sides then
+    draw the emitted token from p_k itself."""
+    d, q, p, sd, off = _case(12, 3, 9000, seed=6)
+    p[:, :3] = (0.5 * q.astype(np.float64)).astype(np.float32)
+    n, out = verify_gpu(d, q, p, sd, off)
+    assert (n < 3).any()
+    check(d, q, p, sd, off, n, out)
