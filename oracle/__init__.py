@@ -81,6 +81,13 @@ def _load():
             P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
             P, P, P, P, P, P]
         lib.dspark_oracle_verify_standard.restype = ctypes.c_int
+        lib.dspark_oracle_verify_block_weights.argtypes = [
+            P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P]
+        lib.dspark_oracle_verify_block_weights.restype = ctypes.c_int
+        lib.dspark_oracle_verify_block.argtypes = [
+            P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+            P, P, P, P, P, P]
+        lib.dspark_oracle_verify_block.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -213,3 +220,66 @@ def verify_standard(draft_tokens, q, p, seed, offset, tie_eps: float = TIE_EPS) 
     if rc != 0:
         raise RuntimeError(f"oracle verify_standard failed with {rc}")
     return VerifyResult(n_accepted=n, out_tokens=out, margin=margin, ncand=ncand, cand=cand)
+
+
+def _verify_inputs(draft_tokens, q, p):
+    d = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    B, K = d.shape
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    V = p.shape[-1]
+    if q.shape != (B, K, V) or p.shape != (B, K + 1, V):
+        raise ValueError("shapes: q [B,K,V], p [B,K+1,V]")
+    return d, q, p, B, K, V
+
+
+@dataclasses.dataclass
+class BlockWeights:
+    w: np.ndarray               # [B,K+1] float64: prefix weights w_0 .. w_K
+    S: np.ndarray               # [B,K+1] float64: residual masses S_0 .. S_{K-1} (S_K = 0)
+    h: np.ndarray               # [B,K+1] float64: thresholds (h_0 = 1)
+    resid: Optional[np.ndarray]  # [B,K+1,V] float32: weights of each position's emission
+
+
+def verify_block_weights(draft_tokens, q, p, want_resid: bool = True) -> BlockWeights:
+    """Prefix weights, residual masses and thresholds of block verification
+    (rule and readings in the block-verification section of
+    ``dspark_oracle.c``)."""
+    lib = _load()
+    d, q, p, B, K, V = _verify_inputs(draft_tokens, q, p)
+    w = np.zeros((B, K + 1), dtype=np.float64)
+    S = np.zeros((B, K + 1), dtype=np.float64)
+    h = np.zeros((B, K + 1), dtype=np.float64)
+    resid = np.zeros((B, K + 1, V), dtype=np.float32) if want_resid else None
+    rc = lib.dspark_oracle_verify_block_weights(_ptr(q), _ptr(p), _ptr(d), B, K, V, _ptr(w), _ptr(S),
+                                                _ptr(h), _ptr(resid))
+    if rc != 0:
+        raise RuntimeError(f"oracle verify_block_weights failed with {rc}")
+    return BlockWeights(w=w, S=S, h=h, resid=resid)
+
+
+@dataclasses.dataclass
+class BlockVerifyResult(VerifyResult):
+    tau_margin: np.ndarray = None   # [B] float64: min over j of |eta_j - h_j|
+
+
+def verify_block(draft_tokens, q, p, seed, offset, tie_eps: float = TIE_EPS) -> BlockVerifyResult:
+    """Block verification of a draft block (Sun et al., 2024; rule and
+    readings in the block-verification section of ``dspark_oracle.c``)."""
+    lib = _load()
+    d, q, p, B, K, V = _verify_inputs(draft_tokens, q, p)
+    sd = np.ascontiguousarray(seed, dtype=np.int64)
+    off = np.ascontiguousarray(offset, dtype=np.int64)
+    n = np.zeros(B, dtype=np.int32)
+    out = np.zeros((B, K + 1), dtype=np.int32)
+    tm = np.zeros(B, dtype=np.float64)
+    margin = np.zeros(B, dtype=np.float64)
+    ncand = np.zeros(B, dtype=np.int32)
+    cand = np.full((B, MAX_CAND), -1, dtype=np.int32)
+    rc = lib.dspark_oracle_verify_block(_ptr(q), _ptr(p), _ptr(d), _ptr(sd), _ptr(off), B, K, V,
+                                        float(tie_eps), MAX_CAND, _ptr(n), _ptr(out), _ptr(tm),
+                                        _ptr(margin), _ptr(ncand), _ptr(cand))
+    if rc != 0:
+        raise RuntimeError(f"oracle verify_block failed with {rc}")
+    return BlockVerifyResult(n_accepted=n, out_tokens=out, margin=margin, ncand=ncand, cand=cand,
+                             tau_margin=tm)

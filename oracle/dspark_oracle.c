@@ -429,3 +429,166 @@ int dspark_oracle_verify_standard(
     }
     return 0;
 }
+
+/* ---- block verification ----------------------------------------------------
+ *
+ * The pages' other rule ("brb-nv/TensorRT-LLM pull 21", section "2. Golden
+ * sampling semantics": rejection_sample_method block, which replaces the
+ * token-level chain with block verification, Sun et al., 2024; its test
+ * list states that the rule is lossless, checked by chi-square). The pages
+ * only name it; the algorithm is the one of Sun, Mendlovic, Leviathan,
+ * Aharoni, Beirami, Ro and Suresh, "Block Verification Accelerates
+ * Speculative Decoding" (2024), restated here in the indices of the draft
+ * block (drafts d_0 .. d_{K-1}, d_j drawn from q_j; p_j the target
+ * distribution after d_0 .. d_{j-1}, p_K the one after the whole block):
+ *   w_0 = 1,  w_{j+1} = min(1, w_j * p_j(d_j) / q_j(d_j))   (prefix weights)
+ *   S_j = sum_v max(w_j p_j(v) - q_j(v), 0)                 (residual mass)
+ *   h_j = S_j / (S_j + 1 - w_j) for 1 <= j < K,  h_K = w_K
+ *   n = the largest j in 1..K whose uniform eta_j passes h_j, else 0
+ *   emit d_0 .. d_{n-1}, then a token drawn from max(w_n p_n - q_n, 0)
+ *   (normalised) if n < K, or from p_K if n = K.
+ * Unlike the token-level rule, a failed test at j does not end the scan: a
+ * later position can still pass and keep the whole prefix.
+ *
+ * Readings (the pages are silent; each is listed in the design notes):
+ *  - Weights, residual masses and thresholds in double. The ratio is one
+ *    IEEE double division of the float32 inputs; w_{j+1} is the product
+ *    w_j * ratio clamped to [0, 1] (q = 0 < p gives 1; 0/0 gives 0).
+ *    Residual entries are w_j * p - q (a product and a difference, no fused
+ *    multiply-add) clamped at 0. h_j = 0 when S_j = 0 (a stop there would
+ *    need an empty residual; in exact arithmetic such a stop has
+ *    probability zero, whatever h_j is).
+ *  - eta_j is the acceptance uniform of draft d_{j-1}, the same word as the
+ *    token-level rule's u_{j-1}; the test passes iff eta_j < h_j (the
+ *    comparison in double).
+ *  - The emitted token is drawn as in the token-level rule, from the weights
+ *    float32(max(w_n p_n(v) - q_n(v), 0)) (or p_K(v)) with the Gumbel words
+ *    of position n; an empty residual is replaced by p_n.
+ */
+
+static int clamp_tok(int d, int V)
+{
+    return d < 0 ? 0 : (d > V - 1 ? V - 1 : d);
+}
+
+/* Prefix weights w[0..K], residual masses S[0..K-1] and thresholds h[1..K]
+ * of one row (h[0] = 1: the empty prefix is always kept). */
+static void block_weights(const float* q, const float* p, const int32_t* draft, int K, int V,
+                          double* w, double* S, double* h)
+{
+    w[0] = 1.0;
+    for (int j = 0; j < K; ++j) {
+        const int d = clamp_tok(draft[j], V);
+        const double ratio = (double)p[(size_t)j * V + d] / (double)q[(size_t)j * V + d];
+        const double t = w[j] * ratio;
+        w[j + 1] = t >= 1.0 ? 1.0 : (t > 0.0 ? t : 0.0);
+    }
+    for (int j = 0; j < K; ++j) {
+        double s = 0.0;
+        for (int v = 0; v < V; ++v) {
+            const double e = w[j] * (double)p[(size_t)j * V + v] - (double)q[(size_t)j * V + v];
+            if (e > 0.0) s += e;
+        }
+        S[j] = s;
+    }
+    h[0] = 1.0;
+    for (int j = 1; j < K; ++j) h[j] = S[j] > 0.0 ? S[j] / (S[j] + (1.0 - w[j])) : 0.0;
+    if (K > 0) h[K] = w[K];
+}
+
+/* The float32 weight of column v of the distribution the token emitted at
+ * position n is drawn from (before the empty-residual fallback). */
+static float block_emit_weight(const float* q, const float* p, const double* w, int n, int K, int V, int v)
+{
+    if (n == K) return p[(size_t)K * V + v];
+    const double e = w[n] * (double)p[(size_t)n * V + v] - (double)q[(size_t)n * V + v];
+    return (float)(e > 0.0 ? e : 0.0);
+}
+
+/* The rule's quantities for inspection: w [B,K+1], S [B,K+1] (S[K] = 0),
+ * h [B,K+1] and, if resid is given, the float32 weights of every position's
+ * emission distribution [B,K+1,V] (position K: p_K). */
+int dspark_oracle_verify_block_weights(
+    const float* q, const float* p, const int32_t* draft, int B, int K, int V,
+    double* w, double* S, double* h, float* resid)
+{
+    if (B < 0 || K < 0 || V <= 0 || !q || !p || !draft || !w || !S || !h) return -1;
+    for (int b = 0; b < B; ++b) {
+        const float* qb = q + (size_t)b * K * V;
+        const float* pb = p + (size_t)b * (K + 1) * V;
+        double* wb = w + (size_t)b * (K + 1);
+        double* Sb = S + (size_t)b * (K + 1);
+        double* hb = h + (size_t)b * (K + 1);
+        block_weights(qb, pb, draft + (size_t)b * K, K, V, wb, Sb, hb);
+        Sb[K] = 0.0;
+        if (K == 0) hb[0] = 1.0;
+        if (resid)
+            for (int n = 0; n <= K; ++n)
+                for (int v = 0; v < V; ++v)
+                    resid[((size_t)b * (K + 1) + n) * V + v] = block_emit_weight(qb, pb, wb, n, K, V, v);
+    }
+    return 0;
+}
+
+int dspark_oracle_verify_block(
+    const float* q, const float* p, const int32_t* draft, const int64_t* seed, const int64_t* offset,
+    int B, int K, int V, double tie_eps, int max_cand,
+    int32_t* n_accepted, int32_t* out_tokens, double* tau_margin,
+    double* margin, int32_t* ncand, int32_t* cand)
+{
+    if (B < 0 || K < 0 || V <= 0 || K > 255) return -1;
+    if (!q || !p || !draft || !seed || !offset || !n_accepted || !out_tokens) return -1;
+    if (cand && max_cand <= 0) return -1;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int b = 0; b < B; ++b) {
+        double w[256], S[256], h[256];
+        const float* qb = q + (size_t)b * K * V;
+        const float* pb = p + (size_t)b * (K + 1) * V;
+        const uint64_t sd = (uint64_t)seed[b], off = (uint64_t)offset[b];
+        block_weights(qb, pb, draft + (size_t)b * K, K, V, w, S, h);
+        int n = 0;
+        double tm = INFINITY;
+        for (int j = 1; j <= K; ++j) {
+            const double eta = (double)dspark_oracle_verify_uniform(sd, off, (uint32_t)(j - 1));
+            if (eta < h[j]) n = j;
+            if (fabs(eta - h[j]) < tm) tm = fabs(eta - h[j]);
+        }
+        int use_p = 0;
+        if (n < K) {
+            int any = 0;
+            for (int v = 0; v < V && !any; ++v) any = block_emit_weight(qb, pb, w, n, K, V, v) > 0.0f;
+            use_p = !any;
+        }
+        int best = -1;
+        float zbest = 0.0f;
+        for (int v = 0; v < V; ++v) {
+            const float wt = use_p ? pb[(size_t)n * V + v] : block_emit_weight(qb, pb, w, n, K, V, v);
+            if (!(wt > 0.0f)) continue;
+            const float z = (float)log((double)wt) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            if (best < 0 || z > zbest) { best = v; zbest = z; }
+        }
+        double second = -INFINITY;
+        int n_near = 0;
+        for (int v = 0; v < V && best >= 0; ++v) {
+            const float wt = use_p ? pb[(size_t)n * V + v] : block_emit_weight(qb, pb, w, n, K, V, v);
+            if (!(wt > 0.0f)) continue;
+            const float z = (float)log((double)wt) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            if (v != best && (double)z > second) second = (double)z;
+            if ((double)z >= (double)zbest - tie_eps) {
+                if (cand && n_near < max_cand) cand[(size_t)b * max_cand + n_near] = v;
+                ++n_near;
+            }
+        }
+        n_accepted[b] = n;
+        int32_t* out = out_tokens + (size_t)b * (K + 1);
+        for (int i = 0; i < n; ++i) out[i] = clamp_tok(draft[(size_t)b * K + i], V);
+        out[n] = best < 0 ? 0 : best;
+        for (int i = n + 1; i <= K; ++i) out[i] = -1;
+        if (tau_margin) tau_margin[b] = tm;
+        if (margin) margin[b] = best < 0 ? INFINITY : (double)zbest - second;
+        if (ncand) ncand[b] = n_near;
+    }
+    return 0;
+}
