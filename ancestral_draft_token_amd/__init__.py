@@ -28,7 +28,8 @@ DSPARK_ERR_HIP = -4
 
 EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_launch_plan",
-            "dspark_status_string", "dspark_verify_workspace_bytes", "dspark_verify_standard")
+            "dspark_status_string", "dspark_verify_workspace_bytes", "dspark_verify_standard",
+            "dspark_verify_block_workspace_bytes", "dspark_verify_block")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
                 3: "resident_clear", 4: "markov_bias_gumbel_argmax"}
@@ -74,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_verify_workspace_bytes.restype = Z
     lib.dspark_verify_standard.argtypes = [P, P, P, P, P, I, I, I, P, P, P, Z, P]
     lib.dspark_verify_standard.restype = I
+    lib.dspark_verify_block_workspace_bytes.argtypes = [I, I, I]
+    lib.dspark_verify_block_workspace_bytes.restype = Z
+    lib.dspark_verify_block.argtypes = [P, P, P, P, P, I, I, I, P, P, P, Z, P]
+    lib.dspark_verify_block.restype = I
     _lib = lib
     return lib
 
@@ -166,4 +171,22 @@ def dspark_verify_standard(draft_tokens, draft_probs, target_probs, seed, offset
                                     _ptr(workspace), int(workspace_bytes), _stream_ptr(stream))
     if check and rc != DSPARK_OK:
         raise DSparkError(rc, "dspark_verify_standard")
+    return rc
+
+
+def dspark_verify_block_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(load_library().dspark_verify_block_workspace_bytes(B, K, V))
+
+
+def dspark_verify_block(draft_tokens, draft_probs, target_probs, seed, offset, B: int, K: int, V: int,
+                        n_accepted, out_tokens, workspace, workspace_bytes: int, stream=None,
+                        check: bool = True) -> int:
+    """Enqueue block verification; arguments as in ``include/dspark.h`` (the same
+    as ``dspark_verify_standard``)."""
+    lib = load_library()
+    rc = lib.dspark_verify_block(_ptr(draft_tokens), _ptr(draft_probs), _ptr(target_probs), _ptr(seed),
+                                 _ptr(offset), int(B), int(K), int(V), _ptr(n_accepted), _ptr(out_tokens),
+                                 _ptr(workspace), int(workspace_bytes), _stream_ptr(stream))
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_verify_block")
     return rc

@@ -2159,6 +2159,182 @@ __global__ __launch_bounds__(64) void verify_finish(VerArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Block verification of a draft block ("brb-nv/TensorRT-LLM pull 21",
+// section "2. Golden sampling semantics": rejection_sample_method block;
+// Sun, Mendlovic, Leviathan, Aharoni, Beirami, Ro and Suresh, "Block
+// Verification Accelerates Speculative Decoding", 2024). With prefix weights
+// w_0 = 1, w_{j+1} = min(1, w_j p_j(d_j) / q_j(d_j)), residual masses
+// S_j = sum_v max(w_j p_j(v) - q_j(v), 0) and thresholds
+// h_j = S_j / (S_j + 1 - w_j) (j < K), h_K = w_K, the row keeps the longest
+// prefix d_0 .. d_{n-1} whose test eta_n < h_n passes (n = 0 if none) and
+// emits a draw from max(w_n p_n - q_n, 0), or from p_K when n = K. The
+// precision of each step (weights, masses and thresholds in double, the
+// draw's weights rounded to float32) and the Philox counters are stated in
+// include/dspark.h.
+//
+// Every S_j is needed before n is known, so the whole of p_0..p_K and
+// q_0..q_{K-1} is read once: vblock_partials, one block per (chunk, row),
+// streams each position of its chunk and leaves the chunk's partial S_j and
+// the best Gumbel-max key of each position's emission distribution (so the
+// draw needs no second pass). vblock_finish, one wave per row, sums the
+// partials in a fixed order, finds n and merges the keys of position n.
+// ---------------------------------------------------------------------------
+struct VbArgs {
+  const int32_t* draft;    // [B,K]
+  const float* q;          // [B,K,V]
+  const float* p;          // [B,K+1,V]
+  const int64_t* seed;
+  const int64_t* offset;
+  double* part_s;          // [B][n_chunks][K]: partial residual masses (index 0 unused)
+  uint64_t* part_k;        // [B][n_chunks][K+1]: best key of each position's emission
+  int32_t* n_accepted;     // [B]
+  int32_t* out_tokens;     // [B,K+1]
+  int B, K, V, n_chunks;
+};
+
+// Prefix weights w_0 .. w_K of row b into s_w (all threads of the block
+// take part; s_w is ready after the call).
+__device__ __forceinline__ void vblock_weights(const VbArgs& a, int b, double* s_w, double* s_r) {
+  for (int j = threadIdx.x; j < a.K; j += blockDim.x) {
+    const int d = clamp_token(a.draft[(size_t)b * a.K + j], a.V);
+    const double pv = (double)a.p[((size_t)b * (a.K + 1) + j) * a.V + d];
+    const double qv = (double)a.q[((size_t)b * a.K + j) * a.V + d];
+    s_r[j] = pv / qv;   // IEEE double division
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double w = 1.0;
+    s_w[0] = w;
+    for (int j = 0; j < a.K; ++j) {
+      const double t = __dmul_rn(w, s_r[j]);
+      w = t >= 1.0 ? 1.0 : (t > 0.0 ? t : 0.0);
+      s_w[j + 1] = w;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = __dadd_rn(x, __shfl_xor(x, m));
+  return x;
+}
+
+template <int kIt>
+__global__ __launch_bounds__(kThreads) void vblock_partials(VbArgs a) {
+  __shared__ double s_w[kMaxK + 1], s_r[kMaxK];
+  __shared__ uint64_t s_k[kWaves];
+  __shared__ double s_s[kWaves];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  vblock_weights(a, b, s_w, s_r);
+  const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
+  const int c0 = c * (kIt * kVerColsMin) + 4 * t;
+  const size_t slot = (size_t)b * a.n_chunks + c;
+  for (int j = 0; j <= a.K; ++j) {
+    const bool bonus = j == a.K;
+    const float* pj = a.p + ((size_t)b * (a.K + 1) + j) * a.V;
+    const float* qj = a.q + ((size_t)b * a.K + (bonus ? 0 : j)) * a.V;
+    float4 pv[kIt], qv[kIt];
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = c0 + i * kVerColsMin;
+      pv[i] = v < a.V ? *reinterpret_cast<const float4*>(pj + v) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      qv[i] = (!bonus && v < a.V) ? *reinterpret_cast<const float4*>(qj + v) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    const double wj = s_w[j];
+    double sj = 0.0;
+    uint64_t kw = 0;
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = c0 + i * kVerColsMin;
+      if (v >= a.V) break;
+      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)j);
+      const float pe[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+      const float qe[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
+      const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float wt = pe[e];
+        if (!bonus) {
+          double r = __dsub_rn(__dmul_rn(wj, (double)pe[e]), (double)qe[e]);
+          r = r > 0.0 ? r : 0.0;
+          sj = __dadd_rn(sj, r);
+          wt = __double2float_rn(r);
+        }
+        if (wt > 0.0f)
+          kw = umax64(kw, score_key(__fsub_rn(__builtin_amdgcn_logf(wt), gumbel_log2(xe[e])), (uint32_t)(v + e)));
+      }
+    }
+    kw = wave_max_u64(kw);
+    sj = wave_sum_f64(sj);
+    if (lane == 0) {
+      s_k[wv] = kw;
+      s_s[wv] = sj;
+    }
+    __syncthreads();
+    if (t == 0) {
+      uint64_t m = s_k[0];
+      double sum = s_s[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        m = umax64(m, s_k[w]);
+        sum = __dadd_rn(sum, s_s[w]);
+      }
+      a.part_k[slot * (a.K + 1) + j] = m;
+      if (!bonus) a.part_s[slot * a.K + j] = sum;
+    }
+    __syncthreads();   // s_k and s_s are reused by the next position
+  }
+}
+
+__global__ __launch_bounds__(64) void vblock_finish(VbArgs a) {
+  __shared__ double s_w[kMaxK + 1], s_r[kMaxK];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  vblock_weights(a, b, s_w, s_r);
+  const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
+  const size_t row = (size_t)b * a.n_chunks;
+  int n = 0;
+  for (int j = 1; j <= a.K; ++j) {
+    double h;
+    if (j < a.K) {
+      double s = 0.0;
+      for (int c = lane; c < a.n_chunks; c += 64) s = __dadd_rn(s, a.part_s[(row + c) * a.K + j]);
+      s = wave_sum_f64(s);
+      h = s > 0.0 ? s / __dadd_rn(s, __dsub_rn(1.0, s_w[j])) : 0.0;
+    } else {
+      h = s_w[a.K];
+    }
+    const uint32_t x = verify_philox(seed, off, 0xFFFFFFFFu, 256u + (uint32_t)(j - 1)).x;
+    const float eta = __fmul_rn(__fadd_rn((float)(x >> 9), 0.5f), 0x1p-23f);   // exact
+    if ((double)eta < h) n = j;
+  }
+  uint64_t key = 0;
+  for (int c = lane; c < a.n_chunks; c += 64) key = umax64(key, a.part_k[(row + c) * (a.K + 1) + n]);
+  key = wave_max_u64(key);
+  if (key == 0 && n < a.K) {
+    // an empty residual: the draw falls back to p_n, scored here by this one
+    // wave (slow, never on the common path)
+    const float* pn = a.p + ((size_t)b * (a.K + 1) + n) * a.V;
+    for (int v = 4 * lane; v < a.V; v += 4 * 64) {
+      const float4 pv = *reinterpret_cast<const float4*>(pn + v);
+      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)n);
+      const float pe[4] = {pv.x, pv.y, pv.z, pv.w};
+      const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (pe[e] > 0.0f)
+          key = umax64(key, score_key(__fsub_rn(__builtin_amdgcn_logf(pe[e]), gumbel_log2(xe[e])), (uint32_t)(v + e)));
+    }
+    key = wave_max_u64(key);
+  }
+  const int tok = key ? clamp_token((int)key_token(key), a.V) : 0;
+  int32_t* out = a.out_tokens + (size_t)b * (a.K + 1);
+  for (int i = lane; i <= a.K; i += 64)
+    out[i] = i < n ? clamp_token(a.draft[(size_t)b * a.K + i], a.V) : (i == n ? tok : -1);
+  if (lane == 0) a.n_accepted[b] = n;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Workspace {
@@ -2517,6 +2693,52 @@ int verify_standard_impl(const int32_t* draft, const float* q, const float* p, c
   return DSPARK_OK;
 }
 
+// 1024-column units per vblock_partials block: 2 once that still gives
+// ~8192 blocks, else 1 (each block streams K+1 positions, and more columns
+// per thread cost occupancy: 52 registers at 1 unit, 82 at 2, 142 at 4).
+inline int vblock_iters(int B, int V) {
+  const long long units = (long long)B * ((V + kVerColsMin - 1) / kVerColsMin);
+  return units >= 2 * 8192 ? 2 : 1;
+}
+inline int vblock_chunks(int B, int V) {
+  const int cols = vblock_iters(B, V) * kVerColsMin;
+  return (V + cols - 1) / cols;
+}
+inline size_t vblock_part_s_bytes(int B, int K, int V) {
+  return align_up((size_t)B * vblock_chunks(B, V) * K * sizeof(double), 256);
+}
+inline size_t vblock_workspace(int B, int K, int V) {
+  return vblock_part_s_bytes(B, K, V) + align_up((size_t)B * vblock_chunks(B, V) * (K + 1) * sizeof(uint64_t), 256);
+}
+
+int verify_block_impl(const int32_t* draft, const float* q, const float* p, const int64_t* seed,
+                      const int64_t* offset, int B, int K, int V, int32_t* n_accepted, int32_t* out_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  int rc = verify_check(B, K, V);
+  if (rc != DSPARK_OK) return rc;
+  if (B == 0) return DSPARK_OK;
+  if ((K > 0 && (!draft || !q)) || !p || !seed || !offset || !n_accepted || !out_tokens) return DSPARK_ERR_ARG;
+  if ((K > 0 && !aligned16(q)) || !aligned16(p)) return DSPARK_ERR_ARG;
+  if (!workspace || workspace_bytes < vblock_workspace(B, K, V) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return DSPARK_ERR_WORKSPACE;
+  VbArgs a;
+  a.draft = draft; a.q = q; a.p = p; a.seed = seed; a.offset = offset;
+  a.part_s = static_cast<double*>(workspace);
+  a.part_k = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + vblock_part_s_bytes(B, K, V));
+  a.n_accepted = n_accepted; a.out_tokens = out_tokens;
+  a.B = B; a.K = K; a.V = V; a.n_chunks = vblock_chunks(B, V);
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const dim3 grid(a.n_chunks, B);
+  if (vblock_iters(B, V) == 2)
+    hipLaunchKernelGGL(vblock_partials<2>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(vblock_partials<1>, grid, dim3(kThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
+  hipLaunchKernelGGL(vblock_finish, dim3(B), dim3(64), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
 }  // namespace dspark
 
 extern "C" {
@@ -2544,6 +2766,9 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&verify_partials<4>),
       reinterpret_cast<const void*>(&verify_partials<8>),
       reinterpret_cast<const void*>(&verify_finish),
+      reinterpret_cast<const void*>(&vblock_partials<1>),
+      reinterpret_cast<const void*>(&vblock_partials<2>),
+      reinterpret_cast<const void*>(&vblock_finish),
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false>),
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false>),
       reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true>),
@@ -2570,6 +2795,18 @@ int dspark_verify_standard(const int32_t* draft_tokens, const float* draft_probs
                            void* stream) {
   return dspark::verify_standard_impl(draft_tokens, draft_probs, target_probs, seed, offset, B, K, V, n_accepted,
                                       out_tokens, workspace, workspace_bytes, stream);
+}
+
+size_t dspark_verify_block_workspace_bytes(int B, int K, int V) {
+  if (dspark::verify_check(B, K, V) != DSPARK_OK) return 0;
+  return dspark::vblock_workspace(B, K, V);
+}
+
+int dspark_verify_block(const int32_t* draft_tokens, const float* draft_probs, const float* target_probs,
+                        const int64_t* seed, const int64_t* offset, int B, int K, int V, int32_t* n_accepted,
+                        int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return dspark::verify_block_impl(draft_tokens, draft_probs, target_probs, seed, offset, B, K, V, n_accepted,
+                                   out_tokens, workspace, workspace_bytes, stream);
 }
 
 int dspark_draft_block(const void* base_logits, int base_dtype, const uint16_t* E, const uint16_t* W,

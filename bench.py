@@ -117,17 +117,20 @@ class Bench:
 
 
 def measure_verify(w, reps=10, mall="cold"):
-    """Standard token-level verification after one draft block of ``w``: the
-    block's own tokens and proposals against targets p_k = 0.7 q_k + 0.3
-    softmax(noise) (p_K = softmax(noise)), synthetic. Mean us per call over
-    ``reps`` calls (two launches each, events on the launch stream, the MALL
-    flushed before each); algorithmic bytes from the outcome: per row the
-    distribution the emitted token is drawn from is read once (p_j and q_j
-    after a rejection, p_K after all K accepted), plus the 2 (n + 1) probes of
-    the acceptance tests and the K + 1 tokens written."""
+    """Both verification rules after one draft block of ``w``: the block's own
+    tokens and proposals against targets p_k = 0.7 q_k + 0.3 softmax(noise)
+    (p_K = softmax(noise)), synthetic. Mean us per call over ``reps`` calls
+    (two launches each, events on the launch stream, the MALL flushed before
+    each). Algorithmic bytes per row:
+    - standard: the distribution the emitted token is drawn from, read once
+      (p_j and q_j after a rejection, p_K after all K accepted), plus the
+      2 (n + 1) probes of the acceptance tests and the K + 1 tokens written;
+    - block: every p_0..p_K and q_0..q_{K-1} read once (every residual mass is
+      needed before the stop is known), plus the 2 K probes and the tokens."""
     import numpy as np
     import torch
-    from ancestral_draft_token_amd import dspark_verify_standard, dspark_verify_workspace_bytes
+    from ancestral_draft_token_amd import (dspark_verify_block, dspark_verify_block_workspace_bytes,
+                                           dspark_verify_standard, dspark_verify_workspace_bytes)
     from ancestral_draft_token_amd.device import DeviceProblem
     prob = DeviceProblem(w)
     prob.enqueue()
@@ -138,36 +141,43 @@ def measure_verify(w, reps=10, mall="cold"):
     p = torch.softmax(torch.randn((B, K + 1, V), device=dev, generator=g) * 2.0, dim=-1)
     p[:, :K] = 0.7 * prob.q + 0.3 * p[:, :K]
     p = p.contiguous()
-    n = torch.empty(B, dtype=torch.int32, device=dev)
-    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    wb = dspark_verify_workspace_bytes(B, K, V)
-    ws = torch.empty(wb, dtype=torch.uint8, device=dev)
     flush_buf = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     flush_out = torch.empty((), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        for i in range(reps + 2):
-            if mall == "cold":
-                torch.amax(flush_buf, dim=0, out=flush_out)
-            starts[i].record(stream)
-            dspark_verify_standard(prob.tokens, prob.q, p, prob.seed, prob.offset, B, K, V, n, out, ws, wb,
-                                   stream=stream)
-            ends[i].record(stream)
-    torch.cuda.synchronize()
-    us = [s_.elapsed_time(e) * 1e3 for s_, e in zip(starts[2:], ends[2:])]
-    acc = n.cpu().numpy().astype(np.int64)
-    row_bytes = np.where(acc < K, 8 * V, 4 * V) + 8 * (np.minimum(acc, K - 1) + 1 if K else 0) + 4 * (K + 1)
-    algo = int(row_bytes.sum())
-    mean_us = statistics.mean(us)
+    targets = "p_k = 0.7 q_k + 0.3 softmax(2 N(0,1)), p_K = softmax(2 N(0,1)), synthetic"
+    res = {}
+    for rule, fn, wsb in (("standard", dspark_verify_standard, dspark_verify_workspace_bytes),
+                          ("block", dspark_verify_block, dspark_verify_block_workspace_bytes)):
+        n = torch.empty(B, dtype=torch.int32, device=dev)
+        out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        wb = wsb(B, K, V)
+        ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for i in range(reps + 2):
+                if mall == "cold":
+                    torch.amax(flush_buf, dim=0, out=flush_out)
+                starts[i].record(stream)
+                fn(prob.tokens, prob.q, p, prob.seed, prob.offset, B, K, V, n, out, ws, wb, stream=stream)
+                ends[i].record(stream)
+        torch.cuda.synchronize()
+        us = [s_.elapsed_time(e) * 1e3 for s_, e in zip(starts[2:], ends[2:])]
+        acc = n.cpu().numpy().astype(np.int64)
+        if rule == "standard":
+            row_bytes = np.where(acc < K, 8 * V, 4 * V) + 8 * (np.minimum(acc, K - 1) + 1 if K else 0) + 4 * (K + 1)
+        else:
+            row_bytes = np.full(B, 8 * K * V + 4 * V + 8 * K + 4 * (K + 1), dtype=np.int64)
+        algo = int(row_bytes.sum())
+        mean_us = statistics.mean(us)
+        res[rule] = {"workload": w.name, "us": round(mean_us, 2), "accepted_mean": round(float(acc.mean()), 3),
+                     "bytes": algo, "achieved_gbs": round(algo / (mean_us * 1e-6) / 1e9, 1),
+                     "roofline_frac": round(algo / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "targets": targets}
     del prob, p, flush_buf
     torch.cuda.empty_cache()
-    return {"workload": w.name, "us": round(mean_us, 2), "accepted_mean": round(float(acc.mean()), 3),
-            "bytes": algo, "achieved_gbs": round(algo / (mean_us * 1e-6) / 1e9, 1),
-            "roofline_frac": round(algo / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "targets": "p_k = 0.7 q_k + 0.3 softmax(2 N(0,1)), p_K = softmax(2 N(0,1)), synthetic"}
+    return res
 
 
 def traffic_for(w, args):
@@ -317,7 +327,8 @@ def main():
                           "kernels_us": {k: round(v, 2) for k, v in ro["kernels_us"].items()}}
             del wo
         line["also"] = also
-    # the step after the block: standard token-level verification of its drafts
+    # the step after the block: verification of its drafts (standard token-level
+    # and block verification; each entry holds both)
     print(f"[bench] verify {w.name}", file=sys.stderr, flush=True)
     line["verify"] = {args.workload: measure_verify(w, mall=args.mall)}
     if not args.no_sweep:

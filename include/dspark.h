@@ -213,6 +213,44 @@ int dspark_verify_standard(
     int32_t* n_accepted, int32_t* out_tokens,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Block verification of a draft block ("brb-nv/TensorRT-LLM pull 21",
+ * section "2. Golden sampling semantics": rejection_sample_method block).
+ * The pages name the rule; this is the algorithm of Sun, Mendlovic,
+ * Leviathan, Aharoni, Beirami, Ro and Suresh, "Block Verification
+ * Accelerates Speculative Decoding" (2024), in the draft block's indices:
+ *   w_0 = 1, w_{j+1} = min(1, w_j p_j(d_j) / q_j(d_j));
+ *   S_j = sum_v max(w_j p_j(v) - q_j(v), 0);
+ *   h_j = S_j / (S_j + 1 - w_j) for 1 <= j < K, h_K = w_K;
+ *   n = the largest j in 1..K with eta_j < h_j, else 0;
+ *   out: d_0 .. d_{n-1}, then a token drawn from max(w_n p_n - q_n, 0)
+ *   normalised (n < K) or from p_K (n = K).
+ * Arguments, layouts and errors as for dspark_verify_standard; the
+ * workspace is at least dspark_verify_block_workspace_bytes(B,K,V) bytes,
+ * 8-byte aligned, and needs no initialisation.
+ *
+ * Conventions (the pages leave them open):
+ *   - w, S and h in double: the ratio is one IEEE double division of the
+ *     float32 inputs, w_{j+1} = w_j * ratio clamped to [0, 1] (q = 0 < p
+ *     gives 1, 0/0 gives 0); residual entries are the double product w_j p
+ *     minus q (no fused multiply-add), clamped at 0; h_j = 0 when S_j = 0.
+ *     Only the summation order of S_j is the implementation's own.
+ *   - eta_j is the token-level rule's u_{j-1} (same Philox word); the test
+ *     is eta_j < h_j in double.
+ *   - The emitted token is drawn as in the token-level rule (Gumbel words
+ *     of position n), from the weights float32(max(w_n p_n(v) - q_n(v), 0))
+ *     or p_K(v); an empty residual is replaced by p_n; a row with no
+ *     positive entry at all emits token 0.
+ *
+ * Two launches on `stream` (a pass over all K+1 target and K draft
+ * distributions per chunk and row, then a merge per row); graph-capturable;
+ * nothing is allocated. */
+size_t dspark_verify_block_workspace_bytes(int B, int K, int V);
+int dspark_verify_block(
+    const int32_t* draft_tokens, const float* draft_probs, const float* target_probs,
+    const int64_t* seed, const int64_t* offset, int B, int K, int V,
+    int32_t* n_accepted, int32_t* out_tokens,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* dspark_status_string(int status);
 

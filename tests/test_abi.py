@@ -127,12 +127,13 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
 
 # ---- standard verification: host checks (nothing is enqueued) ---------------
 
-def _verify(lib, **kw):
+def _verify(lib, rule="standard", **kw):
     a = dict(draft=16, q=16, p=16, seed=16, offset=16, B=2, K=3, V=64, n=16, out=16, ws=16,
              ws_bytes=1 << 20)
     a.update(kw)
-    return lib.dspark_verify_standard(a["draft"], a["q"], a["p"], a["seed"], a["offset"], a["B"], a["K"],
-                                      a["V"], a["n"], a["out"], a["ws"], a["ws_bytes"], None)
+    fn = lib.dspark_verify_standard if rule == "standard" else lib.dspark_verify_block
+    return fn(a["draft"], a["q"], a["p"], a["seed"], a["offset"], a["B"], a["K"], a["V"], a["n"], a["out"],
+              a["ws"], a["ws_bytes"], None)
 
 
 def test_verify_workspace_bytes(lib):
@@ -140,6 +141,14 @@ def test_verify_workspace_bytes(lib):
     assert adt.dspark_verify_workspace_bytes(1, 7, 8) > 0
     assert adt.dspark_verify_workspace_bytes(1, 256, 64) == 0      # K > 255
     assert adt.dspark_verify_workspace_bytes(1, 7, 66) == 0        # V % 4 != 0
+
+
+def test_verify_block_workspace_bytes(lib):
+    # 98 chunks of 2048 columns per row: a partial mass per position, a key per position and the bonus
+    assert adt.dspark_verify_block_workspace_bytes(88, 7, 200064) >= 88 * 98 * (7 + 8) * 8
+    assert adt.dspark_verify_block_workspace_bytes(1, 0, 8) > 0
+    assert adt.dspark_verify_block_workspace_bytes(1, 256, 64) == 0
+    assert adt.dspark_verify_block_workspace_bytes(1, 7, 66) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -153,9 +162,11 @@ def test_verify_workspace_bytes(lib):
     (dict(ws=None), adt.DSPARK_ERR_WORKSPACE),
     (dict(ws_bytes=8), adt.DSPARK_ERR_WORKSPACE),
 ])
-def test_verify_host_checks(lib, kw, status):
-    assert _verify(lib, **kw) == status
+@pytest.mark.parametrize("rule", ["standard", "block"])
+def test_verify_host_checks(lib, kw, status, rule):
+    assert _verify(lib, rule, **kw) == status
 
 
-def test_verify_empty_batch_enqueues_nothing(lib):
-    assert _verify(lib, B=0, draft=None, q=None, p=None) == adt.DSPARK_OK
+@pytest.mark.parametrize("rule", ["standard", "block"])
+def test_verify_empty_batch_enqueues_nothing(lib, rule):
+    assert _verify(lib, rule, B=0, draft=None, q=None, p=None) == adt.DSPARK_OK
