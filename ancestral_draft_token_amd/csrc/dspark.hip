@@ -2103,7 +2103,7 @@ __global__ __launch_bounds__(kThreads) void verify_partials(VerArgs a) {
   for (int i = 0; i < kIt; ++i) {
     const int v = c0 + i * kVerColsMin;
     if (v >= a.V) break;
-    const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)j);
+    const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u);
     const float pe[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
     const float qe[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
     const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
@@ -2140,7 +2140,7 @@ __global__ __launch_bounds__(64) void verify_finish(VerArgs a) {
     const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
     for (int v = 4 * lane; v < a.V; v += 4 * 64) {
       const float4 pv = *reinterpret_cast<const float4*>(pn + v);
-      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)n);
+      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u);
       const float pe[4] = {pv.x, pv.y, pv.z, pv.w};
       const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -2170,7 +2170,9 @@ __global__ __launch_bounds__(64) void verify_finish(VerArgs a) {
 // emits a draw from max(w_n p_n - q_n, 0), or from p_K when n = K. The
 // precision of each step (weights, masses and thresholds in double, the
 // draw's weights rounded to float32) and the Philox counters are stated in
-// include/dspark.h.
+// include/dspark.h. The emission noise is the same at every position, so its
+// Philox block and Gumbel logarithms are computed once per column, not once
+// per position.
 //
 // Every S_j is needed before n is known, so the whole of p_0..p_K and
 // q_0..q_{K-1} is read once: vblock_partials, one block per (chunk, row),
@@ -2190,6 +2192,7 @@ struct VbArgs {
   int32_t* n_accepted;     // [B]
   int32_t* out_tokens;     // [B,K+1]
   int B, K, V, n_chunks;
+  int pos_per_block;       // positions a vblock_partials block covers (all K+1 at large B)
 };
 
 // Prefix weights w_0 .. w_K of row b into s_w (all threads of the block
@@ -2220,70 +2223,96 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return x;
 }
 
+// One block per (chunk of kIt x 1024 columns, group of positions, row): at
+// large B one group holds all K+1 positions, so the Gumbel terms serve them
+// all; small batches split the positions over blocks to fill the GPU. No
+// barrier inside the position loop: each wave leaves its per-position
+// partials in LDS and the block merges them once at the end. Per lane the best draw of a position is
+// kept as (score, column) and compared strictly in ascending column order,
+// so equal scores keep the lowest column, as the 64-bit key order does.
 template <int kIt>
 __global__ __launch_bounds__(kThreads) void vblock_partials(VbArgs a) {
   __shared__ double s_w[kMaxK + 1], s_r[kMaxK];
-  __shared__ uint64_t s_k[kWaves];
-  __shared__ double s_s[kWaves];
-  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  vblock_weights(a, b, s_w, s_r);
-  const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
+  __shared__ uint64_t s_k[kMaxK + 1][kWaves];
+  __shared__ double s_s[kMaxK][kWaves];
+  const int c = blockIdx.x, b = blockIdx.z, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int j0 = blockIdx.y * a.pos_per_block;
+  const int j1 = min(j0 + a.pos_per_block, a.K + 1);
   const int c0 = c * (kIt * kVerColsMin) + 4 * t;
   const size_t slot = (size_t)b * a.n_chunks + c;
-  for (int j = 0; j <= a.K; ++j) {
+  fx4_t pv[kIt], qv[kIt];
+  auto load = [&](int j) {
     const bool bonus = j == a.K;
     const float* pj = a.p + ((size_t)b * (a.K + 1) + j) * a.V;
     const float* qj = a.q + ((size_t)b * a.K + (bonus ? 0 : j)) * a.V;
-    float4 pv[kIt], qv[kIt];
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       const int v = c0 + i * kVerColsMin;
-      pv[i] = v < a.V ? *reinterpret_cast<const float4*>(pj + v) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      qv[i] = (!bonus && v < a.V) ? *reinterpret_cast<const float4*>(qj + v) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      pv[i] = v < a.V ? __builtin_nontemporal_load(reinterpret_cast<const fx4_t*>(pj + v))
+                      : fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      qv[i] = (!bonus && v < a.V) ? __builtin_nontemporal_load(reinterpret_cast<const fx4_t*>(qj + v))
+                                  : fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  };
+  load(j0);   // in flight while the prefix weights and the Gumbel terms are made
+  vblock_weights(a, b, s_w, s_r);
+  const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
+  // the emission noise does not depend on the position: its Gumbel terms are
+  // computed once and serve every position of the block
+  float gl[kIt][4];
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+    const uint4 x = verify_philox(seed, off, (uint32_t)(c0 + i * kVerColsMin) >> 2, 512u);
+    gl[i][0] = gumbel_log2(x.x);
+    gl[i][1] = gumbel_log2(x.y);
+    gl[i][2] = gumbel_log2(x.z);
+    gl[i][3] = gumbel_log2(x.w);
+  }
+  for (int j = j0; j < j1; ++j) {
+    const bool bonus = j == a.K;
+    if (j > j0) load(j);
     const double wj = s_w[j];
     double sj = 0.0;
-    uint64_t kw = 0;
+    float zb = 0.0f;
+    int ib = -1;
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       const int v = c0 + i * kVerColsMin;
-      if (v >= a.V) break;
-      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)j);
       const float pe[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
       const float qe[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
-      const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float wt = pe[e];
         if (!bonus) {
-          double r = __dsub_rn(__dmul_rn(wj, (double)pe[e]), (double)qe[e]);
-          r = r > 0.0 ? r : 0.0;
+          const double r = __builtin_fmax(__dsub_rn(__dmul_rn(wj, (double)pe[e]), (double)qe[e]), 0.0);
           sj = __dadd_rn(sj, r);
           wt = __double2float_rn(r);
         }
-        if (wt > 0.0f)
-          kw = umax64(kw, score_key(__fsub_rn(__builtin_amdgcn_logf(wt), gumbel_log2(xe[e])), (uint32_t)(v + e)));
+        const float z = __fsub_rn(__builtin_amdgcn_logf(wt), gl[i][e]);
+        const bool take = wt > 0.0f && (ib < 0 || z > zb);
+        zb = take ? z : zb;
+        ib = take ? v + e : ib;
       }
     }
-    kw = wave_max_u64(kw);
+    const uint64_t kw = wave_max_u64(ib < 0 ? 0ull : score_key(zb, (uint32_t)ib));
     sj = wave_sum_f64(sj);
     if (lane == 0) {
-      s_k[wv] = kw;
-      s_s[wv] = sj;
+      s_k[j][wv] = kw;
+      if (!bonus) s_s[j][wv] = sj;
     }
-    __syncthreads();
-    if (t == 0) {
-      uint64_t m = s_k[0];
-      double sum = s_s[0];
+  }
+  __syncthreads();
+  for (int j = j0 + t; j < j1; j += kThreads) {
+    uint64_t m = s_k[j][0];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) {
-        m = umax64(m, s_k[w]);
-        sum = __dadd_rn(sum, s_s[w]);
-      }
-      a.part_k[slot * (a.K + 1) + j] = m;
-      if (!bonus) a.part_s[slot * a.K + j] = sum;
+    for (int w = 1; w < kWaves; ++w) m = umax64(m, s_k[j][w]);
+    a.part_k[slot * (a.K + 1) + j] = m;
+    if (j < a.K) {
+      double sum = s_s[j][0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) sum = __dadd_rn(sum, s_s[j][w]);
+      a.part_s[slot * a.K + j] = sum;
     }
-    __syncthreads();   // s_k and s_s are reused by the next position
   }
 }
 
@@ -2317,7 +2346,7 @@ __global__ __launch_bounds__(64) void vblock_finish(VbArgs a) {
     const float* pn = a.p + ((size_t)b * (a.K + 1) + n) * a.V;
     for (int v = 4 * lane; v < a.V; v += 4 * 64) {
       const float4 pv = *reinterpret_cast<const float4*>(pn + v);
-      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u + (uint32_t)n);
+      const uint4 x = verify_philox(seed, off, (uint32_t)v >> 2, 512u);
       const float pe[4] = {pv.x, pv.y, pv.z, pv.w};
       const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -2694,11 +2723,11 @@ int verify_standard_impl(const int32_t* draft, const float* q, const float* p, c
 }
 
 // 1024-column units per vblock_partials block: 2 once that still gives
-// ~8192 blocks, else 1 (each block streams K+1 positions, and more columns
-// per thread cost occupancy: 52 registers at 1 unit, 82 at 2, 142 at 4).
+// ~4096 blocks, else 1 (a block streams up to K+1 positions; at B=88,
+// V=200064: 185 us with 2 units against 193 with 1 and 189 with 4).
 inline int vblock_iters(int B, int V) {
   const long long units = (long long)B * ((V + kVerColsMin - 1) / kVerColsMin);
-  return units >= 2 * 8192 ? 2 : 1;
+  return units >= 2 * 4096 ? 2 : 1;
 }
 inline int vblock_chunks(int B, int V) {
   const int cols = vblock_iters(B, V) * kVerColsMin;
@@ -2727,8 +2756,13 @@ int verify_block_impl(const int32_t* draft, const float* q, const float* p, cons
   a.part_k = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + vblock_part_s_bytes(B, K, V));
   a.n_accepted = n_accepted; a.out_tokens = out_tokens;
   a.B = B; a.K = K; a.V = V; a.n_chunks = vblock_chunks(B, V);
+  // small batches split the positions over ~4096 blocks (B=1, V=200064: 196
+  // blocks of 8 positions would leave most of the GPU idle)
+  const long long cb = (long long)B * a.n_chunks;
+  const int groups = cb >= 2048 ? 1 : (int)std::min<long long>(K + 1, (4096 + cb - 1) / cb);
+  a.pos_per_block = (K + 1 + groups - 1) / groups;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const dim3 grid(a.n_chunks, B);
+  const dim3 grid(a.n_chunks, (K + 1 + a.pos_per_block - 1) / a.pos_per_block, B);
   if (vblock_iters(B, V) == 2)
     hipLaunchKernelGGL(vblock_partials<2>, grid, dim3(kThreads), 0, stream, a);
   else

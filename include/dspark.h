@@ -195,7 +195,9 @@ int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds);
  *     bonus) is the Gumbel-max draw over w_v = float32(p_j(v) - q_j(v)) (or
  *     p_K(v)) among v with w_v > 0: the lowest index of the largest
  *     ln w_v + g_v, g_v = -ln(-ln u) of output word (v & 3) of counter
- *     (v >> 2, 512 + j, lo32(offset), hi32(offset)). A residual with no
+ *     (v >> 2, 512, lo32(offset), hi32(offset)), the same at every position
+ *     (a row emits one drawn token; where is decided by the uniforms, another
+ *     stream). A residual with no
  *     positive entry (only through rounding) is replaced by p_j; a row with
  *     no positive entry at all emits token 0.
  *
@@ -236,8 +238,8 @@ int dspark_verify_standard(
  *     Only the summation order of S_j is the implementation's own.
  *   - eta_j is the token-level rule's u_{j-1} (same Philox word); the test
  *     is eta_j < h_j in double.
- *   - The emitted token is drawn as in the token-level rule (Gumbel words
- *     of position n), from the weights float32(max(w_n p_n(v) - q_n(v), 0))
+ *   - The emitted token is drawn as in the token-level rule (the same
+ *     Gumbel words), from the weights float32(max(w_n p_n(v) - q_n(v), 0))
  *     or p_K(v); an empty residual is replaced by p_n; a row with no
  *     positive entry at all emits token 0.
  *

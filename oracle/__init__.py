@@ -74,8 +74,7 @@ def _load():
         lib.dspark_oracle_draft_block.restype = ctypes.c_int
         lib.dspark_oracle_verify_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32]
         lib.dspark_oracle_verify_uniform.restype = ctypes.c_float
-        lib.dspark_oracle_verify_gumbel.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32,
-                                                    ctypes.c_uint32]
+        lib.dspark_oracle_verify_gumbel.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32]
         lib.dspark_oracle_verify_gumbel.restype = ctypes.c_float
         lib.dspark_oracle_verify_standard.argtypes = [
             P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
@@ -191,8 +190,8 @@ def verify_uniform(seed: int, offset: int, k: int) -> float:
     return float(_load().dspark_oracle_verify_uniform(seed & (2**64 - 1), offset & (2**64 - 1), k))
 
 
-def verify_gumbel(seed: int, offset: int, j: int, v: int) -> float:
-    return float(_load().dspark_oracle_verify_gumbel(seed & (2**64 - 1), offset & (2**64 - 1), j, v))
+def verify_gumbel(seed: int, offset: int, v: int) -> float:
+    return float(_load().dspark_oracle_verify_gumbel(seed & (2**64 - 1), offset & (2**64 - 1), v))
 
 
 def verify_standard(draft_tokens, q, p, seed, offset, tie_eps: float = TIE_EPS) -> VerifyResult:

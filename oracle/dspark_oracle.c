@@ -334,7 +334,10 @@ int dspark_oracle_max_threads(void)
  *    Gumbel-max draw over w_v = float32(p_j(v) - q_j(v)) where that is > 0
  *    (residual) or w_v = p_j(v) (bonus), among v with w_v > 0: the lowest
  *    index of the largest ln(w_v) + g_v, g_v = -ln(-ln u) of word (v & 3) of
- *    counter (v >> 2, 512 + j, lo32(offset), hi32(offset)). Scores are
+ *    counter (v >> 2, 512, lo32(offset), hi32(offset)). The counter does not
+ *    depend on j: a row emits exactly one drawn token, and which position it
+ *    is drawn at is decided by the acceptance uniforms (another stream), so
+ *    the positions can share one noise stream. Scores are
  *    rounded to float32 before the argmax, as the kernel decides in float32.
  *    A residual with no positive entry (possible only through rounding, as
  *    p = q then) is replaced by p_j.
@@ -355,10 +358,10 @@ float dspark_oracle_verify_uniform(uint64_t seed, uint64_t offset, uint32_t k)
     return (float)dspark_oracle_uniform(verify_word(seed, offset, 0xFFFFFFFFu, 256u + k, 0u));
 }
 
-/* Gumbel variate of column v for the token emitted at position j. */
-float dspark_oracle_verify_gumbel(uint64_t seed, uint64_t offset, uint32_t j, uint32_t v)
+/* Gumbel variate of column v for the emitted token (at any position). */
+float dspark_oracle_verify_gumbel(uint64_t seed, uint64_t offset, uint32_t v)
 {
-    return dspark_oracle_gumbel(verify_word(seed, offset, v >> 2, 512u + j, v));
+    return dspark_oracle_gumbel(verify_word(seed, offset, v >> 2, 512u, v));
 }
 
 int dspark_oracle_verify_standard(
@@ -400,7 +403,7 @@ int dspark_oracle_verify_standard(
         for (int v = 0; v < V; ++v) {
             const float w = use_p ? pj[v] : pj[v] - qj[v];
             if (!(w > 0.0f)) continue;
-            const float z = (float)log((double)w) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            const float z = (float)log((double)w) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)v);
             if (best < 0 || z > zbest) { best = v; zbest = z; }
         }
         double second = -INFINITY;
@@ -408,7 +411,7 @@ int dspark_oracle_verify_standard(
         for (int v = 0; v < V && best >= 0; ++v) {
             const float w = use_p ? pj[v] : pj[v] - qj[v];
             if (!(w > 0.0f)) continue;
-            const float z = (float)log((double)w) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            const float z = (float)log((double)w) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)v);
             if (v != best && (double)z > second) second = (double)z;
             if ((double)z >= (double)zbest - tie_eps) {
                 if (cand && n_near < max_cand) cand[(size_t)b * max_cand + n_near] = v;
@@ -461,9 +464,10 @@ int dspark_oracle_verify_standard(
  *  - eta_j is the acceptance uniform of draft d_{j-1}, the same word as the
  *    token-level rule's u_{j-1}; the test passes iff eta_j < h_j (the
  *    comparison in double).
- *  - The emitted token is drawn as in the token-level rule, from the weights
- *    float32(max(w_n p_n(v) - q_n(v), 0)) (or p_K(v)) with the Gumbel words
- *    of position n; an empty residual is replaced by p_n.
+ *  - The emitted token is drawn as in the token-level rule (the same
+ *    position-free Gumbel words), from the weights
+ *    float32(max(w_n p_n(v) - q_n(v), 0)) (or p_K(v)); an empty residual is
+ *    replaced by p_n.
  */
 
 static int clamp_tok(int d, int V)
@@ -566,7 +570,7 @@ int dspark_oracle_verify_block(
         for (int v = 0; v < V; ++v) {
             const float wt = use_p ? pb[(size_t)n * V + v] : block_emit_weight(qb, pb, w, n, K, V, v);
             if (!(wt > 0.0f)) continue;
-            const float z = (float)log((double)wt) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            const float z = (float)log((double)wt) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)v);
             if (best < 0 || z > zbest) { best = v; zbest = z; }
         }
         double second = -INFINITY;
@@ -574,7 +578,7 @@ int dspark_oracle_verify_block(
         for (int v = 0; v < V && best >= 0; ++v) {
             const float wt = use_p ? pb[(size_t)n * V + v] : block_emit_weight(qb, pb, w, n, K, V, v);
             if (!(wt > 0.0f)) continue;
-            const float z = (float)log((double)wt) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)n, (uint32_t)v);
+            const float z = (float)log((double)wt) + dspark_oracle_verify_gumbel(sd, off, (uint32_t)v);
             if (v != best && (double)z > second) second = (double)z;
             if ((double)z >= (double)zbest - tie_eps) {
                 if (cand && n_near < max_cand) cand[(size_t)b * max_cand + n_near] = v;
