@@ -29,7 +29,8 @@ DSPARK_ERR_HIP = -4
 EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_launch_plan",
             "dspark_status_string", "dspark_verify_workspace_bytes", "dspark_verify_standard",
-            "dspark_verify_block_workspace_bytes", "dspark_verify_block")
+            "dspark_verify_block_workspace_bytes", "dspark_verify_block",
+            "dspark_window_attention_workspace_bytes", "dspark_window_block_attention")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
                 3: "resident_clear", 4: "markov_bias_gumbel_argmax"}
@@ -79,6 +80,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_verify_block_workspace_bytes.restype = Z
     lib.dspark_verify_block.argtypes = [P, P, P, P, P, I, I, I, P, P, P, Z, P]
     lib.dspark_verify_block.restype = I
+    lib.dspark_window_attention_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.dspark_window_attention_workspace_bytes.restype = Z
+    lib.dspark_window_block_attention.argtypes = [P, P, P, P, I, I, I, I, I, I, I, ctypes.c_float, P, P, P, Z, P]
+    lib.dspark_window_block_attention.restype = I
     _lib = lib
     return lib
 
@@ -189,4 +194,22 @@ def dspark_verify_block(draft_tokens, draft_probs, target_probs, seed, offset, B
                                  _ptr(workspace), int(workspace_bytes), _stream_ptr(stream))
     if check and rc != DSPARK_OK:
         raise DSparkError(rc, "dspark_verify_block")
+    return rc
+
+
+def dspark_window_attention_workspace_bytes(B: int, K: int, Hq: int, Hkv: int, D: int, L: int, W: int) -> int:
+    return int(load_library().dspark_window_attention_workspace_bytes(B, K, Hq, Hkv, D, L, W))
+
+
+def dspark_window_block_attention(q, k_cache, v_cache, ctx_len, B: int, K: int, Hq: int, Hkv: int, D: int, L: int,
+                                  W: int, scale: float, out, lse, workspace, workspace_bytes: int, stream=None,
+                                  check: bool = True) -> int:
+    """Enqueue the drafter's non-causal windowed block attention; arguments as in
+    ``include/dspark.h``."""
+    lib = load_library()
+    rc = lib.dspark_window_block_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), int(B), int(K),
+                                           int(Hq), int(Hkv), int(D), int(L), int(W), float(scale), _ptr(out),
+                                           _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream_ptr(stream))
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_window_block_attention")
     return rc

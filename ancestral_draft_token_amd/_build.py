@@ -1,6 +1,8 @@
 """Build the HIP library in-tree for gfx950 (MI355X).
 
-``hipcc`` cross-compiles without a GPU. The library is one shared object,
+``hipcc`` cross-compiles without a GPU. The library is one shared object
+built from ``csrc/dspark.hip`` (the sampler and verification) and
+``csrc/window_attn.hip`` (the drafter's windowed block attention),
 ``ancestral_draft_token_amd/libdspark.so``, exporting the C ABI declared in
 ``include/dspark.h``.
 """
@@ -13,6 +15,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "dspark.hip")
+SOURCES = [SRC, os.path.join(PKG, "csrc", "window_attn.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspark.so")
 ARCH = "gfx950"
@@ -37,9 +40,9 @@ def hipcc() -> str:
 
 
 def build_library(out: str = LIB, extra_flags=()) -> str:
-    """Compile ``csrc/dspark.hip`` into ``out`` (always recompiles)."""
+    """Compile the sources under ``csrc/`` into ``out`` (always recompiles)."""
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", "-o", tmp, *SOURCES]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -1,0 +1,351 @@
+// window_attn.hip -- non-causal windowed block attention of a DSpark drafter
+// layer on gfx950 (MI355X).
+//
+// What it computes ("brb-nv/TensorRT-LLM pull 21", section "1. Non-causal
+// DSpark draft blocks on TRTLLM (default path)"; the modeling_dspark.py /
+// modeling_dflash.py note of the MiniMax-M3.1-Flash page): K draft-block
+// queries at positions P .. P+K-1 after a context of P tokens; query i
+// attends every existing key t (t < P + K) with |i - t| <= W - 1: the
+// context keys inside its window and every block position. GQA: 16 query
+// heads share one key/value head. Outputs o (float32) and the log-sum-exp
+// (natural log) of every (position, query head).
+//
+// The pages lower this as a causal window decode plus a log-sum-exp merge of
+// the later block keys, because their attention kernel only windows causally.
+// Here the two-sided window is computed directly: one pass over the key
+// range [max(0, P - W + 1), P + K), split over workgroups, each query
+// masking its own lower bound; the splits are then combined by the same
+// log-sum-exp merge.
+//
+// wa_partials: one 256-thread workgroup per (split, key/value head, row).
+// The key range is streamed in tiles of 64 keys through LDS (K as rows, V
+// transposed as dim rows), the next tile's global loads in flight while the
+// current one is used. Wave w owns draft positions w and w + 4; a position's
+// 16 heads are one MFMA tile. Scores are computed transposed,
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16: M = 16 keys, N = 16 heads, 4 steps
+// over D = 128), with the keys of each 32-key step assigned to the two score
+// tiles so that the accumulators land exactly in the B-operand layout of the
+// second product, O^T += V^T P^T (M = 16 dims x 8 tiles, N = 16 heads, 32 keys
+// per step): each lane holds keys 8 (lane / 16) .. + 7 of one head, with no
+// data movement between the two products. Online softmax in base 2 per head;
+// probabilities rounded to bf16 for the second product.
+// wa_combine: one 128-thread block per (head, position, row) merges the
+// splits: M = max m_s, L = sum l_s 2^(m_s - M), o = sum 2^(m_s - M) o_s / L,
+// lse = (M + log2 L) ln 2.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark_wa {
+
+constexpr int kD = 128;                      // head dimension
+constexpr int kG = 16;                       // query heads per key/value head
+constexpr int kKMax = 8;                     // draft positions: two per wave
+constexpr int kThreads = 256;
+constexpr int kTileKeys = 64;
+constexpr int kKRow = kD * 2 + 16;           // LDS bytes per key row (16-byte pad: conflict-free 16-lane reads)
+constexpr int kVRow = kTileKeys * 2 + 16;    // LDS bytes per transposed V row (one dim, 64 keys)
+constexpr int kLdsK = kTileKeys * kKRow;     // 17,408
+constexpr int kLdsV = kD * kVRow;            // 18,432
+constexpr int kTargetBlocks = 1024;          // workgroups a call aims for (splits are chosen from it)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  c, 0, 0, 0);
+}
+
+// float32 -> bf16, round to nearest even (inputs are finite and >= 0 here)
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+struct WaArgs {
+  const uint16_t* q;        // [B,K,Hq,D] bf16
+  const uint16_t* kc;       // [B,L,Hkv,D] bf16
+  const uint16_t* vc;       // [B,L,Hkv,D] bf16
+  const int32_t* ctx_len;   // [B]
+  float* part_o;            // [B][Hkv][S][K][16][D] unnormalised partial outputs
+  float* part_ml;           // [B][Hkv][S][K][16][2]: running max (base-2 units) and sum
+  float* out;               // [B,K,Hq,D]
+  float* lse;               // [B,K,Hq]
+  int B, K, Hkv, L, W, S, keys_per_split;
+  float scale_log2;         // scale * log2(e)
+};
+
+__device__ __forceinline__ int clamp_ctx(const WaArgs& a, int b) {
+  const int P = a.ctx_len[b];
+  return P < 0 ? 0 : (P > a.L - a.K ? a.L - a.K : P);
+}
+
+__global__ __launch_bounds__(kThreads) void wa_partials(WaArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsK + kLdsV];
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int Hq = a.Hkv * kG;
+  const int P = clamp_ctx(a, b);
+  const int lo0 = P - (a.W - 1) > 0 ? P - (a.W - 1) : 0;
+  const int hi = P + a.K;
+  const int k_begin = lo0 + s * a.keys_per_split;
+  const int k_end = k_begin + a.keys_per_split < hi ? k_begin + a.keys_per_split : hi;
+  const size_t rs = (size_t)a.Hkv * kD;                                 // elements between keys
+  const uint16_t* kb = a.kc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
+  const uint16_t* vb = a.vc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
+  const size_t pslot = (((size_t)b * a.Hkv + kvh) * a.S + s) * a.K;    // (b, kvh, s, position 0)
+
+  // the two draft positions of this wave and their query fragments:
+  // lane (c, g) holds head kvh*16 + c, dims 32 ds + 8 g .. + 7
+  int kq[2];
+  bool has[2];
+  u32x4_t qf[2][4];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    kq[qi] = wv + 4 * qi;
+    has[qi] = kq[qi] < a.K;
+    const uint16_t* qrow = a.q + (((size_t)b * a.K + (has[qi] ? kq[qi] : 0)) * Hq + kvh * kG + c) * kD;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qf[qi][ds] = has[qi] ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * ds + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  f32x4_t acc[2][8];
+  float m[2], l[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    m[qi] = -INFINITY;
+    l[qi] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[qi][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // staging: K rows as 16-byte pieces (16 lanes per 256-byte row), V as
+  // pairs of keys x 8 dims (written transposed, a dword per dim)
+  uint4 ks0, ks1, ks2, ks3, vs00, vs01, vs10, vs11;
+#define WA_LOAD_TILE(tb)                                                                              \
+  do {                                                                                                \
+    const int tb_ = (tb);                                                                             \
+    const int r0_ = tb_ + (t >> 4), r1_ = r0_ + 16, r2_ = r0_ + 32, r3_ = r0_ + 48;                   \
+    const int cw_ = (t & 15) * 8;                                                                     \
+    ks0 = *reinterpret_cast<const uint4*>(kb + (size_t)(r0_ < hi ? r0_ : hi - 1) * rs + cw_);         \
+    ks1 = *reinterpret_cast<const uint4*>(kb + (size_t)(r1_ < hi ? r1_ : hi - 1) * rs + cw_);         \
+    ks2 = *reinterpret_cast<const uint4*>(kb + (size_t)(r2_ < hi ? r2_ : hi - 1) * rs + cw_);         \
+    ks3 = *reinterpret_cast<const uint4*>(kb + (size_t)(r3_ < hi ? r3_ : hi - 1) * rs + cw_);         \
+    const int p0_ = tb_ + 2 * (t >> 4), p1_ = p0_ + 32;                                               \
+    vs00 = *reinterpret_cast<const uint4*>(vb + (size_t)(p0_ < hi ? p0_ : hi - 1) * rs + cw_);        \
+    vs01 = *reinterpret_cast<const uint4*>(vb + (size_t)(p0_ + 1 < hi ? p0_ + 1 : hi - 1) * rs + cw_); \
+    vs10 = *reinterpret_cast<const uint4*>(vb + (size_t)(p1_ < hi ? p1_ : hi - 1) * rs + cw_);        \
+    vs11 = *reinterpret_cast<const uint4*>(vb + (size_t)(p1_ + 1 < hi ? p1_ + 1 : hi - 1) * rs + cw_); \
+  } while (0)
+
+  const int n_tiles = k_begin < k_end ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  if (n_tiles > 0) WA_LOAD_TILE(k_begin);
+  for (int n = 0; n < n_tiles; ++n) {
+    const int tb = k_begin + n * kTileKeys;
+    __syncthreads();   // the previous tile is no longer read
+    {
+      // thread t: K rows t/16 + 16 r, bytes 16 (t % 16) ..; V key pairs t/16 and
+      // t/16 + 16, dims 8 (t % 16) .. + 7
+      unsigned char* kd = lds + (t >> 4) * kKRow + (t & 15) * 16;
+      *reinterpret_cast<uint4*>(kd) = ks0;
+      *reinterpret_cast<uint4*>(kd + 16 * kKRow) = ks1;
+      *reinterpret_cast<uint4*>(kd + 32 * kKRow) = ks2;
+      *reinterpret_cast<uint4*>(kd + 48 * kKRow) = ks3;
+      unsigned char* vd = lds + kLdsK + (t & 15) * 8 * kVRow + 4 * (t >> 4);
+      const uint32_t a0[4] = {vs00.x, vs00.y, vs00.z, vs00.w}, a1[4] = {vs01.x, vs01.y, vs01.z, vs01.w};
+      const uint32_t b0[4] = {vs10.x, vs10.y, vs10.z, vs10.w}, b1[4] = {vs11.x, vs11.y, vs11.z, vs11.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        *reinterpret_cast<uint32_t*>(vd + e * kVRow) =
+            ((a0[e >> 1] >> sh) & 0xFFFFu) | (((a1[e >> 1] >> sh) & 0xFFFFu) << 16);
+        *reinterpret_cast<uint32_t*>(vd + e * kVRow + 64) =
+            ((b0[e >> 1] >> sh) & 0xFFFFu) | (((b1[e >> 1] >> sh) & 0xFFFFu) << 16);
+      }
+    }
+    __syncthreads();
+    if (n + 1 < n_tiles) WA_LOAD_TILE(tb + kTileKeys);   // in flight while this tile is used
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // S^T tiles: tile tt, A row r = key 32 st + 8 (r / 4) + 4 tt + r % 4 of the tile
+      f32x4_t sc[2][2];
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) sc[qi][0] = sc[qi][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int krow = 32 * st + 8 * (c >> 2) + 4 * tt + (c & 3);
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(lds + krow * kKRow + (32 * ds + 8 * g) * 2);
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi)
+            if (has[qi]) sc[qi][tt] = mfma_bf16(af, qf[qi][ds], sc[qi][tt]);
+        }
+      }
+      // lane (c, g) now holds the scores of keys tb + 32 st + 8 g + j, j = 0..7, for head c
+      const int kt0 = tb + 32 * st + 8 * g;
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        if (!has[qi]) continue;
+        const int lo_k = P + kq[qi] - (a.W - 1);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kt = kt0 + j;
+          const float v = sc[qi][j >> 2][j & 3];
+          x[j] = (kt >= lo_k && kt < k_end) ? v * a.scale_log2 : -INFINITY;
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m[qi], mt);
+        if (mn == -INFINITY) continue;   // no key of this head so far (uniform over the head's lanes)
+        const float alpha = exp2f(m[qi] - mn);
+        float p[8], ps = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = exp2f(x[j] - mn);
+          ps += p[j];
+        }
+        l[qi] = l[qi] * alpha + ps;
+        m[qi] = mn;
+        const u32x4_t pb{bf16_rne(p[0]) | (bf16_rne(p[1]) << 16), bf16_rne(p[2]) | (bf16_rne(p[3]) << 16),
+                         bf16_rne(p[4]) | (bf16_rne(p[5]) << 16), bf16_rne(p[6]) | (bf16_rne(p[7]) << 16)};
+        // V^T fragments: dim 16 dt + c, keys 32 st + 8 g .. + 7 of the tile
+        const unsigned char* vrow = lds + kLdsK + c * kVRow + (32 * st + 8 * g) * 2;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vrow + 16 * dt * kVRow);
+          acc[qi][dt] *= alpha;
+          acc[qi][dt] = mfma_bf16(vf, pb, acc[qi][dt]);
+        }
+      }
+    }
+  }
+#undef WA_LOAD_TILE
+
+  // partials: lane (c, g) holds O^T dims 16 dt + 4 g .. + 3 of head c
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    if (!has[qi]) continue;
+    float lt = l[qi];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const size_t row = (pslot + kq[qi]) * kG + c;
+    float* po = a.part_o + row * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * g) = acc[qi][dt];
+    if (g == 0) {
+      a.part_ml[2 * row] = m[qi];
+      a.part_ml[2 * row + 1] = lt;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kD) void wa_combine(WaArgs a) {
+  const int h = blockIdx.x, k = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int kvh = h / kG, c = h % kG;
+  const int Hq = a.Hkv * kG;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) {
+    const size_t row = ((((size_t)b * a.Hkv + kvh) * a.S + s) * a.K + k) * kG + c;
+    M = fmaxf(M, a.part_ml[2 * row]);
+  }
+  float Ls = 0.0f, o = 0.0f;
+  for (int s = 0; s < a.S; ++s) {
+    const size_t row = ((((size_t)b * a.Hkv + kvh) * a.S + s) * a.K + k) * kG + c;
+    const float ms = a.part_ml[2 * row];
+    if (ms == -INFINITY) continue;   // no key of this head in the split
+    const float wgt = exp2f(ms - M);
+    Ls += a.part_ml[2 * row + 1] * wgt;
+    o += a.part_o[row * kD + d] * wgt;
+  }
+  const size_t orow = ((size_t)b * a.K + k) * Hq + h;
+  a.out[orow * kD + d] = o / Ls;
+  if (d == 0) a.lse[orow] = (M + log2f(Ls)) * 0.69314718055994531f;
+}
+
+struct Plan {
+  int S, keys_per_split;
+};
+
+inline int check(int B, int K, int Hq, int Hkv, int D, int L, int W) {
+  if (B < 0 || K <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || L <= 0 || W <= 0) return DSPARK_ERR_ARG;
+  if (D != kD || Hq != kG * Hkv || K > kKMax || K > W || L < K || B > 65535 || Hkv > 65535)
+    return DSPARK_ERR_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
+inline Plan plan(int B, int K, int Hkv, int W) {
+  const long long span = (long long)W - 1 + K;                 // keys of the widest range
+  const long long tiles = (span + kTileKeys - 1) / kTileKeys;
+  long long S = (kTargetBlocks + (long long)B * Hkv - 1) / ((long long)B * Hkv > 0 ? (long long)B * Hkv : 1);
+  if (S < 1) S = 1;
+  if (S > tiles) S = tiles;
+  const long long per = ((tiles + S - 1) / S) * kTileKeys;
+  Plan p;
+  p.keys_per_split = (int)per;
+  p.S = (int)((span + per - 1) / per);
+  return p;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline size_t workspace(int B, int K, int Hkv, int W, size_t* o_bytes) {
+  const Plan p = plan(B, K, Hkv, W);
+  const size_t rows = (size_t)B * Hkv * p.S * K * kG;
+  const size_t ob = align_up(rows * kD * sizeof(float), 256);
+  if (o_bytes) *o_bytes = ob;
+  return ob + align_up(rows * 2 * sizeof(float), 256);
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace dspark_wa
+
+extern "C" {
+
+size_t dspark_window_attention_workspace_bytes(int B, int K, int Hq, int Hkv, int D, int L, int W) {
+  using namespace dspark_wa;
+  if (check(B, K, Hq, Hkv, D, L, W) != DSPARK_OK) return 0;
+  return workspace(B, K, Hkv, W, nullptr);
+}
+
+int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* ctx_len, int B, int K, int Hq, int Hkv, int D, int L, int W,
+                                  float scale, float* out, float* lse, void* workspace_ptr,
+                                  size_t workspace_bytes, void* stream_ptr) {
+  using namespace dspark_wa;
+  int rc = check(B, K, Hq, Hkv, D, L, W);
+  if (rc != DSPARK_OK) return rc;
+  if (B == 0) return DSPARK_OK;
+  if (!q || !k_cache || !v_cache || !ctx_len || !out || !lse) return DSPARK_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DSPARK_ERR_ARG;
+  if (!(scale > 0.0f) || scale == INFINITY) return DSPARK_ERR_ARG;
+  size_t ob = 0;
+  const size_t need = workspace(B, K, Hkv, W, &ob);
+  if (!workspace_ptr || workspace_bytes < need || !aligned16(workspace_ptr)) return DSPARK_ERR_WORKSPACE;
+  const Plan p = plan(B, K, Hkv, W);
+  WaArgs a;
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.ctx_len = ctx_len;
+  a.part_o = static_cast<float*>(workspace_ptr);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace_ptr) + ob);
+  a.out = out; a.lse = lse;
+  a.B = B; a.K = K; a.Hkv = Hkv; a.L = L; a.W = W; a.S = p.S; a.keys_per_split = p.keys_per_split;
+  a.scale_log2 = scale * 1.44269504088896341f;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  hipLaunchKernelGGL(wa_partials, dim3(p.S, Hkv, B), dim3(kThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
+  hipLaunchKernelGGL(wa_combine, dim3(Hq, K, B), dim3(kD), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -253,6 +253,37 @@ int dspark_verify_block(
     int32_t* n_accepted, int32_t* out_tokens,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Non-causal windowed block attention of a DSpark drafter layer
+ * ("brb-nv/TensorRT-LLM pull 21", section "1. Non-causal DSpark draft blocks
+ * on TRTLLM (default path)"): K draft-block queries at positions
+ * P .. P+K-1 after a context of P tokens; query i attends every key t < P+K
+ * with |i - t| <= W - 1 (the context keys inside its window and every block
+ * position). GQA with 16 query heads per key/value head.
+ *
+ *   q          [B,K,Hq,D]   bf16 queries, 16-byte aligned
+ *   k_cache    [B,L,Hkv,D]  bf16 keys of positions 0 .. L-1 (the block's own
+ *   v_cache    [B,L,Hkv,D]  keys and values already at P .. P+K-1), 16-byte aligned
+ *   ctx_len    [B]          int32 P per row, device; clamped into [0, L-K]
+ *   D == 128, Hq == 16 Hkv, 1 <= K <= 8, K <= W, K <= L, B <= 65535
+ *   scale      the score scale (s = scale <q, k>), finite and > 0
+ *   out        [B,K,Hq,D]   float32 out: softmax-weighted values
+ *   lse        [B,K,Hq]     float32 out: ln sum_t exp(s_t)
+ *   workspace  at least dspark_window_attention_workspace_bytes(...) bytes,
+ *              16-byte aligned; contents need no initialisation
+ *
+ * Scores are bf16 products accumulated in float32, the softmax is float32
+ * in base 2, and the probabilities are rounded to bf16 for the product with
+ * V. Two launches on `stream` (the key range split over workgroups, then a
+ * log-sum-exp merge of the splits); graph-capturable; nothing is allocated.
+ * Errors: DSPARK_ERR_ARG (null or misaligned pointers, bad scale or sizes),
+ * DSPARK_ERR_UNSUPPORTED (sizes outside the limits), DSPARK_ERR_WORKSPACE,
+ * DSPARK_ERR_HIP. B == 0 enqueues nothing. */
+size_t dspark_window_attention_workspace_bytes(int B, int K, int Hq, int Hkv, int D, int L, int W);
+int dspark_window_block_attention(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* ctx_len,
+    int B, int K, int Hq, int Hkv, int D, int L, int W, float scale,
+    float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* dspark_status_string(int status);
 

@@ -170,3 +170,44 @@ def test_verify_host_checks(lib, kw, status, rule):
 @pytest.mark.parametrize("rule", ["standard", "block"])
 def test_verify_empty_batch_enqueues_nothing(lib, rule):
     assert _verify(lib, rule, B=0, draft=None, q=None, p=None) == adt.DSPARK_OK
+
+
+def _attn(lib, **kw):
+    a = dict(q=16, k=16, v=16, ctx=16, B=2, K=7, Hq=64, Hkv=4, D=128, L=9000, W=4096, scale=0.088, out=16,
+             lse=16, ws=16, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.dspark_window_block_attention(a["q"], a["k"], a["v"], a["ctx"], a["B"], a["K"], a["Hq"], a["Hkv"],
+                                             a["D"], a["L"], a["W"], a["scale"], a["out"], a["lse"], a["ws"],
+                                             a["ws_bytes"], None)
+
+
+def test_window_attention_workspace_bytes(lib):
+    # B=88, 4 key/value heads: 3 splits of 1408 keys; partial outputs and (max, sum) per split
+    n = adt.dspark_window_attention_workspace_bytes(88, 7, 64, 4, 128, 8199, 4096)
+    assert n >= 88 * 4 * 3 * 7 * 16 * (128 + 2) * 4
+    assert adt.dspark_window_attention_workspace_bytes(1, 7, 64, 4, 64, 8199, 4096) == 0    # D != 128
+    assert adt.dspark_window_attention_workspace_bytes(1, 7, 48, 4, 128, 8199, 4096) == 0   # Hq != 16 Hkv
+    assert adt.dspark_window_attention_workspace_bytes(1, 9, 64, 4, 128, 8199, 4096) == 0   # K > 8
+    assert adt.dspark_window_attention_workspace_bytes(1, 7, 64, 4, 128, 8199, 4) == 0      # K > W
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), adt.DSPARK_ERR_ARG),
+    (dict(ctx=None), adt.DSPARK_ERR_ARG),
+    (dict(lse=None), adt.DSPARK_ERR_ARG),
+    (dict(k=24), adt.DSPARK_ERR_ARG),                  # cache not 16-byte aligned
+    (dict(scale=0.0), adt.DSPARK_ERR_ARG),
+    (dict(D=64), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(Hq=32), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(K=9), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(L=3), adt.DSPARK_ERR_UNSUPPORTED),
+    (dict(K=0), adt.DSPARK_ERR_ARG),
+    (dict(ws=None), adt.DSPARK_ERR_WORKSPACE),
+    (dict(ws_bytes=8), adt.DSPARK_ERR_WORKSPACE),
+])
+def test_window_attention_host_checks(lib, kw, status):
+    assert _attn(lib, **kw) == status
+
+
+def test_window_attention_empty_batch_enqueues_nothing(lib):
+    assert _attn(lib, B=0, q=None, k=None, v=None, ctx=None, out=None, lse=None) == adt.DSPARK_OK

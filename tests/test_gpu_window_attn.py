@@ -1,0 +1,116 @@
+"""GPU non-causal windowed block attention vs the float64 oracle, through the C ABI.
+
+Tolerances follow from the arithmetic: scores are exact bf16 products summed
+in float32 (an error far below 2e-4 in the log-sum-exp at these sizes), and
+the probabilities are rounded to bf16 (relative error 2^-9) before the
+product with V while the normaliser keeps them in float32, so each output
+component is within 2^-9 * max |v| of the exact value; the test allows twice
+that. Cases: a window over part of the context, contexts around the window
+edge (P = 0, W-1, W, W+1), K = 3/7/8 and K = W, the pages' head layouts 16/1
+and 64/4, the 4096-token window, and the full-size benchmark shape (B=88,
+P=8192) on sampled (row, position, head) triples.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import window_attn as wa
+from ancestral_draft_token_amd import (dspark_init, dspark_window_attention_workspace_bytes,
+                                       dspark_window_block_attention)
+
+from gpu_util import require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _inputs(B, K, Hq, Hkv, L, seed):
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(seed)
+    q = torch.randn((B, K, Hq, D), device="cuda:0", generator=g).to(torch.bfloat16)
+    kc = torch.randn((B, L, Hkv, D), device="cuda:0", generator=g).to(torch.bfloat16)
+    vc = torch.randn((B, L, Hkv, D), device="cuda:0", generator=g).to(torch.bfloat16)
+    return q, kc, vc
+
+
+def run_gpu(q, kc, vc, P, W, scale):
+    import torch
+    dspark_init()
+    B, K, Hq, _ = q.shape
+    L, Hkv = kc.shape[1], kc.shape[2]
+    ctx = torch.tensor(P, dtype=torch.int32, device="cuda:0")
+    out = torch.empty((B, K, Hq, D), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, K, Hq), dtype=torch.float32, device="cuda:0")
+    wb = dspark_window_attention_workspace_bytes(B, K, Hq, Hkv, D, L, W)
+    ws = torch.empty(wb, dtype=torch.uint8, device="cuda:0")
+    say(f"window attention B={B} K={K} Hq={Hq} Hkv={Hkv} L={L} W={W} P={list(P)[:8]}")
+    dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, scale, out, lse, ws, wb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def _f64(t):
+    import torch
+    return t.to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def check(o, lse, o_ref, lse_ref, vmax):
+    err_o = np.abs(o - o_ref)
+    tol_o = 2.0 ** -8 * vmax + 1e-6
+    assert (err_o <= tol_o).all(), (float(err_o.max()), float(np.max(tol_o)))
+    err_l = np.abs(lse - lse_ref)
+    assert err_l.max() <= 2e-4, float(err_l.max())
+    say(f"attention parity ok: max |do| {err_o.max():.2e} (bound {np.min(tol_o):.2e}..), max |dlse| {err_l.max():.2e}")
+
+
+@pytest.mark.parametrize("B,K,Hq,Hkv,L,W,P", [
+    (2, 7, 16, 1, 200, 64, [100, 37]),
+    (7, 3, 64, 4, 400, 128, [0, 1, 126, 127, 128, 129, 300]),
+    (3, 8, 16, 1, 40, 8, [0, 7, 30]),
+    (2, 7, 64, 4, 9100, 4096, [4095, 9000]),
+    (1, 1, 16, 1, 5000, 4096, [4999]),
+])
+def test_window_attention_parity(B, K, Hq, Hkv, L, W, P):
+    q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=B * 100 + K + W)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(q, kc, vc, P, W, scale)
+    vq, vk, vv = _f64(q), _f64(kc), _f64(vc)
+    o_ref, lse_ref = wa.window_block_attention(vq, vk, vv, np.asarray(P), W, scale)
+    vmax = np.abs(vv).max(axis=(1, 3)).max()
+    check(o, lse, o_ref, lse_ref, vmax)
+
+
+def test_window_attention_full_size_sampled():
+    """The benchmark shape: B=88 rows, 64/4 heads, K=7, W=4096, P=8192 for every
+    row; 48 sampled (row, position, head) triples against the oracle."""
+    B, K, Hq, Hkv, W, P = 88, 7, 64, 4, 4096, 8192
+    L = P + K
+    q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=4242)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(q, kc, vc, [P] * B, W, scale)
+    rng = np.random.default_rng(9)
+    rows = [(int(rng.integers(B)), int(rng.integers(K)), int(rng.integers(Hq))) for _ in range(48)]
+    rows += [(0, 0, 0), (B - 1, K - 1, Hq - 1)]
+    qs = _f64(q)
+    lo = P - (W - 1)
+    for (b, k, h) in rows:
+        kvh = h // (Hq // Hkv)
+        kk = _f64(kc[b, lo:, kvh:kvh + 1])
+        vv = _f64(vc[b, lo:, kvh:kvh + 1])
+        # the same triple on a cache cut to the window: context P - lo
+        ro, rl = wa.window_block_attention_rows(qs[b:b + 1, :, h:h + 1], kk[None], vv[None], [P - lo], W, scale,
+                                                [(0, k, 0)])
+        assert np.abs(o[b, k, h] - ro[0]).max() <= 2.0 ** -8 * np.abs(vv).max() + 1e-6, (b, k, h)
+        assert abs(lse[b, k, h] - rl[0]) <= 2e-4, (b, k, h)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    say(f"full-size attention: {len(rows)} sampled triples ok")
