@@ -84,7 +84,10 @@ __device__ __forceinline__ int clamp_ctx(const WaArgs& a, int b) {
   return P < 0 ? 0 : (P > a.L - a.K ? a.L - a.K : P);
 }
 
-__global__ __launch_bounds__(kThreads) void wa_partials(WaArgs a) {
+// Transposed V rows are swizzled: key pair j of dim row d is stored at pair
+// j ^ (4 ((d / 16) % 8)), which keeps the transposing stores and the
+// fragment reads free of bank conflicts (rows of 144 bytes).
+__global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsK + kLdsV];
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -145,85 +148,103 @@ __global__ __launch_bounds__(kThreads) void wa_partials(WaArgs a) {
 
   const int n_tiles = k_begin < k_end ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
   if (n_tiles > 0) WA_LOAD_TILE(k_begin);
+  const int lo_max = P + a.K - 1 - (a.W - 1);   // the largest lower bound of a position
   for (int n = 0; n < n_tiles; ++n) {
     const int tb = k_begin + n * kTileKeys;
     __syncthreads();   // the previous tile is no longer read
     {
       // thread t: K rows t/16 + 16 r, bytes 16 (t % 16) ..; V key pairs t/16 and
-      // t/16 + 16, dims 8 (t % 16) .. + 7
+      // t/16 + 16, dims 8 (t % 16) .. + 7, into the swizzled transposed layout
       unsigned char* kd = lds + (t >> 4) * kKRow + (t & 15) * 16;
       *reinterpret_cast<uint4*>(kd) = ks0;
       *reinterpret_cast<uint4*>(kd + 16 * kKRow) = ks1;
       *reinterpret_cast<uint4*>(kd + 32 * kKRow) = ks2;
       *reinterpret_cast<uint4*>(kd + 48 * kKRow) = ks3;
-      unsigned char* vd = lds + kLdsK + (t & 15) * 8 * kVRow + 4 * (t >> 4);
+      const int sw = 4 * (((t & 15) >> 1) & 7);   // = vt_swizzle(8 (t % 16) + e) for every e < 8
+      const int s0 = 4 * ((t >> 4) ^ sw), s1 = 4 * (((t >> 4) + 16) ^ sw);
+      unsigned char* vd = lds + kLdsK + (t & 15) * 8 * kVRow;
       const uint32_t a0[4] = {vs00.x, vs00.y, vs00.z, vs00.w}, a1[4] = {vs01.x, vs01.y, vs01.z, vs01.w};
       const uint32_t b0[4] = {vs10.x, vs10.y, vs10.z, vs10.w}, b1[4] = {vs11.x, vs11.y, vs11.z, vs11.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sh = 16 * (e & 1);
-        *reinterpret_cast<uint32_t*>(vd + e * kVRow) =
+        *reinterpret_cast<uint32_t*>(vd + e * kVRow + s0) =
             ((a0[e >> 1] >> sh) & 0xFFFFu) | (((a1[e >> 1] >> sh) & 0xFFFFu) << 16);
-        *reinterpret_cast<uint32_t*>(vd + e * kVRow + 64) =
+        *reinterpret_cast<uint32_t*>(vd + e * kVRow + s1) =
             ((b0[e >> 1] >> sh) & 0xFFFFu) | (((b1[e >> 1] >> sh) & 0xFFFFu) << 16);
       }
     }
     __syncthreads();
     if (n + 1 < n_tiles) WA_LOAD_TILE(tb + kTileKeys);   // in flight while this tile is used
+
+    // scores of the whole tile: sc[qi][2 st + tt]; score tile (st, tt) has A
+    // row r = key 32 st + 8 (r / 4) + 4 tt + r % 4, so lane (c, g) ends up with
+    // keys 32 st + 8 g + 4 tt + i of head c
+    f32x4_t sc[2][4];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      // S^T tiles: tile tt, A row r = key 32 st + 8 (r / 4) + 4 tt + r % 4 of the tile
-      f32x4_t sc[2][2];
+    for (int qi = 0; qi < 2; ++qi)
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) sc[qi][0] = sc[qi][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int u = 0; u < 4; ++u) sc[qi][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int krow = 32 * st + 8 * (c >> 2) + 4 * tt + (c & 3);
+    for (int u = 0; u < 4; ++u) {
+      const int krow = 32 * (u >> 1) + 8 * (c >> 2) + 4 * (u & 1) + (c & 3);
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(lds + krow * kKRow + (32 * ds + 8 * g) * 2);
+      for (int ds = 0; ds < 4; ++ds) {
+        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(lds + krow * kKRow + (32 * ds + 8 * g) * 2);
 #pragma unroll
-          for (int qi = 0; qi < 2; ++qi)
-            if (has[qi]) sc[qi][tt] = mfma_bf16(af, qf[qi][ds], sc[qi][tt]);
+        for (int qi = 0; qi < 2; ++qi)
+          if (has[qi]) sc[qi][u] = mfma_bf16(af, qf[qi][ds], sc[qi][u]);
+      }
+    }
+    // only the tiles at a split's ends or below a position's window start mask
+    const bool edge = tb < lo_max || tb + kTileKeys > k_end;
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      if (!has[qi]) continue;
+      // x[8 st + j]: key tb + 32 st + 8 g + j (base-2 scaled score)
+      float x[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = sc[qi][2 * (j >> 3) + ((j >> 2) & 1)][j & 3] * a.scale_log2;
+      if (edge) {
+        const int lo_k = P + kq[qi] - (a.W - 1);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kt = tb + 32 * (j >> 3) + 8 * g + (j & 7);
+          if (!(kt >= lo_k && kt < k_end)) x[j] = -INFINITY;
         }
       }
-      // lane (c, g) now holds the scores of keys tb + 32 st + 8 g + j, j = 0..7, for head c
-      const int kt0 = tb + 32 * st + 8 * g;
+      float mt = x[0];
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) {
-        if (!has[qi]) continue;
-        const int lo_k = P + kq[qi] - (a.W - 1);
-        float x[8];
+      for (int j = 1; j < 16; ++j) mt = fmaxf(mt, x[j]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (mt == -INFINITY && m[qi] == -INFINITY) continue;   // no key of this position yet (uniform)
+      if (mt > m[qi]) {
+        // the running maximum grows: rescale (skipped once it has settled)
+        const float alpha = __builtin_amdgcn_exp2f(m[qi] - mt);
+        l[qi] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kt = kt0 + j;
-          const float v = sc[qi][j >> 2][j & 3];
-          x[j] = (kt >= lo_k && kt < k_end) ? v * a.scale_log2 : -INFINITY;
-        }
-        float mt = x[0];
+        for (int dt = 0; dt < 8; ++dt) acc[qi][dt] *= alpha;
+        m[qi] = mt;
+      }
+      float ps = 0.0f;
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m[qi], mt);
-        if (mn == -INFINITY) continue;   // no key of this head so far (uniform over the head's lanes)
-        const float alpha = exp2f(m[qi] - mn);
-        float p[8], ps = 0.0f;
+      for (int j = 0; j < 16; ++j) {
+        x[j] = __builtin_amdgcn_exp2f(x[j] - m[qi]);
+        ps += x[j];
+      }
+      l[qi] += ps;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = exp2f(x[j] - mn);
-          ps += p[j];
-        }
-        l[qi] = l[qi] * alpha + ps;
-        m[qi] = mn;
-        const u32x4_t pb{bf16_rne(p[0]) | (bf16_rne(p[1]) << 16), bf16_rne(p[2]) | (bf16_rne(p[3]) << 16),
-                         bf16_rne(p[4]) | (bf16_rne(p[5]) << 16), bf16_rne(p[6]) | (bf16_rne(p[7]) << 16)};
-        // V^T fragments: dim 16 dt + c, keys 32 st + 8 g .. + 7 of the tile
-        const unsigned char* vrow = lds + kLdsK + c * kVRow + (32 * st + 8 * g) * 2;
+      for (int st = 0; st < 2; ++st) {
+        const float* pp = x + 8 * st;
+        const u32x4_t pb{bf16_rne(pp[0]) | (bf16_rne(pp[1]) << 16), bf16_rne(pp[2]) | (bf16_rne(pp[3]) << 16),
+                         bf16_rne(pp[4]) | (bf16_rne(pp[5]) << 16), bf16_rne(pp[6]) | (bf16_rne(pp[7]) << 16)};
+        // V^T fragment of dim 16 dt + c: logical key pairs 16 st + 4 g .. + 3,
+        // stored at pair (16 st + 4 g) ^ 4 dt
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vrow + 16 * dt * kVRow);
-          acc[qi][dt] *= alpha;
+          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(lds + kLdsK + (16 * dt + c) * kVRow +
+                                                               4 * ((16 * st + 4 * g) ^ (4 * dt)));
           acc[qi][dt] = mfma_bf16(vf, pb, acc[qi][dt]);
         }
       }

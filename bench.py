@@ -180,6 +180,64 @@ def measure_verify(w, reps=10, mall="cold"):
     return res
 
 
+ATTN_SHAPES = {
+    # the drafter's windowed GQA layer at the sampler's batch sizes: 64 query /
+    # 4 key-value heads of 128, a 4096-token window, K=7, a full window of
+    # context (P = 8192) for every row
+    "b1": dict(B=1, K=7, Hq=64, Hkv=4, W=4096, P=8192),
+    "b88": dict(B=88, K=7, Hq=64, Hkv=4, W=4096, P=8192),
+}
+
+
+def measure_attention(name, reps=20, mall="cold"):
+    """The drafter's non-causal windowed block attention (one layer) on
+    synthetic bf16 Q/K/V of the ``ATTN_SHAPES`` shape. Mean us per call (two
+    launches, events on the launch stream, MALL flushed before each).
+    Algorithmic bytes: per (row, key/value head) the K and V rows of the
+    window's key range (W - 1 + K keys), plus Q read and o, lse written."""
+    import math
+    import torch
+    from ancestral_draft_token_amd import dspark_window_attention_workspace_bytes, dspark_window_block_attention
+    c = ATTN_SHAPES[name]
+    B, K, Hq, Hkv, W, P = c["B"], c["K"], c["Hq"], c["Hkv"], c["W"], c["P"]
+    D, L = 128, c["P"] + c["K"]
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(5)
+    q = torch.randn((B, K, Hq, D), device=dev, generator=g).to(torch.bfloat16)
+    kc = torch.randn((B, L, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn((B, L, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    ctx = torch.full((B,), P, dtype=torch.int32, device=dev)
+    out = torch.empty((B, K, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, K, Hq), dtype=torch.float32, device=dev)
+    wb = dspark_window_attention_workspace_bytes(B, K, Hq, Hkv, D, L, W)
+    ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+    flush_buf = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(reps + 2):
+            if mall == "cold":
+                torch.amax(flush_buf, dim=0, out=flush_out)
+            starts[i].record(stream)
+            dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, 1.0 / math.sqrt(D), out, lse, ws,
+                                          wb, stream=stream)
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    us = statistics.mean(s_.elapsed_time(e) * 1e3 for s_, e in zip(starts[2:], ends[2:]))
+    keys = min(P + K, W - 1 + K)
+    algo = B * Hkv * keys * D * 2 * 2 + B * K * Hq * D * 2 + B * K * Hq * (D + 1) * 4
+    flops = 4 * B * K * Hq * D * keys
+    del q, kc, vc, flush_buf
+    torch.cuda.empty_cache()
+    return {"shape": dict(c, D=D), "us": round(us, 2), "bytes": algo,
+            "achieved_gbs": round(algo / (us * 1e-6) / 1e9, 1),
+            "roofline_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1), "data": "synthetic bf16 N(0,1)"}
+
+
 def traffic_for(w, args):
     """Measured HBM bytes per launch of the dominant kernel, from the committed
     rocprofv3 counter summary for this workload (profiles/), scaled by the
@@ -336,6 +394,11 @@ def main():
             if name != args.workload:
                 print(f"[bench] verify {name}", file=sys.stderr, flush=True)
                 line["verify"][name] = measure_verify(inputs.WORKLOADS[name](), mall=args.mall)
+    # the drafter's windowed block attention (a second workload of the pages)
+    line["attention"] = {}
+    for name in (("b1", "b88") if not args.no_sweep else ("b88",)):
+        print(f"[bench] window attention {name}", file=sys.stderr, flush=True)
+        line["attention"][name] = measure_attention(name, mall=args.mall)
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
