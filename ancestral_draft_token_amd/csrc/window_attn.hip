@@ -49,7 +49,8 @@ constexpr int kKRow = kD * 2 + 16;           // LDS bytes per key row (16-byte p
 constexpr int kVRow = kTileKeys * 2 + 16;    // LDS bytes per transposed V row (one dim, 64 keys)
 constexpr int kLdsK = kTileKeys * kKRow;     // 17,408
 constexpr int kLdsV = kD * kVRow;            // 18,432
-constexpr int kTargetBlocks = 1024;          // workgroups a call aims for (splits are chosen from it)
+constexpr int kSlots = 512;                  // resident workgroups: two per CU on 256 CUs
+constexpr int kMaxSplits = 128;              // splits of one key range (combine's weight table)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -271,23 +272,46 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
 }
 
 __global__ __launch_bounds__(kD) void wa_combine(WaArgs a) {
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[2][kD / 64];
   const int h = blockIdx.x, k = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int kvh = h / kG, c = h % kG;
   const int Hq = a.Hkv * kG;
-  float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s) {
-    const size_t row = ((((size_t)b * a.Hkv + kvh) * a.S + s) * a.K + k) * kG + c;
-    M = fmaxf(M, a.part_ml[2 * row]);
+  // row of split s: base + s * stride
+  const size_t base = ((((size_t)b * a.Hkv + kvh) * a.S) * a.K + k) * kG + c;
+  const size_t stride = (size_t)a.K * kG;
+  // the splits' maxima and sums, one split per thread (every split is read once)
+  float mx = -INFINITY;
+  for (int s = d; s < a.S; s += kD) mx = fmaxf(mx, a.part_ml[2 * (base + s * stride)]);
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((d & 63) == 0) s_red[0][d >> 6] = mx;
+  __syncthreads();
+  float M = s_red[0][0];
+  for (int w = 1; w < kD / 64; ++w) M = fmaxf(M, s_red[0][w]);
+  float ls = 0.0f;
+  for (int s = d; s < a.S; s += kD) {
+    const float ms = a.part_ml[2 * (base + s * stride)];
+    const float wgt = ms == -INFINITY ? 0.0f : exp2f(ms - M);   // a split without a key of this head: 0
+    s_w[s] = wgt;
+    ls += a.part_ml[2 * (base + s * stride) + 1] * wgt;
   }
-  float Ls = 0.0f, o = 0.0f;
-  for (int s = 0; s < a.S; ++s) {
-    const size_t row = ((((size_t)b * a.Hkv + kvh) * a.S + s) * a.K + k) * kG + c;
-    const float ms = a.part_ml[2 * row];
-    if (ms == -INFINITY) continue;   // no key of this head in the split
-    const float wgt = exp2f(ms - M);
-    Ls += a.part_ml[2 * row + 1] * wgt;
-    o += a.part_o[row * kD + d] * wgt;
+  for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+  if ((d & 63) == 0) s_red[1][d >> 6] = ls;
+  __syncthreads();
+  float Ls = s_red[1][0];
+  for (int w = 1; w < kD / 64; ++w) Ls += s_red[1][w];
+  // the weighted sum of the partial outputs, 8 splits' loads in flight
+  float o = 0.0f;
+  int s = 0;
+  for (; s + 8 <= a.S; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = s_w[s + i] == 0.0f ? 0.0f : a.part_o[(base + (s + i) * stride) * kD + d];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o += v[i] * s_w[s + i];
   }
+  for (; s < a.S; ++s)
+    if (s_w[s] != 0.0f) o += a.part_o[(base + s * stride) * kD + d] * s_w[s];
   const size_t orow = ((size_t)b * a.K + k) * Hq + h;
   a.out[orow * kD + d] = o / Ls;
   if (d == 0) a.lse[orow] = (M + log2f(Ls)) * 0.69314718055994531f;
@@ -304,13 +328,32 @@ inline int check(int B, int K, int Hq, int Hkv, int D, int L, int W) {
   return DSPARK_OK;
 }
 
+// Splits of the key range, from a cost in units of one 64-key tile of K and
+// V (32 KB): a round of resident workgroups (two per CU) takes as long as
+// its largest split plus the partial output it writes (16 heads x K
+// positions x 128 floats, ~1.8 tiles at K = 7), and the merge reads every
+// partial once more, spread over the GPU. B=88, 4 heads: 4 splits (1408
+// workgroups in 3 rounds) against 3 (1056 in 3 rounds of larger splits) or
+// 13 (fuller rounds, 4x the partials). B=1: 65 splits of one tile.
 inline Plan plan(int B, int K, int Hkv, int W) {
   const long long span = (long long)W - 1 + K;                 // keys of the widest range
   const long long tiles = (span + kTileKeys - 1) / kTileKeys;
-  long long S = (kTargetBlocks + (long long)B * Hkv - 1) / ((long long)B * Hkv > 0 ? (long long)B * Hkv : 1);
-  if (S < 1) S = 1;
-  if (S > tiles) S = tiles;
-  const long long per = ((tiles + S - 1) / S) * kTileKeys;
+  const long long pairs = (long long)B * Hkv > 0 ? (long long)B * Hkv : 1;
+  const long long smax = tiles < kMaxSplits ? tiles : kMaxSplits;
+  const double part = (double)K * kG * kD * 4 / (kTileKeys * kD * 2 * 2);   // partial output, in tiles
+  long long best = 1;
+  double best_cost = 0.0;
+  for (long long S = 1; S <= smax; ++S) {
+    const long long per = (tiles + S - 1) / S;                 // tiles per split
+    const long long ns = (tiles + per - 1) / per;              // splits actually used
+    const long long rounds = (pairs * ns + kSlots - 1) / kSlots;
+    const double cost = (double)rounds * ((double)per + part) + (double)(pairs * ns) * part / kSlots;
+    if (S == 1 || cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  const long long per = ((tiles + best - 1) / best) * kTileKeys;
   Plan p;
   p.keys_per_split = (int)per;
   p.S = (int)((span + per - 1) / per);
