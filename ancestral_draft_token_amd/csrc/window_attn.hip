@@ -18,9 +18,9 @@
 // log-sum-exp merge.
 //
 // wa_partials: one 256-thread workgroup per (split, key/value head, row).
-// The key range is streamed in tiles of 64 keys through LDS (K as rows, V
-// transposed as dim rows), the next tile's global loads in flight while the
-// current one is used. Wave w owns draft positions w and w + 4; a position's
+// The key range is streamed in tiles of 64 keys through LDS (K as rows with
+// swizzled 16-byte chunks, V transposed as dim rows with swizzled key pairs),
+// the next tile's global loads in flight while the current one is used. Wave w owns draft positions w and w + 4; a position's
 // 16 heads are one MFMA tile. Scores are computed transposed,
 // S^T = K Q^T (v_mfma_f32_16x16x32_bf16: M = 16 keys, N = 16 heads, 4 steps
 // over D = 128), with the keys of each 32-key step assigned to the two score
@@ -45,7 +45,7 @@ constexpr int kG = 16;                       // query heads per key/value head
 constexpr int kKMax = 8;                     // draft positions: two per wave
 constexpr int kThreads = 256;
 constexpr int kTileKeys = 64;
-constexpr int kKRow = kD * 2 + 16;           // LDS bytes per key row (16-byte pad: conflict-free 16-lane reads)
+constexpr int kKRow = kD * 2;                // LDS bytes per key row (16-byte chunks swizzled by row)
 constexpr int kVRow = kTileKeys * 2 + 16;    // LDS bytes per transposed V row (one dim, 64 keys)
 constexpr int kLdsK = kTileKeys * kKRow;     // 17,408
 constexpr int kLdsV = kD * kVRow;            // 18,432
@@ -66,6 +66,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
+
+// K rows in LDS: 16-byte chunk j of row r sits at chunk j ^ kswz(r). The 16
+// rows one score-tile read touches (r = 32 st + 8 (c / 4) + 4 tt + c % 4 for
+// c = 0..15) get 16 different offsets, so a read is free of bank conflicts
+// with 32 or 64 banks; the stores (16 lanes per row) stay conflict-free.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
 
 struct WaArgs {
   const uint16_t* q;        // [B,K,Hq,D] bf16
@@ -156,11 +162,11 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
     {
       // thread t: K rows t/16 + 16 r, bytes 16 (t % 16) ..; V key pairs t/16 and
       // t/16 + 16, dims 8 (t % 16) .. + 7, into the swizzled transposed layout
-      unsigned char* kd = lds + (t >> 4) * kKRow + (t & 15) * 16;
-      *reinterpret_cast<uint4*>(kd) = ks0;
-      *reinterpret_cast<uint4*>(kd + 16 * kKRow) = ks1;
-      *reinterpret_cast<uint4*>(kd + 32 * kKRow) = ks2;
-      *reinterpret_cast<uint4*>(kd + 48 * kKRow) = ks3;
+      const int kr = t >> 4, kc = t & 15;
+      *reinterpret_cast<uint4*>(lds + kr * kKRow + 16 * (kc ^ kswz(kr))) = ks0;
+      *reinterpret_cast<uint4*>(lds + (kr + 16) * kKRow + 16 * (kc ^ kswz(kr + 16))) = ks1;
+      *reinterpret_cast<uint4*>(lds + (kr + 32) * kKRow + 16 * (kc ^ kswz(kr + 32))) = ks2;
+      *reinterpret_cast<uint4*>(lds + (kr + 48) * kKRow + 16 * (kc ^ kswz(kr + 48))) = ks3;
       const int sw = 4 * (((t & 15) >> 1) & 7);   // = vt_swizzle(8 (t % 16) + e) for every e < 8
       const int s0 = 4 * ((t >> 4) ^ sw), s1 = 4 * (((t >> 4) + 16) ^ sw);
       unsigned char* vd = lds + kLdsK + (t & 15) * 8 * kVRow;
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
       const int krow = 32 * (u >> 1) + 8 * (c >> 2) + 4 * (u & 1) + (c & 3);
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
-        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(lds + krow * kKRow + (32 * ds + 8 * g) * 2);
+        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(lds + krow * kKRow + 16 * ((4 * ds + g) ^ kswz(krow)));
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi)
           if (has[qi]) sc[qi][u] = mfma_bf16(af, qf[qi][ds], sc[qi][u]);
@@ -199,8 +205,14 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
     }
     // only the tiles at a split's ends or below a position's window start mask
     const bool edge = tb < lo_max || tb + kTileKeys > k_end;
+    // both positions' probabilities first, so each V^T fragment is read once
+    // per wave: pb[qi][st] is the bf16 B operand of keys 32 st + 8 g .. + 7
+    u32x4_t pb[2][2];
+    bool live[2];
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi) {
+      pb[qi][0] = pb[qi][1] = u32x4_t{0u, 0u, 0u, 0u};
+      live[qi] = false;
       if (!has[qi]) continue;
       // x[8 st + j]: key tb + 32 st + 8 g + j (base-2 scaled score)
       float x[16];
@@ -220,6 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       if (mt == -INFINITY && m[qi] == -INFINITY) continue;   // no key of this position yet (uniform)
+      live[qi] = true;
       if (mt > m[qi]) {
         // the running maximum grows: rescale (skipped once it has settled)
         const float alpha = __builtin_amdgcn_exp2f(m[qi] - mt);
@@ -238,16 +251,21 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const float* pp = x + 8 * st;
-        const u32x4_t pb{bf16_rne(pp[0]) | (bf16_rne(pp[1]) << 16), bf16_rne(pp[2]) | (bf16_rne(pp[3]) << 16),
-                         bf16_rne(pp[4]) | (bf16_rne(pp[5]) << 16), bf16_rne(pp[6]) | (bf16_rne(pp[7]) << 16)};
-        // V^T fragment of dim 16 dt + c: logical key pairs 16 st + 4 g .. + 3,
-        // stored at pair (16 st + 4 g) ^ 4 dt
+        pb[qi][st] = u32x4_t{bf16_rne(pp[0]) | (bf16_rne(pp[1]) << 16), bf16_rne(pp[2]) | (bf16_rne(pp[3]) << 16),
+                             bf16_rne(pp[4]) | (bf16_rne(pp[5]) << 16), bf16_rne(pp[6]) | (bf16_rne(pp[7]) << 16)};
+      }
+    }
+    // O^T += V^T P^T; V^T fragment of dim 16 dt + c: logical key pairs
+    // 16 st + 4 g .. + 3, stored at pair (16 st + 4 g) ^ 4 dt
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(lds + kLdsK + (16 * dt + c) * kVRow +
-                                                               4 * ((16 * st + 4 * g) ^ (4 * dt)));
-          acc[qi][dt] = mfma_bf16(vf, pb, acc[qi][dt]);
-        }
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(lds + kLdsK + (16 * dt + c) * kVRow +
+                                                             4 * ((16 * st + 4 * g) ^ (4 * dt)));
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi)
+          if (live[qi]) acc[qi][dt] = mfma_bf16(vf, pb[qi][st], acc[qi][dt]);
       }
     }
   }
