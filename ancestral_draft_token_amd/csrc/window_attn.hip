@@ -29,8 +29,9 @@
 // per step): each lane holds keys 8 (lane / 16) .. + 7 of one head, with no
 // data movement between the two products. Online softmax in base 2 per head;
 // probabilities rounded to bf16 for the second product.
-// wa_combine: one 128-thread block per (head, position, row) merges the
-// splits: M = max m_s, L = sum l_s 2^(m_s - M), o = sum 2^(m_s - M) o_s / L,
+// wa_combine: one 256-thread block per (position, key/value head, row)
+// merges the splits of its 16 heads (wa_combine_splits, for many splits,
+// spreads one head's splits over its threads): M = max m_s, L = sum l_s 2^(m_s - M), o = sum 2^(m_s - M) o_s / L,
 // lse = (M + log2 L) ln 2.
 
 #include <hip/hip_runtime.h>
@@ -50,7 +51,8 @@ constexpr int kVRow = kTileKeys * 2 + 16;    // LDS bytes per transposed V row (
 constexpr int kLdsK = kTileKeys * kKRow;     // 17,408
 constexpr int kLdsV = kD * kVRow;            // 18,432
 constexpr int kSlots = 512;                  // resident workgroups: two per CU on 256 CUs
-constexpr int kMaxSplits = 128;              // splits of one key range (combine's weight table)
+constexpr int kMaxSplits = 128;              // splits of one key range at most (wa_combine_splits' table)
+constexpr int kFewSplits = 16;               // up to this many, each merge thread walks the splits itself
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -289,7 +291,42 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kD) void wa_combine(WaArgs a) {
+// One 256-thread block per (position, key/value head, row): thread t merges
+// dims 8 (t % 16) .. + 7 of head t / 16 over the splits. The 16 threads of a
+// head read the same (max, sum) words (cached) and each computes the
+// weights itself; the partial outputs are read as float4.
+__global__ __launch_bounds__(kThreads) void wa_combine(WaArgs a) {
+  const int k = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int c = t >> 4, d0 = 8 * (t & 15);
+  const int Hq = a.Hkv * kG;
+  // row of split s: base + s * stride
+  const size_t base = ((((size_t)b * a.Hkv + kvh) * a.S) * a.K + k) * kG + c;
+  const size_t stride = (size_t)a.K * kG;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[2 * (base + s * stride)]);
+  float Ls = 0.0f;
+  f32x4_t o0{0.0f, 0.0f, 0.0f, 0.0f}, o1{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < a.S; ++s) {
+    const size_t row = base + s * stride;
+    const float ms = a.part_ml[2 * row];
+    if (ms == -INFINITY) continue;   // no key of this head in the split
+    const float w = exp2f(ms - M);
+    Ls += a.part_ml[2 * row + 1] * w;
+    const f32x4_t* po = reinterpret_cast<const f32x4_t*>(a.part_o + row * kD + d0);
+    o0 += po[0] * w;
+    o1 += po[1] * w;
+  }
+  const size_t orow = ((size_t)b * a.K + k) * Hq + kvh * kG + c;
+  f32x4_t* out = reinterpret_cast<f32x4_t*>(a.out + orow * kD + d0);
+  out[0] = o0 / Ls;
+  out[1] = o1 / Ls;
+  if ((t & 15) == 0) a.lse[orow] = (M + log2f(Ls)) * 0.69314718055994531f;
+}
+
+// The merge for many splits (small batches: B=1 has 65): one 128-thread
+// block per (head, position, row), the splits' maxima and weights read in
+// parallel (one split per thread), eight splits' partial outputs in flight.
+__global__ __launch_bounds__(kD) void wa_combine_splits(WaArgs a) {
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[2][kD / 64];
   const int h = blockIdx.x, k = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
@@ -425,7 +462,10 @@ int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, co
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   hipLaunchKernelGGL(wa_partials, dim3(p.S, Hkv, B), dim3(kThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
-  hipLaunchKernelGGL(wa_combine, dim3(Hq, K, B), dim3(kD), 0, stream, a);
+  if (p.S <= kFewSplits)
+    hipLaunchKernelGGL(wa_combine, dim3(K, Hkv, B), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(wa_combine_splits, dim3(Hq, K, B), dim3(kD), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
   return DSPARK_OK;
 }
