@@ -17,11 +17,12 @@
 // masking its own lower bound; the splits are then combined by the same
 // log-sum-exp merge.
 //
-// wa_partials: one 256-thread workgroup per (split, key/value head, row).
+// wa_partials: one 512-thread workgroup per (split, key/value head, row).
 // The key range is streamed in tiles of 64 keys through LDS (K as rows with
 // swizzled 16-byte chunks, V transposed as dim rows with swizzled key pairs),
-// the next tile's global loads in flight while the current one is used. Wave w owns draft positions w and w + 4; a position's
-// 16 heads are one MFMA tile. Scores are computed transposed,
+// the next tile's global loads in flight while the current one is used.
+// Wave w owns draft position w (eight waves, ~124 registers: four waves per
+// SIMD); a position's 16 heads are one MFMA tile. Scores are computed transposed,
 // S^T = K Q^T (v_mfma_f32_16x16x32_bf16: M = 16 keys, N = 16 heads, 4 steps
 // over D = 128), with the keys of each 32-key step assigned to the two score
 // tiles so that the accumulators land exactly in the B-operand layout of the
@@ -43,9 +44,15 @@ namespace dspark_wa {
 
 constexpr int kD = 128;                      // head dimension
 constexpr int kG = 16;                       // query heads per key/value head
-constexpr int kKMax = 8;                     // draft positions: two per wave
-constexpr int kThreads = 256;
+constexpr int kKMax = 8;                     // draft positions: one per wave of wa_partials
+constexpr int kThreads = 256;                // wa_combine
+constexpr int kQ = 1;                        // draft positions per wave of wa_partials
+constexpr int kPW = kKMax / kQ;              // waves of a wa_partials workgroup
+constexpr int kPartThreads = 64 * kPW;
+
 constexpr int kTileKeys = 64;
+constexpr int kKUnits = kTileKeys * 16 / kPartThreads;       // 16-byte K pieces a thread stages per tile
+constexpr int kVUnits = kTileKeys / 2 * 16 / kPartThreads;   // (key pair, 8 dims) V pieces
 constexpr int kKRow = kD * 2;                // LDS bytes per key row (16-byte chunks swizzled by row)
 constexpr int kVRow = kTileKeys * 2 + 16;    // LDS bytes per transposed V row (one dim, 64 keys)
 constexpr int kLdsK = kTileKeys * kKRow;     // 17,408
@@ -96,7 +103,7 @@ __device__ __forceinline__ int clamp_ctx(const WaArgs& a, int b) {
 // Transposed V rows are swizzled: key pair j of dim row d is stored at pair
 // j ^ (4 ((d / 16) % 8)), which keeps the transposing stores and the
 // fragment reads free of bank conflicts (rows of 144 bytes).
-__global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
+__global__ __launch_bounds__(kPartThreads, 4) void wa_partials(WaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsK + kLdsV];
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -114,22 +121,22 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
 
   // the two draft positions of this wave and their query fragments:
   // lane (c, g) holds head kvh*16 + c, dims 32 ds + 8 g .. + 7
-  int kq[2];
-  bool has[2];
-  u32x4_t qf[2][4];
+  int kq[kQ];
+  bool has[kQ];
+  u32x4_t qf[kQ][4];
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
-    kq[qi] = wv + 4 * qi;
+  for (int qi = 0; qi < kQ; ++qi) {
+    kq[qi] = wv + kPW * qi;
     has[qi] = kq[qi] < a.K;
     const uint16_t* qrow = a.q + (((size_t)b * a.K + (has[qi] ? kq[qi] : 0)) * Hq + kvh * kG + c) * kD;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
       qf[qi][ds] = has[qi] ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * ds + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  f32x4_t acc[2][8];
-  float m[2], l[2];
+  f32x4_t acc[kQ][8];
+  float m[kQ], l[kQ];
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
+  for (int qi = 0; qi < kQ; ++qi) {
     m[qi] = -INFINITY;
     l[qi] = 0.0f;
 #pragma unroll
@@ -138,21 +145,17 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
 
   // staging: K rows as 16-byte pieces (16 lanes per 256-byte row), V as
   // pairs of keys x 8 dims (written transposed, a dword per dim)
-  uint4 ks0, ks1, ks2, ks3, vs00, vs01, vs10, vs11;
+  static_assert(kKUnits == 2 && kVUnits == 1, "staging below is written for 512 threads");
+  uint4 ks0, ks1, vs0, vs1;
 #define WA_LOAD_TILE(tb)                                                                              \
   do {                                                                                                \
     const int tb_ = (tb);                                                                             \
-    const int r0_ = tb_ + (t >> 4), r1_ = r0_ + 16, r2_ = r0_ + 32, r3_ = r0_ + 48;                   \
-    const int cw_ = (t & 15) * 8;                                                                     \
+    const int r0_ = tb_ + (t >> 4), r1_ = r0_ + 32, cw_ = (t & 15) * 8;                               \
     ks0 = *reinterpret_cast<const uint4*>(kb + (size_t)(r0_ < hi ? r0_ : hi - 1) * rs + cw_);         \
     ks1 = *reinterpret_cast<const uint4*>(kb + (size_t)(r1_ < hi ? r1_ : hi - 1) * rs + cw_);         \
-    ks2 = *reinterpret_cast<const uint4*>(kb + (size_t)(r2_ < hi ? r2_ : hi - 1) * rs + cw_);         \
-    ks3 = *reinterpret_cast<const uint4*>(kb + (size_t)(r3_ < hi ? r3_ : hi - 1) * rs + cw_);         \
-    const int p0_ = tb_ + 2 * (t >> 4), p1_ = p0_ + 32;                                               \
-    vs00 = *reinterpret_cast<const uint4*>(vb + (size_t)(p0_ < hi ? p0_ : hi - 1) * rs + cw_);        \
-    vs01 = *reinterpret_cast<const uint4*>(vb + (size_t)(p0_ + 1 < hi ? p0_ + 1 : hi - 1) * rs + cw_); \
-    vs10 = *reinterpret_cast<const uint4*>(vb + (size_t)(p1_ < hi ? p1_ : hi - 1) * rs + cw_);        \
-    vs11 = *reinterpret_cast<const uint4*>(vb + (size_t)(p1_ + 1 < hi ? p1_ + 1 : hi - 1) * rs + cw_); \
+    const int p_ = tb_ + 2 * (t >> 4);                                                                \
+    vs0 = *reinterpret_cast<const uint4*>(vb + (size_t)(p_ < hi ? p_ : hi - 1) * rs + cw_);           \
+    vs1 = *reinterpret_cast<const uint4*>(vb + (size_t)(p_ + 1 < hi ? p_ + 1 : hi - 1) * rs + cw_);   \
   } while (0)
 
   const int n_tiles = k_begin < k_end ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
@@ -162,25 +165,20 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
     const int tb = k_begin + n * kTileKeys;
     __syncthreads();   // the previous tile is no longer read
     {
-      // thread t: K rows t/16 + 16 r, bytes 16 (t % 16) ..; V key pairs t/16 and
-      // t/16 + 16, dims 8 (t % 16) .. + 7, into the swizzled transposed layout
+      // K pieces: rows t / 16 and t / 16 + 32, chunk t % 16 (swizzled); V: key
+      // pair t / 16, dims 8 (t % 16) .. + 7, transposed and swizzled
       const int kr = t >> 4, kc = t & 15;
       *reinterpret_cast<uint4*>(lds + kr * kKRow + 16 * (kc ^ kswz(kr))) = ks0;
-      *reinterpret_cast<uint4*>(lds + (kr + 16) * kKRow + 16 * (kc ^ kswz(kr + 16))) = ks1;
-      *reinterpret_cast<uint4*>(lds + (kr + 32) * kKRow + 16 * (kc ^ kswz(kr + 32))) = ks2;
-      *reinterpret_cast<uint4*>(lds + (kr + 48) * kKRow + 16 * (kc ^ kswz(kr + 48))) = ks3;
-      const int sw = 4 * (((t & 15) >> 1) & 7);   // = vt_swizzle(8 (t % 16) + e) for every e < 8
-      const int s0 = 4 * ((t >> 4) ^ sw), s1 = 4 * (((t >> 4) + 16) ^ sw);
-      unsigned char* vd = lds + kLdsK + (t & 15) * 8 * kVRow;
-      const uint32_t a0[4] = {vs00.x, vs00.y, vs00.z, vs00.w}, a1[4] = {vs01.x, vs01.y, vs01.z, vs01.w};
-      const uint32_t b0[4] = {vs10.x, vs10.y, vs10.z, vs10.w}, b1[4] = {vs11.x, vs11.y, vs11.z, vs11.w};
+      *reinterpret_cast<uint4*>(lds + (kr + 32) * kKRow + 16 * (kc ^ kswz(kr + 32))) = ks1;
+      const int sl = 4 * (kr ^ (4 * ((kc >> 1) & 7)));
+      unsigned char* vd = lds + kLdsK + kc * 8 * kVRow + sl;
+      const uint32_t a0[4] = {vs0.x, vs0.y, vs0.z, vs0.w};
+      const uint32_t a1[4] = {vs1.x, vs1.y, vs1.z, vs1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sh = 16 * (e & 1);
-        *reinterpret_cast<uint32_t*>(vd + e * kVRow + s0) =
+        *reinterpret_cast<uint32_t*>(vd + e * kVRow) =
             ((a0[e >> 1] >> sh) & 0xFFFFu) | (((a1[e >> 1] >> sh) & 0xFFFFu) << 16);
-        *reinterpret_cast<uint32_t*>(vd + e * kVRow + s1) =
-            ((b0[e >> 1] >> sh) & 0xFFFFu) | (((b1[e >> 1] >> sh) & 0xFFFFu) << 16);
       }
     }
     __syncthreads();
@@ -189,9 +187,9 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
     // scores of the whole tile: sc[qi][2 st + tt]; score tile (st, tt) has A
     // row r = key 32 st + 8 (r / 4) + 4 tt + r % 4, so lane (c, g) ends up with
     // keys 32 st + 8 g + 4 tt + i of head c
-    f32x4_t sc[2][4];
+    f32x4_t sc[kQ][4];
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi)
+    for (int qi = 0; qi < kQ; ++qi)
 #pragma unroll
       for (int u = 0; u < 4; ++u) sc[qi][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -201,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
       for (int ds = 0; ds < 4; ++ds) {
         const u32x4_t af = *reinterpret_cast<const u32x4_t*>(lds + krow * kKRow + 16 * ((4 * ds + g) ^ kswz(krow)));
 #pragma unroll
-        for (int qi = 0; qi < 2; ++qi)
+        for (int qi = 0; qi < kQ; ++qi)
           if (has[qi]) sc[qi][u] = mfma_bf16(af, qf[qi][ds], sc[qi][u]);
       }
     }
@@ -209,10 +207,10 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
     const bool edge = tb < lo_max || tb + kTileKeys > k_end;
     // both positions' probabilities first, so each V^T fragment is read once
     // per wave: pb[qi][st] is the bf16 B operand of keys 32 st + 8 g .. + 7
-    u32x4_t pb[2][2];
-    bool live[2];
+    u32x4_t pb[kQ][2];
+    bool live[kQ];
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
+    for (int qi = 0; qi < kQ; ++qi) {
       pb[qi][0] = pb[qi][1] = u32x4_t{0u, 0u, 0u, 0u};
       live[qi] = false;
       if (!has[qi]) continue;
@@ -266,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
         const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(lds + kLdsK + (16 * dt + c) * kVRow +
                                                              4 * ((16 * st + 4 * g) ^ (4 * dt)));
 #pragma unroll
-        for (int qi = 0; qi < 2; ++qi)
+        for (int qi = 0; qi < kQ; ++qi)
           if (live[qi]) acc[qi][dt] = mfma_bf16(vf, pb[qi][st], acc[qi][dt]);
       }
     }
@@ -275,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void wa_partials(WaArgs a) {
 
   // partials: lane (c, g) holds O^T dims 16 dt + 4 g .. + 3 of head c
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
+  for (int qi = 0; qi < kQ; ++qi) {
     if (!has[qi]) continue;
     float lt = l[qi];
     lt += __shfl_xor(lt, 16);
@@ -460,7 +458,7 @@ int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, co
   a.B = B; a.K = K; a.Hkv = Hkv; a.L = L; a.W = W; a.S = p.S; a.keys_per_split = p.keys_per_split;
   a.scale_log2 = scale * 1.44269504088896341f;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  hipLaunchKernelGGL(wa_partials, dim3(p.S, Hkv, B), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(wa_partials, dim3(p.S, Hkv, B), dim3(kPartThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
   if (p.S <= kFewSplits)
     hipLaunchKernelGGL(wa_combine, dim3(K, Hkv, B), dim3(kThreads), 0, stream, a);
