@@ -301,18 +301,23 @@ __global__ __launch_bounds__(kThreads) void wa_combine(WaArgs a) {
   const size_t base = ((((size_t)b * a.Hkv + kvh) * a.S) * a.K + k) * kG + c;
   const size_t stride = (size_t)a.K * kG;
   float M = -INFINITY;
+#pragma unroll 4
   for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[2 * (base + s * stride)]);
   float Ls = 0.0f;
   f32x4_t o0{0.0f, 0.0f, 0.0f, 0.0f}, o1{0.0f, 0.0f, 0.0f, 0.0f};
+  // unrolled so several splits' loads are in flight; a split without a key
+  // of this head (max -inf) gets weight 0 and its (finite) partial adds 0
+#pragma unroll 4
   for (int s = 0; s < a.S; ++s) {
     const size_t row = base + s * stride;
     const float ms = a.part_ml[2 * row];
-    if (ms == -INFINITY) continue;   // no key of this head in the split
-    const float w = exp2f(ms - M);
-    Ls += a.part_ml[2 * row + 1] * w;
+    const float ls = a.part_ml[2 * row + 1];
     const f32x4_t* po = reinterpret_cast<const f32x4_t*>(a.part_o + row * kD + d0);
-    o0 += po[0] * w;
-    o1 += po[1] * w;
+    const f32x4_t p0 = po[0], p1 = po[1];
+    const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    Ls += ls * w;
+    o0 += p0 * w;
+    o1 += p1 * w;
   }
   const size_t orow = ((size_t)b * a.K + k) * Hq + kvh * kG + c;
   f32x4_t* out = reinterpret_cast<f32x4_t*>(a.out + orow * kD + d0);
