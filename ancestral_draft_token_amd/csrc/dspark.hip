@@ -2098,12 +2098,14 @@ __global__ __launch_bounds__(kThreads) void verify_partials(VerArgs a) {
   const float* qj = a.q + ((size_t)b * a.K + (residual ? j : 0)) * a.V;
   const uint64_t seed = (uint64_t)a.seed[b], off = (uint64_t)a.offset[b];
   const int c0 = c * (kIt * kVerColsMin) + 4 * t;
-  float4 pv[kIt], qv[kIt];
+  // read once: nontemporal loads (B=88: 34.4 us against 36.7)
+  fx4_t pv[kIt], qv[kIt];
 #pragma unroll
   for (int i = 0; i < kIt; ++i) {
     const int v = c0 + i * kVerColsMin;
-    pv[i] = v < a.V ? *reinterpret_cast<const float4*>(pj + v) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    qv[i] = (residual && v < a.V) ? *reinterpret_cast<const float4*>(qj + v) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    pv[i] = v < a.V ? __builtin_nontemporal_load(reinterpret_cast<const fx4_t*>(pj + v)) : fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    qv[i] = (residual && v < a.V) ? __builtin_nontemporal_load(reinterpret_cast<const fx4_t*>(qj + v))
+                                  : fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
   uint64_t kw = 0;   // best key over w = max(0, p - q) (or p)
 #pragma unroll
