@@ -162,3 +162,24 @@ def test_verify_block_full_size_after_the_draft_block():
     nn = n.cpu().numpy()
     assert ((nn >= 0) & (nn <= K)).all()
     say(f"accepted per row: mean {nn.mean():.2f}")
+
+
+@pytest.mark.parametrize("rule", ["standard", "block"])
+def test_verification_clamps_draft_tokens(rule):
+    """Draft tokens are device data: out-of-range ids are clamped into [0, V)
+    by both rules, as the oracle does, and the emitted prefix holds the
+    clamped ids."""
+    from test_gpu_verify import verify_gpu, check
+    B, K, V = 6, 4, 3000
+    d, q, p, sd, off = _case(B, K, V, seed=41, mix=0.95)
+    d[:, 0] = np.array([-5, V + 3, -1, V, 2 * V, -(2**31)], dtype=np.int32)
+    if rule == "standard":
+        n, out = verify_gpu(d, q, p, sd, off)
+        ref = check(d, q, p, sd, off, n, out)
+    else:
+        n, out = verify_block_gpu(d, q, p, sd, off)
+        ref = check_block(d, q, p, sd, off, n, out)
+    clamped = np.clip(d[:, 0].astype(np.int64), 0, V - 1)
+    for b in range(B):
+        if n[b] >= 1:
+            assert out[b, 0] == clamped[b]

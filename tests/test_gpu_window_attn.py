@@ -114,3 +114,15 @@ def test_window_attention_full_size_sampled():
         assert abs(lse[b, k, h] - rl[0]) <= 2e-4, (b, k, h)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     say(f"full-size attention: {len(rows)} sampled triples ok")
+
+
+def test_window_attention_clamps_context_length():
+    """ctx_len is device data: a value below 0 acts as 0 and one above L - K as
+    L - K (the header's defined behaviour); the oracle is run on the clamped
+    values."""
+    B, K, Hq, Hkv, L, W = 3, 7, 16, 1, 300, 128
+    q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=77)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(q, kc, vc, [-40, 5000, L - K], W, scale)
+    o_ref, lse_ref = wa.window_block_attention(_f64(q), _f64(kc), _f64(vc), np.array([0, L - K, L - K]), W, scale)
+    check(o, lse, o_ref, lse_ref, np.abs(_f64(vc)).max())
