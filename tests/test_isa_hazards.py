@@ -99,3 +99,37 @@ def test_depth_parser():
         (2, "scratch_store_dwordx4 off, a[4:7], off"),
         (0, "scratch_store_dword off, v1, off"),
     ]
+
+
+# ---- the windowed block attention ------------------------------------------------
+
+@pytest.fixture(scope="module")
+def attn_asm(tmp_path_factory) -> str:
+    if not os.path.exists(_build.hipcc()):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "window_attn.s"
+    src = [s for s in _build.SOURCES if s.endswith("window_attn.hip")][0]
+    flags = [f for f in _build.HIPCC_FLAGS if f not in ("-shared", "-fPIC", "-Wall")]
+    cmd = [_build.hipcc(), *flags, "--cuda-device-only", "-S", f"-I{_build.INCLUDE}", "-o", str(out), src]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _metadata(asm: str, name_part: str) -> dict:
+    for blk in asm.split("  - .agpr_count")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+        if name_part in name:
+            return {"vgpr": int(re.search(r"\.vgpr_count:\s+(\d+)", blk).group(1)),
+                    "scratch": int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", blk).group(1))}
+    raise AssertionError(f"{name_part} not found")
+
+
+def test_attention_kernel_has_no_scratch_and_four_waves_per_simd(attn_asm):
+    """The tile loop's staging registers were once demoted to scratch (every
+    tile then went through memory twice); and the kernel relies on four
+    waves per SIMD (at most 128 registers) to hide the HBM latency."""
+    md = _metadata(attn_asm, "wa_partials")
+    assert md["scratch"] == 0, md
+    assert md["vgpr"] <= 128, md
+    lines = attn_asm[attn_asm.index("wa_partials"):].splitlines()
+    assert sum(1 for l in lines[:6000] if "v_mfma_f32_16x16x32_bf16" in l) >= 32
