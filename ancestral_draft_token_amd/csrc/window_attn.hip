@@ -6,7 +6,7 @@
 // modeling_dflash.py note of the MiniMax-M3.1-Flash page): K draft-block
 // queries at positions P .. P+K-1 after a context of P tokens; query i
 // attends every existing key t (t < P + K) with |i - t| <= W - 1: the
-// context keys inside its window and every block position. GQA: 16 query
+// whole draft block and the context keys at most W - 1 positions back. GQA: 16 query
 // heads share one key/value head. Outputs o (float32) and the log-sum-exp
 // (natural log) of every (position, query head).
 //

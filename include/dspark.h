@@ -257,8 +257,8 @@ int dspark_verify_block(
  * ("brb-nv/TensorRT-LLM pull 21", section "1. Non-causal DSpark draft blocks
  * on TRTLLM (default path)"): K draft-block queries at positions
  * P .. P+K-1 after a context of P tokens; query i attends every key t < P+K
- * with |i - t| <= W - 1 (the context keys inside its window and every block
- * position). GQA with 16 query heads per key/value head.
+ * with |i - t| <= W - 1 (the whole draft block and the context keys at most
+ * W - 1 back). GQA with 16 query heads per key/value head.
  *
  *   q          [B,K,Hq,D]   bf16 queries, 16-byte aligned
  *   k_cache    [B,L,Hkv,D]  bf16 keys of positions 0 .. L-1 (the block's own

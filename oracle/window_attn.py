@@ -11,7 +11,8 @@ note): the drafter's windowed GQA layers are non-causal inside the draft
 block with a two-sided window (W-1, W-1). A draft block of K queries sits at
 positions P .. P+K-1 after a context of P tokens; query i = P + k attends
 every key t with |i - t| <= W - 1 among the P + K keys that exist (the
-context keys inside its window and every block position). Per query head h
+whole draft block, plus the context keys no more than W - 1 positions
+back). Per query head h
 (GQA: key/value head h // (Hq / Hkv)):
     s_t = scale * <q_h, k_t>,   lse = ln sum_t exp(s_t),
     o = sum_t exp(s_t - lse) v_t.
