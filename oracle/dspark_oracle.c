@@ -436,9 +436,9 @@ int dspark_oracle_verify_standard(
 /* ---- block verification ----------------------------------------------------
  *
  * The pages' other rule ("brb-nv/TensorRT-LLM pull 21", section "2. Golden
- * sampling semantics": rejection_sample_method block, which replaces the
- * token-level chain with block verification, Sun et al., 2024; its test
- * list states that the rule is lossless, checked by chi-square). The pages
+ * sampling semantics": the option rejection_sample_method = block, citing
+ * Sun et al., 2024; the page's test coverage claims losslessness under a
+ * chi-square test). The pages
  * only name it; the algorithm is the one of Sun, Mendlovic, Leviathan,
  * Aharoni, Beirami, Ro and Suresh, "Block Verification Accelerates
  * Speculative Decoding" (2024), restated here in the indices of the draft
