@@ -70,10 +70,12 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                   c, 0, 0, 0);
 }
 
-// float32 -> bf16, round to nearest even (inputs are finite and >= 0 here)
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// two float32 -> a packed bf16 pair (low half first), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // K rows in LDS: 16-byte chunk j of row r sits at chunk j ^ kswz(r). The 16
@@ -251,8 +253,8 @@ __global__ __launch_bounds__(kPartThreads, 4) void wa_partials(WaArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const float* pp = x + 8 * st;
-        pb[qi][st] = u32x4_t{bf16_rne(pp[0]) | (bf16_rne(pp[1]) << 16), bf16_rne(pp[2]) | (bf16_rne(pp[3]) << 16),
-                             bf16_rne(pp[4]) | (bf16_rne(pp[5]) << 16), bf16_rne(pp[6]) | (bf16_rne(pp[7]) << 16)};
+        pb[qi][st] = u32x4_t{pack_bf16(pp[0], pp[1]), pack_bf16(pp[2], pp[3]), pack_bf16(pp[4], pp[5]),
+                             pack_bf16(pp[6], pp[7])};
       }
     }
     // O^T += V^T P^T; V^T fragment of dim 16 dt + c: logical key pairs
