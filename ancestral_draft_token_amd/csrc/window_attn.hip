@@ -216,10 +216,10 @@ __global__ __launch_bounds__(kPartThreads, 4) void wa_partials(WaArgs a) {
       pb[qi][0] = pb[qi][1] = u32x4_t{0u, 0u, 0u, 0u};
       live[qi] = false;
       if (!has[qi]) continue;
-      // x[8 st + j]: key tb + 32 st + 8 g + j (base-2 scaled score)
+      // x[8 st + j]: key tb + 32 st + 8 g + j
       float x[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = sc[qi][2 * (j >> 3) + ((j >> 2) & 1)][j & 3] * a.scale_log2;
+      for (int j = 0; j < 16; ++j) x[j] = sc[qi][2 * (j >> 3) + ((j >> 2) & 1)][j & 3];   // raw <q, k>
       if (edge) {
         const int lo_k = P + kq[qi] - (a.W - 1);
 #pragma unroll
@@ -228,11 +228,14 @@ __global__ __launch_bounds__(kPartThreads, 4) void wa_partials(WaArgs a) {
           if (!(kt >= lo_k && kt < k_end)) x[j] = -INFINITY;
         }
       }
+      // the maximum of the raw scores, then scaled (the scale is positive);
+      // the exponent below is one fma per score
       float mt = x[0];
 #pragma unroll
       for (int j = 1; j < 16; ++j) mt = fmaxf(mt, x[j]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt *= a.scale_log2;
       if (mt == -INFINITY && m[qi] == -INFINITY) continue;   // no key of this position yet (uniform)
       live[qi] = true;
       if (mt > m[qi]) {
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(kPartThreads, 4) void wa_partials(WaArgs a) {
       float ps = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        x[j] = __builtin_amdgcn_exp2f(x[j] - m[qi]);
+        x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2, -m[qi]));
         ps += x[j];
       }
       l[qi] += ps;
