@@ -1378,7 +1378,7 @@ constexpr int kMfLdsTiles = kResSlice / 16 - kMfRegTiles;  // 17
 constexpr int kMfLdsPerWave = (kMfLdsTiles + kMfWaves - 1) / kMfWaves;   // 5
 constexpr int kMfTilesMax = kMfTilesPerWave + kMfLdsPerWave;            // 13
 constexpr int kMfKSteps = kResRank / 32;                   // 8
-constexpr int kMfAhead = 4;                                // base logits loaded this many tiles ahead
+constexpr int kMfAhead = 5;                                // base logits loaded this many tiles ahead (B=88: -4 us against 4)
 constexpr int kMfNextAt = kMfTilesMax - kMfAhead;          // the last kMfAhead tiles load the next N-tile's first bases
 constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
 constexpr int kMfERow = 528;                               // bytes per staged E row: 512 + 16 (16-byte aligned rows; 16 lanes of one 128-bit read cover all banks)
