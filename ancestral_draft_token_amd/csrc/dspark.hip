@@ -1847,9 +1847,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 
   // Base logits of each tile, one register set per tile (compile-time indices
   // after unrolling, so nothing is copied while a load is in flight): tile
-  // i + 4 is loaded during tile i, and tiles 0..3 of the next N-tile (or of the
-  // next position's first N-tile, which does not depend on the token) during
-  // tiles 8..11.
+  // i + kMfAhead is loaded during tile i, and the first kMfAhead tiles of the
+  // next N-tile (or of the next position's first N-tile, which does not depend
+  // on the token) during the last kMfAhead tiles.
   Base4<kBf16Base> bq[kMfTilesMax];
   const unsigned char* bp = lane_base(0, 0);   // base logits of this N-tile's row of the lane
 #pragma unroll
