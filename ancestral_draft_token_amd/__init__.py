@@ -30,10 +30,11 @@ EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_launch_plan",
             "dspark_status_string", "dspark_verify_workspace_bytes", "dspark_verify_standard",
             "dspark_verify_block_workspace_bytes", "dspark_verify_block",
-            "dspark_window_attention_workspace_bytes", "dspark_window_block_attention")
+            "dspark_window_attention_workspace_bytes", "dspark_window_block_attention",
+            "dspark_block_status", "dspark_set_wait_limit")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
-                3: "resident_clear", 4: "markov_bias_gumbel_argmax"}
+                4: "markov_bias_gumbel_argmax"}
 
 _lib = None
 
@@ -84,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_window_attention_workspace_bytes.restype = Z
     lib.dspark_window_block_attention.argtypes = [P, P, P, P, I, I, I, I, I, I, I, ctypes.c_float, P, P, P, Z, P]
     lib.dspark_window_block_attention.restype = I
+    lib.dspark_block_status.argtypes = [P, P]
+    lib.dspark_block_status.restype = I
+    lib.dspark_set_wait_limit.argtypes = [ctypes.c_uint]
+    lib.dspark_set_wait_limit.restype = ctypes.c_uint
     _lib = lib
     return lib
 
@@ -158,6 +163,21 @@ def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, off
     if check and rc != DSPARK_OK:
         raise DSparkError(rc, where)
     return rc
+
+
+def dspark_block_status(status, stream=None, check: bool = True) -> int:
+    """Enqueue the status read of the last resident block on the current device
+    into ``status`` (a device int32 tensor or address); see ``include/dspark.h``."""
+    rc = load_library().dspark_block_status(_ptr(status), _stream_ptr(stream))
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_block_status")
+    return rc
+
+
+def dspark_set_wait_limit(reads: int) -> int:
+    """Set the resident kernels' wait limit (reads of an exchange word) for later
+    calls; returns the previous limit."""
+    return int(load_library().dspark_set_wait_limit(int(reads)))
 
 
 def dspark_verify_workspace_bytes(B: int, K: int, V: int) -> int:

@@ -2,11 +2,11 @@
 //
 // The method ("brb-nv/TensorRT-LLM pull 21", section "2. Golden sampling
 // semantics"; "brb-nv/TensorRT-LLM pull 27", section "2. One fused kernel per
-// draft position"): position k of a draft block is drawn from
-// softmax((base_k + bias(d_{k-1})) / T) by Gumbel-max, where bias(d) = E[d] . W
-// is a rank-r Markov head and d_{k-1} the token drawn just before; after the
-// block the proposal q_k = softmax(logits_k / T) is written from the same
-// float32 logits the draw used.
+// draft position"): each position k of a draft block samples d_k, by
+// Gumbel-max, from the softmax of (base_k + E[d_{k-1}] . W) * (1/T), with
+// E[d] . W a rank-r Markov head evaluated at the previous position's sample;
+// after the block the proposal q_k = softmax(logits_k / T) is written from the
+// same float32 logits the samples were taken from.
 //
 // Kernels, all on one stream (capturable into one hipGraph):
 //   markov_bias_gumbel_argmax (once per position): streams W and the base
@@ -750,7 +750,8 @@ __global__ __launch_bounds__(kThreads) void pick_and_gather(PickArgs a) {
 // nontemporal hint (not touched again by this call); q is written with
 // ordinary stores (B=88: 174 us against 189 with nontemporal stores). Sampling rows
 // recompute s = logit * invT exactly as the draw did; greedy rows get one-hot
-// at d_k. With last_from_partials (B == 1), the last position's token and
+// at d_k; positions a resident block left without a token (token -1 after an
+// expired wait) get NaN. With last_from_partials (B == 1), the last position's token and
 // (M, S) are reduced here from its chunk partials; block 0 of that row stores
 // them.
 // ---------------------------------------------------------------------------
@@ -840,6 +841,17 @@ __device__ __forceinline__ void proposal_block(const PropArgs& a, int b, int k, 
     tok = a.tokens[bk];
   }
 
+  if (tok < 0) {
+    // a resident block whose bounded wait expired left this position without
+    // a token (and without complete statistics): its proposal is NaN
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const int v = c0 + j * kThreads * 4;
+      if (in_row(v)) *reinterpret_cast<fx4_t*>(a.q + row + v) = fx4_t{nan, nan, nan, nan};
+    }
+    return;
+  }
   if (greedy) {
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
@@ -914,7 +926,84 @@ constexpr size_t kResLdsE = (size_t)kResRowsMax * kResRank * 2;      // 2,048 by
 constexpr size_t kResLdsBytes = kResLdsW + kResLdsE;
 constexpr int kResTagShift = 50;                           // word: tag | ord(z) | index
 constexpr uint64_t kResIdxMask = (1ull << 18) - 1;         // V <= 2^18
-constexpr int kResMaxCUs = 1024;
+constexpr int kResMaxCUs = 512;
+constexpr unsigned kDefaultWaitLimit = 1u << 20;           // about a second of polling
+constexpr int kExRows = 128;                               // exchange rows per workgroup (both resident kernels)
+constexpr int kExZeroWords = 512;                          // 4 KB that are never written
+
+// Exchange state of the resident kernels: one copy per device, in the
+// library's own device memory (zero when the code object is loaded), so it
+// never needs clearing before a call. Every resident launch has G = the
+// device's compute-unit count; workgroup i of the launches on a device takes
+// arrival number i in launch order, so call c = arrival / G is the same for
+// all workgroups of one launch (launches never overlap: each needs every CU).
+// A word published at position k of call c carries the tag (c & 1, k + 1).
+// At exit every workgroup rewrites each of its slots this call did not use
+// with a tag of this call (res_retire), so when call c + 1 starts every slot
+// holds a tag of parity c & 1, which no tag call c + 1 waits for can equal.
+struct ResExchange {
+  unsigned long long arrivals;   // resident workgroups started on this device
+  unsigned long long failed;     // 1 + the index of the last call in which a bounded wait expired
+  unsigned long long pad[30];    // the words below start on their own cache line
+  uint64_t xrow[2][kResMaxCUs][kExRows];   // per-workgroup tagged words, by position parity
+  uint64_t xwin[2][kExRows];               // tagged row winners (MFMA kernel), by position parity
+  uint64_t zeros[kExZeroWords];            // never written: base logits of rows that have none
+};
+__device__ __align__(256) ResExchange g_exchange;
+
+__device__ __forceinline__ uint64_t res_tag(uint32_t cpar, int k) {
+  return (((uint64_t)cpar << 8) | (uint64_t)(k + 1)) << kResTagShift;
+}
+
+__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The call index of this launch (thread 0 only; it is the first device
+// access of the workgroup, and its result is needed only at the first
+// publish).
+__device__ __forceinline__ unsigned long long res_arrive(ResExchange* ex, int G) {
+  return __hip_atomic_fetch_add(&ex->arrivals, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) /
+         (unsigned long long)G;
+}
+
+__device__ __forceinline__ void res_fail(ResExchange* ex, unsigned long long call) {
+  __hip_atomic_fetch_max(&ex->failed, call + 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Rewrite, with a tag of this call, each slot of workgroup g that this call
+// did not publish into: rows >= B, and the parity buffers of positions it
+// never reached (n_pub = positions it published; buffer h is used from
+// position h on). Winner slots of rows b = g, g + G, ... are owned by g
+// (n_win = positions it published winners for; 0 where the kernel has none).
+// Called by every thread of the workgroup once it is done with the exchange.
+__device__ __forceinline__ void res_retire(ResExchange* ex, int g, int G, int B, int n_pub, int n_win,
+                                           uint32_t cpar, int t_in, int nthreads) {
+  // the thread index through an opaque copy, so the slot addresses are formed
+  // here and not hoisted into registers held across the caller's loops
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(t_in));
+  const uint64_t old = res_tag(cpar, -1);   // tag (c & 1, 0): never waited for
+  for (int i = t; i < 2 * kExRows; i += nthreads) {
+    const int h = i / kExRows, b = i % kExRows;
+    if (!(b < B && n_pub > h)) st_agent_u64(&ex->xrow[h][g][b], old);
+  }
+  for (int i = t; i < 2 * kExRows; i += nthreads) {
+    const int h = i / kExRows, b = i % kExRows;
+    if (b % G == g && !(b < B && n_win > h)) st_agent_u64(&ex->xwin[h][b], old);
+  }
+}
+
+// Status of the last resident call on this device: 1 if one of its bounded
+// waits expired, else 0 (also when no resident call has run).
+__global__ void res_status(ResExchange* ex, unsigned G, int32_t* out) {
+  const unsigned long long a = __hip_atomic_load(&ex->arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long f = __hip_atomic_load(&ex->failed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  out[0] = (a >= G && f == a / G) ? 1 : 0;
+}
 
 struct ResArgs {
   const void* base;
@@ -927,11 +1016,10 @@ struct ResArgs {
   const int32_t* n_real;
   float* logits;
   int32_t* tokens;
-  uint64_t* xkey;      // [2][G][kResRowsMax] tagged exchange words, zeroed by res_clear
+  ResExchange* ex;     // the device's exchange state
   Stat* stat_part;     // [K][B][G] per-workgroup softmax statistics
-  int* fail;           // set when a bounded device wait expires
   int B, K, V, r, slice;
-  unsigned spin_limit;
+  unsigned spin_limit; // reads of a word before its wait expires (0: expires at once)
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -951,13 +1039,6 @@ __device__ __forceinline__ void pack_pairs(uint4 x, uint4 y, uint32_t out[8]) {
   out[2] = pair_lo(x.y, y.y); out[3] = pair_hi(x.y, y.y);
   out[4] = pair_lo(x.z, y.z); out[5] = pair_hi(x.z, y.z);
   out[6] = pair_lo(x.w, y.w); out[7] = pair_hi(x.w, y.w);
-}
-
-__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Value of lane partner(l) within its group of 8 lanes, by DPP: the half-row
@@ -1072,9 +1153,12 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
   __shared__ Stat s_stat[kResWaves][RB];
   __shared__ uint64_t s_x[kResWaves][RB];
   __shared__ int s_fail;
+  __shared__ unsigned long long s_call;
 
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int g = blockIdx.x, G = gridDim.x;
+  unsigned long long call0 = 0;
+  if (t == 0) call0 = res_arrive(a.ex, G);
   const int V = a.V, r = a.r, K = a.K, B = a.B;
   const int js = lane & 7;                    // rank slice: rows 32 js .. 32 js + 31
   const bool j_ok = 32 * js < r;
@@ -1182,7 +1266,11 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     gather_e(d0);
   }
   prepare(0);
+  if (t == 0) s_call = call0;
   __syncthreads();
+  // the call's parity, wave-uniform (a scalar register); the full index is
+  // read from LDS only where a wait expires
+  const uint32_t cpar = __builtin_amdgcn_readfirstlane((uint32_t)s_call & 1u);
 
   for (int k = 0; k < K; ++k) {
     // ---- bias GEMV: VGPR unit, then LDS unit; reduce-scatter over the rank slices
@@ -1286,8 +1374,7 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       // tag alone, which every real candidate beats
       const uint64_t ord = kk >> 32;
       const uint64_t idx = kk ? kResIdxMask - (uint64_t)key_token(kk) : 0ull;
-      const uint64_t word = ((uint64_t)(k + 1) << kResTagShift) | (ord << 18) | idx;
-      st_agent_u64(a.xkey + ((size_t)(k & 1) * G + g) * kResRowsMax + t, word);
+      st_agent_u64(&a.ex->xrow[k & 1][g][t], res_tag(cpar, k) | (ord << 18) | idx);
     }
 
     // ---- position k+1's noise and base do not depend on d_k: prepare them now
@@ -1299,9 +1386,11 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     uint64_t xb = 0;
     bool failed = false;
     const int xr = t % RB;
+    const uint64_t tag = res_tag(cpar, k) >> kResTagShift;
     if (xr < B) {
       for (int gg = t / RB; gg < G; gg += kResThreads / RB) {
-        const uint64_t* pw = a.xkey + ((size_t)(k & 1) * G + gg) * kResRowsMax + xr;
+        const uint64_t* pw = &a.ex->xrow[k & 1][gg][xr];
+        if (a.spin_limit == 0) { failed = true; break; }
         // two reads of the word in flight, staggered by ~1500 cycles and
         // checked in turn, so a word that lands is seen about half a round trip
         // later on average (three in flight were no better: more traffic)
@@ -1309,27 +1398,30 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
         __builtin_amdgcn_s_sleep(24);
         uint64_t w1 = ld_agent_u64(pw);
         uint64_t w = 0;
-        for (unsigned spins = 0;; ++spins) {
-          if ((int)(w0 >> kResTagShift) == k + 1) { w = w0; break; }
+        for (unsigned reads = 2;; reads += 2) {
+          if ((w0 >> kResTagShift) == tag) { w = w0; break; }
+          if ((w1 >> kResTagShift) == tag) { w = w1; break; }
+          if (reads >= a.spin_limit) { failed = true; break; }
           w0 = ld_agent_u64(pw);
-          if ((int)(w1 >> kResTagShift) == k + 1) { w = w1; break; }
           w1 = ld_agent_u64(pw);
-          if (spins > a.spin_limit) { failed = true; break; }
         }
+        if (failed) break;
         xb = umax64(xb, w);
       }
     }
     if (failed) {
       s_fail = 1;
-      atomicExch(a.fail, 1);
+      res_fail(a.ex, s_call);
     }
     // lanes of the same row (equal t % RB) combine
     xb = wave_max_u64_class<RB>(xb);
     if (lane < RB) s_x[wv][lane] = xb;
     __syncthreads();
     if (s_fail) {
+      // an expired wait: this position and the later ones get no token
       if (g == 0 && t < B)
         for (int kk = k; kk < K; ++kk) a.tokens[(size_t)t * K + kk] = -1;
+      res_retire(a.ex, g, G, B, k + 1, 0, cpar, t, kResThreads);
       return;
     }
     int d[RB];
@@ -1346,12 +1438,7 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       __syncthreads();
     }
   }
-}
-
-// Zero the exchange words and the failure flag before a resident launch.
-__global__ __launch_bounds__(kThreads) void res_clear(uint64_t* xkey, int n, int* fail) {
-  for (int i = threadIdx.x + blockIdx.x * kThreads; i < n; i += kThreads * gridDim.x) xkey[i] = 0ull;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *fail = 0;
+  res_retire(a.ex, g, G, B, K, 0, cpar, t, kResThreads);
 }
 
 // ---------------------------------------------------------------------------
@@ -1383,7 +1470,6 @@ constexpr int kMfNextAt = kMfTilesMax - kMfAhead;          // the last kMfAhead 
 constexpr int kMfRowsMax = 128;                            // 8 N-tiles of 16 rows
 constexpr int kMfERow = 528;                               // bytes per staged E row: 512 + 16 (16-byte aligned rows; 16 lanes of one 128-bit read cover all banks)
 constexpr int kMfSinkFloats = 1024;                        // sink: stores of lanes without a row or column
-constexpr int kMfZeroWords = 512;                          // 4 KB of zeros: base logits of rows that have none
 constexpr size_t kMfLdsW = (size_t)kMfLdsTiles * kMfKSteps * 64 * 16;   // 139,264 bytes
 constexpr size_t kMfLdsE = (size_t)2 * 16 * kMfERow;                    // 16,896 bytes
 constexpr size_t kMfLdsBytes = kMfLdsW + kMfLdsE;
@@ -1454,14 +1540,14 @@ struct MfArgs {
   const int32_t* n_real;
   float* logits;
   int32_t* tokens;
-  uint64_t* xrow;      // [2][G][kMfRowsMax] per-workgroup tagged words
-  uint64_t* xwin;      // [2][kMfRowsMax] tagged row winners
+  ResExchange* ex;     // the device's exchange state (arrivals, failure record, retire)
+  uint64_t* xrow;      // ex->xrow, ex->xwin and ex->zeros, passed as their own arguments
+  uint64_t* xwin;      // (derived from ex inside the N-tile loop they cost scalar registers
+  const void* zeros;   // that were spilled to vector lanes and reloaded every tile)
   Stat* stat_part;     // [K][B][G]
-  int* fail;
   float* sink;         // [kMfSinkFloats] stores of lanes without a real row or column
-  const void* zeros;   // [kMfZeroWords] zeroed words: the base logits of padding rows
   int B, K, V, r, slice;
-  unsigned spin_limit;
+  unsigned spin_limit; // reads of a word before its wait expires (0: expires at once)
 };
 
 // Row state kept in LDS for the whole launch (temperature, slot, padding).
@@ -1641,10 +1727,13 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   __shared__ MfRow s_row[kMfRowsMax];
   __shared__ int s_d[kMfRowsMax];                        // previous token per row
   __shared__ int s_fail;
+  __shared__ unsigned long long s_call;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform
   const int g = blockIdx.x, G = gridDim.x;
+  unsigned long long call0 = 0;
+  if (t == 0) call0 = res_arrive(a.ex, G);
   const int V = a.V, r = a.r, K = a.K, B = a.B;
   const int NT = (B + 15) / 16;
   const int col0 = g * a.slice;
@@ -1771,6 +1860,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     mf_store_erow(lds_e, t, e0);
     mf_store_erow(lds_e + 16 * kMfERow, t, epre);
   }
+  if (t == 0) s_call = call0;
 
   // the wave's tiles: i < 8 are VGPR tiles 8 wv + i; i >= 8 are LDS tiles 32 + wv + 4 (i - 8)
   auto tile_m = [&](int i) {
@@ -1819,6 +1909,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   };
 
   __syncthreads();
+  // the call's parity, wave-uniform (a scalar register); the full index is
+  // read from LDS only where a wait expires
+  const uint32_t cpar = __builtin_amdgcn_readfirstlane((uint32_t)s_call & 1u);
 
   // Combine the waves' partials of N-tile nt and publish each row's tagged
   // word. Wave 1 does it (wave 0 may own one more tile than the others):
@@ -1839,8 +1932,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       if (lane < 16 && b < B) {
         a.stat_part[((size_t)k * B + b) * G + g] = ss;
         const uint64_t idx = kk ? kResIdxMask - (uint64_t)key_token(kk) : 0ull;
-        const uint64_t word = ((uint64_t)(k + 1) << kResTagShift) | ((kk >> 32) << 18) | idx;
-        st_agent_u64(a.xrow + ((size_t)(k & 1) * G + g) * kMfRowsMax + b, word);
+        st_agent_u64(a.xrow + ((size_t)(k & 1) * kResMaxCUs + g) * kExRows + b, res_tag(cpar, k) | ((kk >> 32) << 18) | idx);
       }
     }
   };
@@ -1954,46 +2046,51 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 
     // ---- exchange level 2: the owner of row b (workgroup b, b + G, ...) reduces its G
     // words in wave 0 alone (each lane polls G / 64 of them, the first loads of a
-    // group of four in flight together; no LDS, no barrier) and publishes the winner
-    const uint64_t tag = (uint64_t)(k + 1);
-    uint64_t* xr = a.xrow + (size_t)(k & 1) * G * kMfRowsMax;
-    uint64_t* xw = a.xwin + (size_t)(k & 1) * kMfRowsMax;
+    // group of four in flight together; no LDS, no barrier) and publishes the winner.
+    // A winner is published only when all G words were seen: a wait that expires
+    // publishes nothing, so no workgroup can take a winner made of part of the words.
+    const uint64_t tagw = res_tag(cpar, k);
+    const uint64_t tag = tagw >> kResTagShift;
+    uint64_t* xr = a.xrow + (size_t)(k & 1) * kResMaxCUs * kExRows;
+    uint64_t* xw = a.xwin + (size_t)(k & 1) * kExRows;
     bool failed = false;
     if (wv == 0) {
       for (int b = g; b < B; b += G) {
         uint64_t x = 0;
-        for (int i0 = lane; i0 < G; i0 += 4 * 64) {
+        bool lfail = a.spin_limit == 0;
+        for (int i0 = lane; i0 < G && !lfail; i0 += 4 * 64) {
           // the words still missing are reloaded together: one round trip per pass
           uint64_t w[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            w[j] = i0 + 64 * j < G ? ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kMfRowsMax + b) : (tag << kResTagShift);
-          unsigned spins = 0;
-          for (;;) {
+            w[j] = i0 + 64 * j < G ? ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kExRows + b) : tagw;
+          for (unsigned reads = 1;; ++reads) {
             bool all = true;
 #pragma unroll
             for (int j = 0; j < 4; ++j) all = all && (w[j] >> kResTagShift) == tag;
             if (all) break;
-            if (++spins > a.spin_limit) { failed = true; break; }
+            if (reads >= a.spin_limit) { lfail = true; break; }
             __builtin_amdgcn_s_sleep(1);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if ((w[j] >> kResTagShift) != tag) w[j] = ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kMfRowsMax + b);
+              if ((w[j] >> kResTagShift) != tag) w[j] = ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kExRows + b);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) x = umax64(x, w[j]);
         }
         x = wave_max_u64(x);
-        if (lane == 0) st_agent_u64(xw + b, (tag << kResTagShift) | (x & ((1ull << kResTagShift) - 1)));
+        const bool wave_failed = __ballot(lfail) != 0ull;
+        failed = failed || wave_failed;
+        if (lane == 0 && !wave_failed) st_agent_u64(xw + b, tagw | (x & ((1ull << kResTagShift) - 1)));
       }
     }
     // ---- level 3: every workgroup reads the B winners
     for (int b = t; b < B; b += kMfThreads) {
       const uint64_t* pw = xw + b;
+      if (a.spin_limit == 0) { failed = true; break; }
       uint64_t w = ld_agent_u64(pw);
-      unsigned spins = 0;
-      while ((w >> kResTagShift) != tag) {
-        if (++spins > a.spin_limit) { failed = true; break; }
+      for (unsigned reads = 1; (w >> kResTagShift) != tag; ++reads) {
+        if (reads >= a.spin_limit) { failed = true; break; }
         __builtin_amdgcn_s_sleep(1);
         w = ld_agent_u64(pw);
       }
@@ -2002,13 +2099,15 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     }
     if (failed) {
       s_fail = 1;
-      atomicExch(a.fail, 1);
+      res_fail(a.ex, s_call);
     }
     __syncthreads();
     if (s_fail) {
+      // an expired wait: this position and the later ones get no token
       if (g == 0)
         for (int b = t; b < B; b += kMfThreads)
           for (int kk = k; kk < K; ++kk) a.tokens[(size_t)b * K + kk] = -1;
+      res_retire(a.ex, g, G, B, k + 1, k, cpar, t, kMfThreads);
       return;
     }
     if (g == 0)
@@ -2022,6 +2121,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       mf_store_erow(lds_e + 16 * kMfERow, t, epre);
     }
   }
+  res_retire(a.ex, g, G, B, K, K, cpar, t, kMfThreads);
 }
 
 // ---------------------------------------------------------------------------
@@ -2380,17 +2480,15 @@ struct Workspace {
   Stat* part_stat[2];
   Stat* row_stat;
   uint16_t* e_buf;
-  uint64_t* xkey;          // resident paths: per-workgroup exchange words
-  uint64_t* xwin;          // resident MFMA path: [2][kMfRowsMax] row winners (follows xkey)
   Stat* stat_part;         // resident paths: [K][B][kResMaxCUs]
-  int* fail;               // resident path: bounded-wait failure flag
   float* sink;             // resident MFMA path: [kMfSinkFloats] discarded stores
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Layout for the largest chunk count (chunk = 128 columns), plus the resident
-// paths' exchange words and per-workgroup statistics when B <= 128.
+// paths' per-workgroup statistics and sink when B <= 128. (Their exchange
+// words live in the library's own device memory, g_exchange.)
 inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* base) {
   const size_t max_chunks = (size_t)(V + kTile - 1) / kTile;
   size_t off = 0;
@@ -2401,16 +2499,10 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
   }
   const size_t o_rst = off; off = align_up(off + (size_t)B * K * sizeof(Stat), 256);
   const size_t o_e = off;   off = align_up(off + (size_t)B * r * sizeof(uint16_t), 256);
-  size_t o_x = 0, o_w = 0, o_sp = 0, o_f = 0, o_s = 0;
+  size_t o_sp = 0, o_s = 0;
   const bool resident_ws = B <= kMfRowsMax;
   if (resident_ws) {
-    // exchange words of both resident kernels: [2][CUs][rows] then [2][rows] winners
-    o_x = off;  off += (size_t)2 * kResMaxCUs * kMfRowsMax * sizeof(uint64_t);
-    // (the MFMA kernel's winners follow the G workgroups' words it uses, and
-    // its zeroed words follow the winners, inside this region and the next)
-    o_w = off;  off = align_up(off + (size_t)(2 * kMfRowsMax + kMfZeroWords) * sizeof(uint64_t), 256);
     o_sp = off; off = align_up(off + (size_t)K * B * kResMaxCUs * sizeof(Stat), 256);
-    o_f = off;  off = align_up(off + sizeof(int), 256);
     o_s = off;  off = align_up(off + kMfSinkFloats * sizeof(float), 256);
   }
   if (ws) {
@@ -2420,10 +2512,7 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
     }
     ws->row_stat = reinterpret_cast<Stat*>(base + o_rst);
     ws->e_buf = reinterpret_cast<uint16_t*>(base + o_e);
-    ws->xkey = resident_ws ? reinterpret_cast<uint64_t*>(base + o_x) : nullptr;
-    ws->xwin = resident_ws ? reinterpret_cast<uint64_t*>(base + o_w) : nullptr;
     ws->stat_part = resident_ws ? reinterpret_cast<Stat*>(base + o_sp) : nullptr;
-    ws->fail = resident_ws ? reinterpret_cast<int*>(base + o_f) : nullptr;
     ws->sink = resident_ws ? reinterpret_cast<float*>(base + o_s) : nullptr;
   }
   return off;
@@ -2435,9 +2524,15 @@ struct DeviceInfo {
   bool resident_ok;   // one 512-thread workgroup with kResLdsBytes of LDS fits on every CU
   bool mfma_ok;       // the same for the MFMA resident kernel
   int cus;
+  ResExchange* exchange;   // device address of this device's g_exchange
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
+
+// Reads of an exchange word before a resident kernel's wait expires (set by
+// dspark_set_wait_limit; taken at each call, so a captured graph keeps the
+// value of its capture).
+unsigned g_wait_limit = kDefaultWaitLimit;
 
 template <int RB, bool kBf16>
 bool prepare_resident_kernel() {
@@ -2480,6 +2575,11 @@ int init_device() {
   bool mok = cus > 0 && cus <= kResMaxCUs;
   mok = mok && prepare_mfma_kernel<false, false>() && prepare_mfma_kernel<true, false>();
   mok = mok && prepare_mfma_kernel<false, true>() && prepare_mfma_kernel<true, true>();
+  // the device's own copy of the exchange state: its address from the symbol
+  // (the name itself is no device address in host code)
+  void* ex = nullptr;
+  if (hipGetSymbolAddress(&ex, HIP_SYMBOL(g_exchange)) != hipSuccess || ex == nullptr) return DSPARK_ERR_HIP;
+  info.exchange = static_cast<ResExchange*>(ex);
   info.cus = cus;
   info.resident_ok = ok;
   info.mfma_ok = mok;
@@ -2523,6 +2623,7 @@ struct Plan {
   int chunk_cols;
   int G;
   int slice;
+  ResExchange* exchange;
 };
 
 int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
@@ -2535,6 +2636,7 @@ int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
   if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
   const DeviceInfo& info = g_devices[dev];
   plan->G = info.cus;
+  plan->exchange = info.exchange;
   plan->slice = info.cus > 0 ? ((V + info.cus - 1) / info.cus + 7) / 8 * 8 : 0;
   // resident path: all positions in one persistent launch with W kept on chip
   plan->resident = !explicit_chunk && info.resident_ok && B <= kResRowsMax && r <= kResRank &&
@@ -2580,7 +2682,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   const int n_chunks = plan.n_chunks;
   const int G = plan.G;
   const int slice = plan.slice;
-  const int n_launches = resident ? 3 : in_kernel_pick ? K + 1 : 2 * K + 1;
+  const int n_launches = resident ? 2 : in_kernel_pick ? K + 1 : 2 * K + 1;
   if (events && n_events < n_launches + 1) return DSPARK_ERR_ARG;
 
   Workspace ws;
@@ -2595,19 +2697,17 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   const bool bf16 = base_dtype == DSPARK_BF16;
 
   if (resident) {
-    const int n_clear = plan.resident_mfma ? 2 * G * kMfRowsMax + 2 * kMfRowsMax + kMfZeroWords : 2 * G * kResRowsMax;
-    hipLaunchKernelGGL(res_clear, dim3((n_clear + 4095) / 4096), dim3(kThreads), 0, stream, ws.xkey, n_clear,
-                       ws.fail);
-    if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
     const dim3 grid(G);
     if (plan.resident_mfma) {
       MfArgs ma;
       ma.base = base; ma.E = E; ma.W = W; ma.prev_token = prev_token; ma.seed = seed; ma.offset = offset;
       ma.temperature = temperature; ma.n_real = n_real; ma.logits = logits; ma.tokens = tokens;
-      ma.xrow = ws.xkey; ma.xwin = ws.xkey + (size_t)2 * G * kMfRowsMax; ma.stat_part = ws.stat_part;
-      ma.fail = ws.fail; ma.sink = ws.sink; ma.zeros = ma.xwin + 2 * kMfRowsMax;
+      ma.ex = plan.exchange; ma.stat_part = ws.stat_part; ma.sink = ws.sink;
+      ma.xrow = &plan.exchange->xrow[0][0][0];   // host arithmetic on the device address
+      ma.xwin = &plan.exchange->xwin[0][0];
+      ma.zeros = plan.exchange->zeros;
       ma.B = B; ma.K = K; ma.V = V; ma.r = r; ma.slice = slice;
-      ma.spin_limit = 1u << 20;
+      ma.spin_limit = g_wait_limit;
       const dim3 mblock(kMfThreads);
       // columns come in whole tiles of 16 unless the vocabulary is ragged
       const bool ragged = V % 16 != 0;
@@ -2623,9 +2723,9 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
       ResArgs ra;
       ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
       ra.temperature = temperature; ra.n_real = n_real; ra.logits = logits; ra.tokens = tokens;
-      ra.xkey = ws.xkey; ra.stat_part = ws.stat_part; ra.fail = ws.fail;
+      ra.ex = plan.exchange; ra.stat_part = ws.stat_part;
       ra.B = B; ra.K = K; ra.V = V; ra.r = r; ra.slice = slice;
-      ra.spin_limit = 1u << 20;
+      ra.spin_limit = g_wait_limit;
       const dim3 block(kResThreads);
       if (B == 1) {
         if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, true>), grid, block, kResLdsBytes, stream, ra);
@@ -2809,7 +2909,7 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&pick_and_gather),
       reinterpret_cast<const void*>(&proposal_softmax<kPropVecSmall>),
       reinterpret_cast<const void*>(&proposal_softmax<kPropVecLarge>),
-      reinterpret_cast<const void*>(&res_clear),
+      reinterpret_cast<const void*>(&res_status),
       reinterpret_cast<const void*>(&verify_partials<1>),
       reinterpret_cast<const void*>(&verify_partials<2>),
       reinterpret_cast<const void*>(&verify_partials<4>),
@@ -2904,7 +3004,6 @@ int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds) {
     ++n;
   };
   if (plan.resident || plan.resident_mfma) {
-    put(DSPARK_LAUNCH_CLEAR);
     put(DSPARK_LAUNCH_RESIDENT_BLOCK);
   } else {
     for (int k = 0; k < K; ++k) {
@@ -2914,6 +3013,25 @@ int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds) {
   }
   put(DSPARK_LAUNCH_PROPOSAL);
   return n;
+}
+
+unsigned dspark_set_wait_limit(unsigned reads) {
+  const unsigned prev = dspark::g_wait_limit;
+  dspark::g_wait_limit = reads;
+  return prev;
+}
+
+int dspark_block_status(int32_t* status, void* stream) {
+  using namespace dspark;
+  if (!status) return DSPARK_ERR_ARG;
+  const int rc = init_device();
+  if (rc != DSPARK_OK) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSPARK_ERR_HIP;
+  const DeviceInfo& info = g_devices[dev];
+  hipLaunchKernelGGL(res_status, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), info.exchange,
+                     (unsigned)info.cus, status);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
 }
 
 const char* dspark_status_string(int status) {

@@ -10,8 +10,9 @@
 // heads share one key/value head. Outputs o (float32) and the log-sum-exp
 // (natural log) of every (position, query head).
 //
-// The pages lower this as a causal window decode plus a log-sum-exp merge of
-// the later block keys, because their attention kernel only windows causally.
+// On the pages' hardware this runs as a causal sliding-window decode whose
+// log-sum-exp is then merged with the keys of the rest of the block, since
+// their attention kernel has only a causal window.
 // Here the two-sided window is computed directly: one pass over the key
 // range [max(0, P - W + 1), P + K), split over workgroups, each query
 // masking its own lower bound; the splits are then combined by the same

@@ -5,9 +5,9 @@ arithmetic, so both the CPU oracle's tests and the GPU path's tests and
 benchmark can use it without sharing any part of the method.
 
 The workloads stand in for the drafting-alone measurement of the pages
-("Brings DSpark drafting ... B x 7 x 200064 logits, rank-256 Markov head",
-page "brb-nv/TensorRT-LLM pull 27", section "Commits 1-2: fixed-shape
-decode", drafting-alone table). No dataset or trained weight is needed: the
+(batches of seven draft positions over a 200064-token vocabulary with a
+rank-256 Markov head; page "brb-nv/TensorRT-LLM pull 27", section "Commits
+1-2: fixed-shape decode", drafting-alone table). No dataset or trained weight is needed: the
 sampler moves the same bytes whatever the values are.
 
 Draw order inside one workload (one ``numpy.random.default_rng(data_seed)``):
@@ -201,7 +201,7 @@ def mixed_batch(**kw) -> Workload:
 
 
 def large_padded(**kw) -> Workload:
-    """B=96 launched, 88 real: f32 base ~N(0,3^2); padding rows draw from the bias alone; T=1."""
+    """B=96 launched, 88 real: f32 base ~N(0,3^2); padding rows sample from the Markov bias only; T=1."""
     args = dict(B=96, K=DRAFT_LEN, V=VOCAB, r=RANK, base_dtype=F32, base_std=3.0, ew_std=0.02,
                 data_seed=7, temperature=1.0, n_real=88)
     args.update(kw)

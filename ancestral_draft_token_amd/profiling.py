@@ -1,16 +1,21 @@
 """Turn rocprofv3 outputs into the short summaries kept under profiles/.
 
-Two summaries:
+Three summaries:
   * kernel_summary(): per-kernel call counts and durations from a
     ``--kernel-trace --stats -f csv`` run (the ``*_kernel_stats.csv`` file);
   * traffic_summary(): HBM bytes per dispatch from two ``--pmc`` runs
     (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch), each scaled by
     what the same counter reads for a plain device copy of known size that
-    ``bench.py --pmc-run`` launches first.
+    ``bench.py --pmc-run`` launches first;
+  * counter_summary(): the median per dispatch of the dominant kernel for
+    every counter of one or more ``--pmc`` runs (shader sequencer counters:
+    wave cycles, waits, VALU and matrix-core activity), with the ratios that
+    follow from them.
 
 Usage (from the repository root, after the rocprofv3 runs):
   python -m ancestral_draft_token_amd.profiling kernels <stats.csv> <out.md> <command...>
   python -m ancestral_draft_token_amd.profiling traffic <fetch.csv> <write.csv> <workload> <mall> <out.json> <command...>
+  python -m ancestral_draft_token_amd.profiling counters <out.md> <workload> <pmc.csv>[,<pmc.csv>...] <command...>
 """
 
 from __future__ import annotations
@@ -99,10 +104,55 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, mall: str, ou
     return rec
 
 
+RATIOS = [
+    # (name, numerator, denominator, what it says)
+    ("VALU active / wave cycles", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES",
+     "share of a wave's cycles spent issuing VALU instructions"),
+    ("waiting / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES",
+     "share of a wave's cycles spent waiting (s_waitcnt, barriers, dependencies)"),
+    ("waiting on s_waitcnt / wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES",
+     "share spent waiting for a memory or LDS result"),
+    ("LDS bank conflicts / LDS active", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+     "share of LDS-active cycles lost to bank conflicts"),
+]
+
+
+def counter_summary(out_md: str, workload: str, csvs, command: str = "") -> dict:
+    """Median per dispatch of every counter of the dominant kernel, over the runs given."""
+    med = {}
+    disp = 0
+    for path in csvs:
+        names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
+        for c in names:
+            vals = [v for _, n, v in _per_dispatch(path, c) if DOMINANT in n]
+            if vals:
+                med[c] = statistics.median(vals)
+                disp = max(disp, len(vals))
+    lines = ["# rocprofv3 counter summary", "", f"command: `{command}`", "",
+             f"source sha256[:16] of csrc/dspark.hip: {source_hash()}", "",
+             f"workload: {workload}; kernel: {DOMINANT}; dispatches: {disp}; "
+             "values are the median per dispatch, summed over the device", "",
+             "| counter | per dispatch |", "|---|---|"]
+    for c, v in sorted(med.items()):
+        lines.append(f"| {c} | {v:.6g} |")
+    lines += ["", "| ratio | value | meaning |", "|---|---|---|"]
+    ratios = {}
+    for name, num, den, what in RATIOS:
+        if num in med and den in med and med[den] > 0:
+            ratios[name] = med[num] / med[den]
+            lines.append(f"| {name} | {ratios[name]:.3f} | {what} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return {"counters": med, "ratios": ratios}
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "kernels":
         kernel_summary(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic_summary(*sys.argv[2:7], command=" ".join(sys.argv[7:])), indent=1))
+    elif sys.argv[1] == "counters":
+        print(json.dumps(counter_summary(sys.argv[2], sys.argv[3], sys.argv[4].split(","),
+                                         command=" ".join(sys.argv[5:])), indent=1))
     else:
         raise SystemExit(__doc__)

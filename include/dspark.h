@@ -41,10 +41,20 @@
  * failed check returns a negative status and enqueues nothing. A failed
  * kernel launch returns DSPARK_ERR_HIP. No C++ exception crosses the ABI.
  * Device data never causes an error: an out-of-range prev_token is clamped
- * into [0, V), and the drawn token is always in [0, V).
+ * into [0, V), and a drawn token is always in [0, V).
+ *
+ * Device waits (resident plans, see dspark_launch_plan): one persistent
+ * launch runs the whole block, one workgroup per compute unit, and the
+ * workgroups exchange each position's argmax partials through the library's
+ * own device memory. This needs every compute unit of the device free for
+ * the launch: no other kernel may hold a compute unit while it runs, and two
+ * such calls must never run at the same time on one device (calls ordered on
+ * one stream are fine). The waits are bounded: if one expires (a compute unit
+ * was held elsewhere), the positions from the one that failed on get token -1
+ * and NaN proposals, and dspark_block_status reports it. Nothing hangs.
  *
  * Concurrency: calls on different streams must use different workspaces
- * and outputs.
+ * and outputs, and resident calls must not overlap (above).
  */
 #ifndef DSPARK_H_
 #define DSPARK_H_
@@ -144,7 +154,7 @@ typedef enum {
     DSPARK_LAUNCH_FUSED_POSITION = 0,  /* markov_bias_gumbel_argmax for one position */
     DSPARK_LAUNCH_PICK = 1,            /* pick_and_gather for one position */
     DSPARK_LAUNCH_PROPOSAL = 2,        /* proposal_softmax for the whole block */
-    DSPARK_LAUNCH_CLEAR = 3,           /* clears the exchange words of the resident block */
+    DSPARK_LAUNCH_CLEAR = 3,           /* reserved (no plan uses it) */
     DSPARK_LAUNCH_RESIDENT_BLOCK = 4   /* markov_bias_gumbel_argmax for all K positions at once */
 } dspark_launch_kind_t;
 
@@ -152,18 +162,38 @@ typedef enum {
  * sizes, in order: writes up to max_kinds dspark_launch_kind_t values to
  * `kinds` (host memory, may be NULL) and returns the launch count, or a
  * negative status. Three plans exist:
- *   - resident (r <= 256, V <= 2^18, V <= 784 x the device's CU count, and
- *     B <= 128): CLEAR, RESIDENT_BLOCK, PROPOSAL. One persistent launch runs
- *     all K positions; each workgroup keeps its slice of W on chip for the
- *     block (B <= 4: a VALU GEMV with 512 threads; 4 < B <= 128: bf16 MFMA
- *     tiles with 256 threads). It needs every workgroup resident at once (one
- *     per compute unit); its device-side waits are bounded, and if one
- *     expires the call's tokens are -1 instead of hanging.
+ *   - resident (r <= 256, V <= 2^18, V <= 784 x the device's CU count, at
+ *     most 512 CUs, and B <= 128): RESIDENT_BLOCK, PROPOSAL. One persistent
+ *     launch runs all K positions; each workgroup keeps its slice of W on chip
+ *     for the block (B <= 4: a VALU GEMV with 512 threads; 4 < B <= 128: bf16
+ *     MFMA tiles with 256 threads). It needs every workgroup resident at once
+ *     (one per compute unit); its device-side waits are bounded, and if one
+ *     expires the affected tokens are -1 instead of hanging (see "Device
+ *     waits" above and dspark_block_status).
  *   - B == 1 otherwise: K x FUSED_POSITION, PROPOSAL (each fused kernel picks
  *     the previous position's token itself).
  *   - otherwise: K x (FUSED_POSITION, PICK), PROPOSAL.
  * dspark_draft_block_chunked always uses the last two plans. */
 int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds);
+
+/* Whether a bounded device wait of the most recent resident-plan block on the
+ * current device expired. Enqueues one tiny kernel on `stream` that writes
+ * 1 (a wait expired: that block's tokens from the failed position on are -1
+ * and their proposals NaN) or 0 (it did not, or no resident block has run on
+ * the device) into *status, a DEVICE int32. Enqueue it on the stream of the
+ * block it reports on, after the block; graph-capturable. Plans without
+ * device waits (per-position plans) cannot fail this way and do not change
+ * it. Returns DSPARK_ERR_ARG for a null pointer, DSPARK_ERR_HIP if the launch
+ * fails, else DSPARK_OK. */
+int dspark_block_status(int32_t* status, void* stream);
+
+/* Sets how many times a resident kernel reads an exchange word before its wait
+ * expires, for the calls made after it (a captured graph keeps the value in
+ * force at its capture); returns the previous value. The default, 2^20 reads,
+ * is about a second. 0 makes every wait expire at once without reading, which
+ * is how the failure path is tested. Process-wide, not thread-safe against
+ * concurrent calls. */
+unsigned dspark_set_wait_limit(unsigned reads);
 
 /* Standard token-level verification of a draft block ("brb-nv/TensorRT-LLM
  * pull 21", section "2. Golden sampling semantics": rejection_sample_method

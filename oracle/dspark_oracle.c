@@ -8,18 +8,20 @@
  *
  * Sources (page titles as on the pages):
  *  - "brb-nv/TensorRT-LLM pull 21", section "2. Golden sampling semantics":
- *    position k is drawn from softmax((base_k + bias(d_{k-1})) / T), with
- *    d_{k-1} the token drawn before it; drafts use the temperature only;
- *    greedy requests draft the argmax chain; the distribution each draft was
- *    drawn from is stored as its proposal.
+ *    the law of a draft block (every position is sampled from the
+ *    temperature-scaled softmax of its biased logits, where the bias depends
+ *    on the token sampled one position earlier); temperature is the only
+ *    transformation applied to draft logits; a greedy request takes the
+ *    argmax at every position; what a draft was sampled from is kept as its
+ *    proposal distribution.
  *  - "brb-nv/TensorRT-LLM pull 27", section "2. One fused kernel per draft
- *    position": the Markov bias is added, the logits are scaled by 1/T, the
- *    token is the argmax of the scaled logits plus Gumbel noise; the noise is
- *    a counter-based Philox stream keyed by the request's (seed, offset) slot
- *    and the position; the drafter logits are read as f32 or bf16 and the
- *    biased logits are kept in float32; the proposal q_k = softmax(logits_k/T)
- *    is recomputed from those float32 logits exactly as the draw used them;
- *    CUDA-graph padding rows draw from the bias alone.
+ *    position": the rank-r Markov bias added to the drafter logits, the
+ *    1/T scaling, Gumbel-max sampling with counter-based Philox noise keyed
+ *    per request slot (seed, offset) and per position, drafter logits in
+ *    float32 or bfloat16 with the biased logits kept in float32, the
+ *    proposal written after the block from those same float32 logits with
+ *    the scaled values reproduced exactly, and graph-padding rows sampled
+ *    from the bias term only.
  *  - Philox4x32-10: Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
  *    As Easy as 1, 2, 3", SC'11, section 3 (the Philox round and key schedule).
  *

@@ -4,8 +4,9 @@ Criteria (the sampler's stated pass bar):
   * float32 logits within 2e-3 absolute of the oracle's, every entry;
   * q within 1e-6 absolute of the oracle's q (check A) and of the double
     softmax of the checked path's own float32 logits scaled by float32(1/T)
-    (check B: "the stored proposal equals the softmax of the float32 biased
-    logits", "brb-nv/TensorRT-LLM pull 27", section "Test Coverage");
+    (check B: the pages test that the proposal is exactly the softmax of the
+    float32 biased logits, "brb-nv/TensorRT-LLM pull 27", section "Test
+    Coverage");
     greedy rows must be exactly one-hot at their token;
   * tokens identical wherever the oracle's top-2 score margin exceeds 1e-4.
 

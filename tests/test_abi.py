@@ -114,6 +114,20 @@ def test_empty_block_enqueues_nothing(lib):
     assert call(K=0, tokens=None, logits_f32=None, draft_probs=None, workspace=None) == adt.DSPARK_OK
 
 
+def test_block_status_checks_its_pointer(lib):
+    assert lib.dspark_block_status(None, None) == adt.DSPARK_ERR_ARG
+
+
+def test_wait_limit_round_trip(lib):
+    prev = adt.dspark_set_wait_limit(5)
+    try:
+        assert prev == 1 << 20
+        assert adt.dspark_set_wait_limit(7) == 5
+    finally:
+        adt.dspark_set_wait_limit(prev)
+    assert adt.dspark_set_wait_limit(prev) == prev
+
+
 def test_binding_raises_on_error(lib):
     with pytest.raises(adt.DSparkError):
         call(V=4100, check=True)

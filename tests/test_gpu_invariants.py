@@ -1,6 +1,6 @@
 """GPU properties the pages test: graph replay equals the eager call, a new offset
-draws anew, identical inputs give identical outputs, and the drafter's logits
-are left as they are ("brb-nv/TensorRT-LLM pull 27", section "Test Coverage")."""
+draws anew, identical inputs give identical outputs, and the base logits
+buffer is never written ("brb-nv/TensorRT-LLM pull 27", section "Test Coverage")."""
 
 from __future__ import annotations
 

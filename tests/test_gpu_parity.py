@@ -1,10 +1,9 @@
 """GPU path vs the CPU oracle, through the C ABI.
 
-Small cases compare every output entry; the full-size workloads (V = 200064,
-r = 256, the launch configuration the benchmark times) run every row on the
-GPU and compare sampled rows with the oracle at full width, plus properties
-that hold for every row (legal tokens, rows of q summing to 1, one-hot greedy
-proposals).
+Small cases and the full-size workloads (V = 200064, r = 256, in the launch
+configuration the benchmark times) compare every output entry of every row
+with the oracle, plus properties that hold for every row (legal tokens, rows
+of q summing to 1, one-hot greedy proposals).
 """
 
 from __future__ import annotations
@@ -70,22 +69,35 @@ def test_prev_token_out_of_range_is_clamped():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads: sampled rows at full width + properties on all rows
+# full-size workloads: every row at full width, in the launch configuration
+# the benchmark times, plus properties that hold for every row
 # ---------------------------------------------------------------------------
 
 FULL = {
-    "b1": (inputs.single_request, [0]),
-    "b8": (inputs.small_batch, [0, 5]),
-    "b44": (inputs.mixed_batch, [0, 1, 43]),
-    "b88": (inputs.large_padded, [0, 87, 88, 95]),
+    "b1": inputs.single_request,
+    "b8": inputs.small_batch,
+    "b44": inputs.mixed_batch,
+    "b88": inputs.large_padded,
+    "b88_nan_padding": lambda: inputs.large_padded(pad_base="nan"),
 }
+
+
+def block_status():
+    import torch
+    from ancestral_draft_token_amd import dspark_block_status
+    st = torch.full((1,), -1, dtype=torch.int32, device="cuda:0")
+    dspark_block_status(st)
+    torch.cuda.synchronize()
+    return int(st.item())
 
 
 @pytest.mark.parametrize("name", list(FULL))
 def test_full_size(name):
-    make, rows = FULL[name]
-    w = make()
+    """Every row and position compared with the oracle (run on all host cores):
+    logits within 2e-3, q within 1e-6, tokens equal outside near-ties."""
+    w = FULL[name]()
     p = run_gpu(w)
+    assert block_status() == 0
     import torch
     tok = p.tokens
     assert bool(((tok >= 0) & (tok < w.V)).all())
@@ -96,11 +108,12 @@ def test_full_size(name):
         gq = p.q[greedy]
         assert bool((gq.gather(-1, tok[greedy].long().unsqueeze(-1)) == 1.0).all())
         assert float(gq.sum()) == float(gq.shape[0] * gq.shape[1])
-    sub, order = w.subset_rows(rows)
-    t, l, q = rows_to_host(p, order)
-    say(f"oracle on rows {list(order)} of {name}")
-    rep = parity.check(sub, t, l, q)
-    say(f"parity ok {name} {rep.as_dict()}")
+    t, l, q = p.outputs()
+    del p
+    torch.cuda.empty_cache()
+    say(f"oracle on all {w.B} rows of {name}")
+    rep = parity.check(w, t, l, q)
+    say(f"parity ok {name} (every row) {rep.as_dict()}")
 
 
 def test_full_size_padding_rows_ignore_nan_base():
