@@ -25,13 +25,15 @@ DSPARK_ERR_ARG = -1
 DSPARK_ERR_UNSUPPORTED = -2
 DSPARK_ERR_WORKSPACE = -3
 DSPARK_ERR_HIP = -4
+DSPARK_ERR_SCRATCH = -5
 
 EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_launch_plan",
             "dspark_status_string", "dspark_verify_workspace_bytes", "dspark_verify_standard",
             "dspark_verify_block_workspace_bytes", "dspark_verify_block",
             "dspark_window_attention_workspace_bytes", "dspark_window_block_attention",
-            "dspark_block_status", "dspark_set_wait_limit")
+            "dspark_block_status", "dspark_set_wait_limit",
+            "dspark_draft_block_noalloc", "dspark_noalloc_scratch_bytes")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
                 4: "markov_bias_gumbel_argmax"}
@@ -89,6 +91,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_block_status.restype = I
     lib.dspark_set_wait_limit.argtypes = [ctypes.c_uint]
     lib.dspark_set_wait_limit.restype = ctypes.c_uint
+    lib.dspark_draft_block_noalloc.argtypes = block_args + [P, P, P, P]
+    lib.dspark_draft_block_noalloc.restype = I
+    lib.dspark_noalloc_scratch_bytes.argtypes = []
+    lib.dspark_noalloc_scratch_bytes.restype = Z
     _lib = lib
     return lib
 
@@ -163,6 +169,24 @@ def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, off
     if check and rc != DSPARK_OK:
         raise DSparkError(rc, where)
     return rc
+
+
+def dspark_draft_block_noalloc(base_logits, base_dtype: int, E, W, prev_token, seed, offset, temperature,
+                               n_real, B: int, K: int, V: int, r: int, tokens, logits_f32, draft_probs,
+                               stream=None, check: bool = True) -> int:
+    """Enqueue one draft block without a workspace (the library's static
+    scratch); arguments as in ``include/dspark.h``."""
+    rc = load_library().dspark_draft_block_noalloc(
+        _ptr(base_logits), int(base_dtype), _ptr(E), _ptr(W), _ptr(prev_token), _ptr(seed), _ptr(offset),
+        _ptr(temperature), _ptr(n_real), int(B), int(K), int(V), int(r), _ptr(tokens), _ptr(logits_f32),
+        _ptr(draft_probs), _stream_ptr(stream))
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_draft_block_noalloc")
+    return rc
+
+
+def dspark_noalloc_scratch_bytes() -> int:
+    return int(load_library().dspark_noalloc_scratch_bytes())
 
 
 def dspark_block_status(status, stream=None, check: bool = True) -> int:

@@ -2518,6 +2518,13 @@ inline size_t workspace_layout(int B, int K, int V, int r, Workspace* ws, char* 
   return off;
 }
 
+// Scratch of dspark_draft_block_noalloc, for callers that cannot allocate
+// device memory: one copy per device, held until the process ends. Host code
+// uses only the device address hipGetSymbolAddress gives for it (set-up, once
+// per device); the name itself is a host-side stand-in, not a device address.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // Per-device facts the resident path needs (filled by dspark_init).
 struct DeviceInfo {
   bool ready;
@@ -2525,6 +2532,7 @@ struct DeviceInfo {
   bool mfma_ok;       // the same for the MFMA resident kernel
   int cus;
   ResExchange* exchange;   // device address of this device's g_exchange
+  unsigned char* scratch;  // device address of this device's scratch
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_devices[kMaxDevices];
@@ -2580,6 +2588,9 @@ int init_device() {
   void* ex = nullptr;
   if (hipGetSymbolAddress(&ex, HIP_SYMBOL(g_exchange)) != hipSuccess || ex == nullptr) return DSPARK_ERR_HIP;
   info.exchange = static_cast<ResExchange*>(ex);
+  void* sc = nullptr;
+  if (hipGetSymbolAddress(&sc, HIP_SYMBOL(scratch)) != hipSuccess || sc == nullptr) return DSPARK_ERR_HIP;
+  info.scratch = static_cast<unsigned char*>(sc);
   info.cus = cus;
   info.resident_ok = ok;
   info.mfma_ok = mok;
@@ -2624,6 +2635,7 @@ struct Plan {
   int G;
   int slice;
   ResExchange* exchange;
+  unsigned char* scratch;
 };
 
 int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
@@ -2637,6 +2649,7 @@ int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
   const DeviceInfo& info = g_devices[dev];
   plan->G = info.cus;
   plan->exchange = info.exchange;
+  plan->scratch = info.scratch;
   plan->slice = info.cus > 0 ? ((V + info.cus - 1) / info.cus + 7) / 8 * 8 : 0;
   // resident path: all positions in one persistent launch with W kept on chip
   plan->resident = !explicit_chunk && info.resident_ok && B <= kResRowsMax && r <= kResRank &&
@@ -2653,12 +2666,46 @@ int make_plan(int B, int K, int V, int r, int chunk_cols, Plan* plan) {
   return DSPARK_OK;
 }
 
+// The workspace one call needs for its own plan only (the no-allocation entry
+// point lays it out in the scratch array): a resident plan needs the
+// per-workgroup statistics [K][B][G] and the sink, a per-position plan its
+// chunk partials (double-buffered), row statistics and embedding rows.
+inline size_t plan_layout(const Plan& plan, int B, int K, int r, Workspace* ws, char* base) {
+  size_t off = 0;
+  size_t o_key[2] = {0, 0}, o_pst[2] = {0, 0}, o_rst = 0, o_e = 0, o_sp = 0, o_s = 0;
+  if (plan.resident || plan.resident_mfma) {
+    o_sp = off; off = align_up(off + (size_t)K * B * plan.G * sizeof(Stat), 256);
+    o_s = off;  off = align_up(off + kMfSinkFloats * sizeof(float), 256);
+  } else {
+    for (int i = 0; i < 2; ++i) {
+      o_key[i] = off; off = align_up(off + (size_t)B * plan.n_chunks * sizeof(uint64_t), 256);
+      o_pst[i] = off; off = align_up(off + (size_t)B * plan.n_chunks * sizeof(Stat), 256);
+    }
+    o_rst = off; off = align_up(off + (size_t)B * K * sizeof(Stat), 256);
+    o_e = off;   off = align_up(off + (size_t)B * r * sizeof(uint16_t), 256);
+  }
+  if (ws) {
+    const bool res = plan.resident || plan.resident_mfma;
+    for (int i = 0; i < 2; ++i) {
+      ws->part_key[i] = res ? nullptr : reinterpret_cast<uint64_t*>(base + o_key[i]);
+      ws->part_stat[i] = res ? nullptr : reinterpret_cast<Stat*>(base + o_pst[i]);
+    }
+    ws->row_stat = res ? nullptr : reinterpret_cast<Stat*>(base + o_rst);
+    ws->e_buf = res ? nullptr : reinterpret_cast<uint16_t*>(base + o_e);
+    ws->stat_part = res ? reinterpret_cast<Stat*>(base + o_sp) : nullptr;
+    ws->sink = res ? reinterpret_cast<float*>(base + o_s) : nullptr;
+  }
+  return off;
+}
+
+// workspace == nullptr with use_scratch: the call lays its workspace out in the
+// device's scratch array (dspark_draft_block_noalloc).
 int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const uint16_t* W,
                      const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
                      const float* temperature, const int32_t* n_real, int B, int K, int V, int r,
                      int chunk_cols, int32_t* tokens, float* logits, float* q, void* workspace,
                      size_t workspace_bytes, void* stream_ptr, void* const* events = nullptr,
-                     int n_events = 0) {
+                     int n_events = 0, bool use_scratch = false) {
   int rc = check_sizes(B, K, V, r);
   if (rc != DSPARK_OK) return rc;
   if (base_dtype != DSPARK_F32 && base_dtype != DSPARK_BF16) return DSPARK_ERR_ARG;
@@ -2671,12 +2718,15 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
     return DSPARK_ERR_ARG;
   if (!aligned16(base) || !aligned16(E) || !aligned16(W) || !aligned16(logits) || !aligned16(q))
     return DSPARK_ERR_ARG;
-  const size_t need = workspace_layout(B, K, V, r, nullptr, nullptr);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+  if (!use_scratch) {
+    const size_t need = workspace_layout(B, K, V, r, nullptr, nullptr);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+  }
 
   Plan plan;
   rc = make_plan(B, K, V, r, explicit_chunk ? chunk_cols : 0, &plan);
   if (rc != DSPARK_OK) return rc;
+  if (use_scratch && plan_layout(plan, B, K, r, nullptr, nullptr) > kScratchBytes) return DSPARK_ERR_SCRATCH;
   const bool resident = plan.resident || plan.resident_mfma;
   const bool in_kernel_pick = plan.in_kernel_pick;
   const int n_chunks = plan.n_chunks;
@@ -2686,7 +2736,10 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   if (events && n_events < n_launches + 1) return DSPARK_ERR_ARG;
 
   Workspace ws;
-  workspace_layout(B, K, V, r, &ws, static_cast<char*>(workspace));
+  if (use_scratch)
+    plan_layout(plan, B, K, r, &ws, reinterpret_cast<char*>(plan.scratch));
+  else
+    workspace_layout(B, K, V, r, &ws, static_cast<char*>(workspace));
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   int n_marks = 0;
   auto mark = [&]() -> bool {
@@ -2968,6 +3021,17 @@ int dspark_draft_block(const void* base_logits, int base_dtype, const uint16_t* 
                                   workspace_bytes, stream);
 }
 
+int dspark_draft_block_noalloc(const void* base_logits, int base_dtype, const uint16_t* E, const uint16_t* W,
+                               const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+                               const float* temperature, const int32_t* n_real, int B, int K, int V, int r,
+                               int32_t* tokens, float* logits_f32, float* draft_probs, void* stream) {
+  return dspark::draft_block_impl(base_logits, base_dtype, E, W, prev_token, seed, offset, temperature,
+                                  n_real, B, K, V, r, 0, tokens, logits_f32, draft_probs, nullptr, 0, stream,
+                                  nullptr, 0, /*use_scratch=*/true);
+}
+
+size_t dspark_noalloc_scratch_bytes(void) { return dspark::kScratchBytes; }
+
 int dspark_draft_block_chunked(const void* base_logits, int base_dtype, const uint16_t* E,
                                const uint16_t* W, const int32_t* prev_token, const int64_t* seed,
                                const int64_t* offset, const float* temperature, const int32_t* n_real,
@@ -3041,6 +3105,7 @@ const char* dspark_status_string(int status) {
     case DSPARK_ERR_UNSUPPORTED: return "unsupported size (V % 8, r % 32, r > 1024, K > 255, chunk)";
     case DSPARK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case DSPARK_ERR_HIP: return "HIP runtime error";
+    case DSPARK_ERR_SCRATCH: return "sizes need more scratch than dspark_draft_block_noalloc's static buffer holds";
     default: return "unknown status";
   }
 }

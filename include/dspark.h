@@ -76,7 +76,8 @@ typedef enum {
     DSPARK_ERR_ARG = -1,          /* null pointer, bad size, misaligned pointer, bad dtype */
     DSPARK_ERR_UNSUPPORTED = -2,  /* V % 8 != 0, r % 32 != 0, r > 1024, K > 255, ... */
     DSPARK_ERR_WORKSPACE = -3,    /* workspace missing or smaller than dspark_workspace_bytes */
-    DSPARK_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+    DSPARK_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+    DSPARK_ERR_SCRATCH = -5       /* dspark_draft_block_noalloc: the call needs more than its static scratch */
 } dspark_status_t;
 
 /* Loads the kernels on the current device. Call once per device before any
@@ -116,6 +117,31 @@ int dspark_draft_block(
     int B, int K, int V, int r,
     int32_t* tokens, float* logits_f32, float* draft_probs,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same block for callers that cannot allocate device memory (code under
+ * stream capture that may not allocate, tight serving loops, harnesses that
+ * forbid it): no workspace argument; the call lays out the scratch its plan
+ * needs in a static device array the library holds, one per device, of
+ * dspark_noalloc_scratch_bytes() bytes (8 MiB), taken when the device is first
+ * used and kept until the process ends. Arguments, outputs, launches and
+ * results are those of dspark_draft_block (the same kernels). A call whose plan
+ * needs more scratch than that returns DSPARK_ERR_SCRATCH and enqueues
+ * nothing: the resident plans need 8 K B x (compute units) + 4 KB (on 256 CUs,
+ * B K <= 4094), the per-position plans 32 B ceil(V/128) + 8 B K + 2 B r. Nothing
+ * in the scratch needs to start at zero. Every call on a device shares that
+ * device's array, so calls that overlap on one device (other streams, other
+ * threads) race and give wrong results: enqueue them in order. Allocates
+ * nothing (no hipMalloc, hipFree or allocating library call). */
+int dspark_draft_block_noalloc(
+    const void* base_logits, int base_dtype,
+    const uint16_t* E, const uint16_t* W,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, const int32_t* n_real,
+    int B, int K, int V, int r,
+    int32_t* tokens, float* logits_f32, float* draft_probs, void* stream);
+
+/* Size in bytes of dspark_draft_block_noalloc's static scratch (per device). */
+size_t dspark_noalloc_scratch_bytes(void);
 
 /* The same block with an explicit vocabulary chunking: each workgroup of the
  * fused per-position kernel owns `chunk_cols` consecutive vocabulary columns

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     for code in (adt.DSPARK_OK, adt.DSPARK_ERR_ARG, adt.DSPARK_ERR_UNSUPPORTED,
-                 adt.DSPARK_ERR_WORKSPACE, adt.DSPARK_ERR_HIP):
+                 adt.DSPARK_ERR_WORKSPACE, adt.DSPARK_ERR_HIP, adt.DSPARK_ERR_SCRATCH):
         assert adt.status_string(code) and adt.status_string(code) != "unknown status"
     assert adt.status_string(12345) == "unknown status"
 
@@ -112,6 +112,17 @@ def test_bad_chunking(lib):
 def test_empty_block_enqueues_nothing(lib):
     assert call(B=0, tokens=None, logits_f32=None, draft_probs=None, workspace=None) == adt.DSPARK_OK
     assert call(K=0, tokens=None, logits_f32=None, draft_probs=None, workspace=None) == adt.DSPARK_OK
+
+
+def test_noalloc_host_checks(lib):
+    assert adt.dspark_noalloc_scratch_bytes() == 8 << 20
+    args = dict(base_logits=FAKE, base_dtype=adt.DSPARK_F32, E=FAKE, W=FAKE, prev_token=FAKE, seed=FAKE,
+                offset=FAKE, temperature=FAKE, n_real=None, B=2, K=7, V=4096, r=32, tokens=FAKE,
+                logits_f32=FAKE, draft_probs=FAKE, stream=0, check=False)
+    assert adt.dspark_draft_block_noalloc(**dict(args, V=4100)) == adt.DSPARK_ERR_UNSUPPORTED
+    assert adt.dspark_draft_block_noalloc(**dict(args, E=None)) == adt.DSPARK_ERR_ARG
+    assert adt.dspark_draft_block_noalloc(**dict(args, draft_probs=FAKE + 4)) == adt.DSPARK_ERR_ARG
+    assert adt.dspark_draft_block_noalloc(**dict(args, B=0, tokens=None)) == adt.DSPARK_OK
 
 
 def test_block_status_checks_its_pointer(lib):
