@@ -1498,7 +1498,10 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, uint4 b, f32x4_t c) {
 
 // The bias chain of one LDS M-tile, issued from the epilogue's hooks: step J
 // runs the matrix instruction of K-step J and reads the A fragment of K-step
-// J + 2. Two fragments are in flight, so each read has two stretches of VALU
+// J + 2 into the registers that instruction has just taken as its A operand
+// (A and B are consumed at issue: the compiler's hazard model, which sees
+// these builtins, requires no wait states for that rewrite, only for the
+// accumulator). Two fragments are in flight, so each read has two stretches of VALU
 // work to arrive in (with one in flight a tile carrying an LDS chain took
 // ~1150 cycles against ~780 for a tile whose chain reads registers; with two,
 // ~940). Fences keep the scheduler from gathering the

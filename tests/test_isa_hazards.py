@@ -1,21 +1,34 @@
-"""Checks on the gfx950 assembly of the large-batch (MFMA) kernel.
+"""Checks on the gfx950 assembly of the large-batch (MFMA) kernel, and on the
+compiler's hazard model that its register reuse relies on.
 
 The kernel keeps W resident in registers: 62 of its 64 A-operand fragments
 per lane live in AGPRs for the whole launch, read there by the matrix
 instructions. A build in which the register allocator spilled some of those
-fragments to scratch memory gave bias values that changed from run to run.
-There the spill store of an AGPR tuple was followed two instructions later by
-an AGPR write of the same registers, and the fragments were reloaded inside
-the N-tile loop. This test keeps that configuration out:
+fragments to scratch memory gave bias values that changed from run to run,
+and the fragments were then reloaded inside the N-tile loop. That build can
+no longer be produced (the allocator does not spill them with the current
+source and compiler), and the compiler's hazard model guards the one hazard
+its spill code showed (an AGPR write two instructions after a 16-byte spill
+store of the same registers: the model requires two wait states there, as it
+does for VGPR store data), so its cause is not known. This test keeps that
+configuration out:
 
 * no AGPR is spilled (no scratch store with AGPR data) anywhere in the kernel;
 * no scratch (spill) access sits inside the kernel's inner loops, where the W
   fragments and the per-tile state live (a spill there would also stall every
   tile on the scratch round trip).
 
-A VALU write to a matrix instruction's A or B registers right after it issues
-does not change its result. This was checked on gfx950 with the matrix pipe
-idle and busy, over 5e8 results each, so this test does not restrict it.
+The kernel also overwrites a matrix instruction's A operand with the next
+LDS fragment read right after issuing it (the LDS chains of the epilogue).
+The kernel is written with compiler builtins only, so the backend's hazard
+recognizer, which inserts the wait states the ISA requires between dependent
+instructions, sees every one of those instructions. The tests below run that
+recognizer (llc's post-RA hazard pass for gfx950) on fixed-register
+sequences and pin what it requires after v_mfma_f32_16x16x32_bf16: wait
+states before a VALU write of SrcC or a read of the result, none before a
+VALU or LDS write of SrcA or SrcB (those operands are consumed at issue),
+and two wait states before a write of a 16-byte store's data registers,
+AGPRs included.
 
 The assembly is generated here with the library's own flags (device code only,
 about 15 s); no GPU is needed.
@@ -133,3 +146,56 @@ def test_attention_kernel_has_no_scratch_and_four_waves_per_simd(attn_asm):
     assert md["vgpr"] <= 128, md
     lines = attn_asm[attn_asm.index("wa_partials"):].splitlines()
     assert sum(1 for l in lines[:6000] if "v_mfma_f32_16x16x32_bf16" in l) >= 32
+
+
+# ---- the compiler's hazard model after a matrix instruction ------------------------
+
+LLC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "llc")
+MFMA = ("$vgpr12_vgpr13_vgpr14_vgpr15 = V_MFMA_F32_16X16X32_BF16_vgprcd_e64 $vgpr4_vgpr5_vgpr6_vgpr7, "
+        "$vgpr8_vgpr9_vgpr10_vgpr11, $vgpr0_vgpr1_vgpr2_vgpr3, 0, 0, 0, implicit $mode, implicit $exec")
+ST_AGPR = ("SCRATCH_STORE_DWORDX4_ST $agpr0_agpr1_agpr2_agpr3, 0, 0, implicit $exec, implicit $flat_scr "
+           ":: (store (s128), addrspace 5)")
+ST_VGPR = ("SCRATCH_STORE_DWORDX4_ST $vgpr4_vgpr5_vgpr6_vgpr7, 0, 0, implicit $exec, implicit $flat_scr "
+           ":: (store (s128), addrspace 5)")
+HAZARD_CASES = {
+    # name: (instructions, wait states the recognizer must insert before the last one)
+    "valu_writes_srcC": ([MFMA, "$vgpr0 = V_MOV_B32_e32 $vgpr20, implicit $exec"], "some"),
+    "valu_reads_result": ([MFMA, "$vgpr30 = V_MOV_B32_e32 $vgpr12, implicit $exec"], "some"),
+    "valu_writes_srcA": ([MFMA, "$vgpr4 = V_MOV_B32_e32 $vgpr20, implicit $exec"], 0),
+    "valu_writes_srcB": ([MFMA, "$vgpr8 = V_MOV_B32_e32 $vgpr20, implicit $exec"], 0),
+    "lds_read_writes_srcA": ([MFMA, "$vgpr4_vgpr5_vgpr6_vgpr7 = DS_READ_B128_gfx9 $vgpr20, 0, 0, implicit $exec"], 0),
+    "store_vgpr_data_then_write": ([ST_VGPR, "$vgpr4 = V_MOV_B32_e32 $vgpr20, implicit $exec"], 2),
+    "store_agpr_data_then_write": ([ST_AGPR, "$agpr0 = V_ACCVGPR_WRITE_B32_e64 $vgpr20, implicit $exec"], 2),
+}
+
+
+@pytest.fixture(scope="module")
+def hazard_out(tmp_path_factory) -> str:
+    if not os.path.exists(LLC):
+        pytest.skip("llc not available")
+    lines = ["--- |"] + [f"  define amdgpu_kernel void @{n}() {{ ret void }}" for n in HAZARD_CASES] + ["..."]
+    for n, (ins, _) in HAZARD_CASES.items():
+        lines += ["---", f"name: {n}", "tracksRegLiveness: true", "body: |", "  bb.0:",
+                  "    liveins: $vgpr0_vgpr1_vgpr2_vgpr3, $vgpr4_vgpr5_vgpr6_vgpr7, $vgpr8_vgpr9_vgpr10_vgpr11, "
+                  "$agpr0_agpr1_agpr2_agpr3, $vgpr20"] + ["    " + i for i in ins] + ["    S_ENDPGM 0", "..."]
+    mir = tmp_path_factory.mktemp("hazard") / "cases.mir"
+    mir.write_text("\n".join(lines) + "\n")
+    r = subprocess.run([LLC, "-mtriple=amdgcn-amd-amdhsa", "-mcpu=gfx950", "-run-pass=post-RA-hazard-rec",
+                        "-o", "-", str(mir)], check=True, capture_output=True, text=True)
+    return r.stdout
+
+
+def _wait_states(out: str, name: str) -> int:
+    body = out[out.index(f"name:            {name}"):]
+    body = body[:body.index("S_ENDPGM")]
+    return sum(int(m.group(1)) + 1 for m in re.finditer(r"S_NOP (\d+)", body))
+
+
+@pytest.mark.parametrize("name", list(HAZARD_CASES))
+def test_hazard_model(hazard_out, name):
+    got = _wait_states(hazard_out, name)
+    want = HAZARD_CASES[name][1]
+    if want == "some":
+        assert got > 0, name
+    else:
+        assert got == want, (name, got)
