@@ -316,21 +316,25 @@ struct Base4 {
   float4 f;
 };
 
-// Nontemporal: base logits are read once, and not letting them displace the
-// just-written logits in the Infinity Cache lets the proposal pass re-read
-// more of those from the cache instead of HBM.
+// Nontemporal (kNt): base logits are read once, and not letting them displace
+// the just-written logits in the Infinity Cache lets the proposal pass re-read
+// more of those from the cache instead of HBM. Only where one load instruction
+// covers whole cache lines: a nontemporal read of part of a line does not keep
+// the line for its other parts, which are then fetched again (the large-batch
+// kernel reads 64 or 32 bytes of a 128-byte line per tile, so it loads
+// without the hint: B=88 fetch 734 -> 634 MB, B=44 333 -> 252 MB).
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 
-template <bool kBf16Base>
+template <bool kBf16Base, bool kNt = true>
 __device__ __forceinline__ void load_base4(Base4<kBf16Base>& bv, const void* base, size_t off) {
   if (kBf16Base) {
-    const u32x2_t x =
-        __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(base) + off));
+    const u32x2_t* p = reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(base) + off);
+    const u32x2_t x = kNt ? __builtin_nontemporal_load(p) : *p;
     bv.h = make_uint2(x.x, x.y);
   } else {
-    const f32x4v_t x =
-        __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(static_cast<const float*>(base) + off));
+    const f32x4v_t* p = reinterpret_cast<const f32x4v_t*>(static_cast<const float*>(base) + off);
+    const f32x4v_t x = kNt ? __builtin_nontemporal_load(p) : *p;
     bv.f = make_float4(x.x, x.y, x.z, x.w);
   }
 }
@@ -1948,7 +1952,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   Base4<kBf16Base> bq[kMfTilesMax];
   const unsigned char* bp = lane_base(0, 0);   // base logits of this N-tile's row of the lane
 #pragma unroll
-  for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base>(bq[i], base_at(bp, i), 0);
+  for (int i = 0; i < kMfAhead; ++i) load_base4<kBf16Base, false>(bq[i], base_at(bp, i), 0);
 
   for (int k = 0; k < K; ++k) {
     for (int nt = 0; nt < NT; ++nt) {
@@ -1978,9 +1982,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       acc[0] = tile_bias(0, ef);
 #pragma unroll
       for (int i = 0; i < kMfTilesMax; ++i) {
-        if (i + kMfAhead < kMfTilesMax) load_base4<kBf16Base>(bq[i + kMfAhead], base_at(bp, i + kMfAhead), 0);
+        if (i + kMfAhead < kMfTilesMax) load_base4<kBf16Base, false>(bq[i + kMfAhead], base_at(bp, i + kMfAhead), 0);
         if (i >= kMfNextAt && i < kMfNextAt + kMfAhead)
-          load_base4<kBf16Base>(bq[i - kMfNextAt], base_at(bpn, i - kMfNextAt), 0);
+          load_base4<kBf16Base, false>(bq[i - kMfNextAt], base_at(bpn, i - kMfNextAt), 0);
         // One store per tile, after the branch (to the sink when there is no
         // tile, row or column), keeps the compiler's count of memory
         // operations issued after each prefetch exact; the base registers are
