@@ -112,9 +112,11 @@ RATIOS = [
      "share of a wave's cycles spent waiting (s_waitcnt, barriers, dependencies)"),
     ("waiting on s_waitcnt / wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES",
      "share spent waiting for a memory or LDS result"),
-    ("LDS bank conflicts / LDS active", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
-     "share of LDS-active cycles lost to bank conflicts"),
+    ("LDS bank conflicts / LDS busy", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+     "share of the LDS's busy cycles lost to bank conflicts"),
 ]
+SIMDS = 256 * 4   # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (each counts the shader clock)
 
 
 def counter_summary(out_md: str, workload: str, csvs, command: str = "") -> dict:
@@ -141,6 +143,12 @@ def counter_summary(out_md: str, workload: str, csvs, command: str = "") -> dict
         if num in med and den in med and med[den] > 0:
             ratios[name] = med[num] / med[den]
             lines.append(f"| {name} | {ratios[name]:.3f} | {what} |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE", 0) > 0:
+        ratios["matrix cores busy"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+        lines.append(f"| matrix cores busy | {ratios['matrix cores busy']:.3f} | SQ_VALU_MFMA_BUSY_CYCLES / "
+                     f"(GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs) |")
+    if "SQ_INSTS_MFMA" in med:
+        lines.append(f"| matrix instructions per dispatch | {med['SQ_INSTS_MFMA']:.4g} | v_mfma issued |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return {"counters": med, "ratios": ratios}

@@ -448,7 +448,7 @@ def main():
                 continue
             wo = inputs.WORKLOADS[name]()
             print(f"[bench] also {wo.name}", file=sys.stderr, flush=True)
-            ro = measure(wo, max(10, args.steps // 4), 3, args.mall)
+            ro = measure(wo, max(20, args.steps), max(5, args.warmup), args.mall)
             also[name] = {"workload": wo.name, "us_per_block": round(ro["us_per_block"], 2),
                           "us_median": round(ro["us_median"], 2),
                           "block_roofline_frac": round(ro["block_gbs"] / HBM_PEAK_GBS, 4),
