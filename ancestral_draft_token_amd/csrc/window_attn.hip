@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dspark.h"
 
 namespace dspark_wa {
@@ -381,8 +383,321 @@ __global__ __launch_bounds__(kD) void wa_combine_splits(WaArgs a) {
   if (d == 0) a.lse[orow] = (M + log2f(Ls)) * 0.69314718055994531f;
 }
 
+// ---------------------------------------------------------------------------
+// wa_block: the large-batch form. One 256-thread workgroup (four waves) per
+// (key/value head, row), two per CU (up to 256 registers a lane: two waves
+// per SIMD, so one hides the other's latencies). The key range streams
+// through an LDS ring of kNB tiles of 32 keys, loaded straight from HBM into
+// LDS by LDS-direct loads (no registers), kNB - 1 tiles ahead; each wave
+// loads 8 keys of every tile. The waves split the draft positions (wave w:
+// positions kPos w .. + kPos - 1) and each reads the whole tile from LDS, so
+// a position's softmax and output stay in one wave and no merge is needed:
+//   scores S^T = K Q^T (v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads, 4 steps
+//     over D) for each half of the tile, K rows with their 16-byte chunks
+//     XOR-swizzled by key (the swizzle is applied by choosing each lane's
+//     source chunk);
+//   O^T += V^T P^T over all 32 keys at once (v_mfma_f32_16x16x32_bf16: 16 dims
+//     x 16 heads). The reduction index pairs k = 8 g + 4 h + i with key
+//     16 h + 4 g + i, which is where the score accumulators already hold
+//     P^T (lane (c, g) of half h: keys 16 h + 4 g + i of head c), so they are
+//     the B operand once packed. The A operand (dim 16 dt + c of those 8
+//     keys) comes from two transposing LDS reads ds_read_b64_tr_b16 of the
+//     row-major V tile: lane r of a 16-lane group reads 4 dims of key r / 4
+//     and lane j receives dim j of the group's 4 keys.
+// Online softmax in base 2 per position and head over each 32-key tile, lazy
+// rescale; outputs are normalised and written by the wave that owns them.
+// ---------------------------------------------------------------------------
+constexpr int kBT = 32;                        // keys per tile (each wave loads 8)
+constexpr int kBWaves = 4;
+constexpr int kBThreads = 64 * kBWaves;
+constexpr int kNB = 4;                         // tiles in the LDS ring
+constexpr int kBTile = kBT * kD * 2;           // bytes of one tensor's tile (8 KB)
+constexpr int kBLds = kNB * 2 * kBTile;        // 64 KB
+constexpr long long kBlockMinPairs = 256;      // (row, key/value head) pairs from which wa_block is used
+static_assert(kKMax <= 2 * kBWaves, "positions per wave");
+constexpr int kBRows = kBT / kBWaves;          // key rows each wave loads per tile
+constexpr int kBLoads = 2 * kBRows / 4;        // its LDS-direct loads per tile (K and V, 4 rows each)
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Chunk swizzles of the ring rows (256 bytes, 16 chunks of 16 bytes): logical
+// chunk j of key row r sits at physical chunk j ^ swz(r). K: r % 16, so the
+// 16 rows of a fragment read (one chunk each) hit 16 different chunks. V:
+// 2 (r % 8), so the 4 rows of a transposing read's 16-lane group (a chunk
+// pair each) hit 4 different pairs.
+__device__ __forceinline__ int kswz_b(int r) { return r & 15; }
+__device__ __forceinline__ int vswz_b(int r) { return 2 * (r & 7); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (n < 64)
+#define WA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// One LDS-direct load, 16 bytes a lane: lane i's bytes at gsrc land at LDS
+// byte lds + 16 i (lds wave-uniform, in M0). Written out so that the compiler
+// does not tie later LDS reads to these loads (it would make every read wait
+// for all of them, emptying the ring); the tile loop waits for them itself
+// with vmcnt, which counts them in issue order like any vector memory load.
+// The instruction writes no register; one wait state separates the M0 write
+// from the load that reads it. M0 is declared clobbered, though the compiler
+// reserves it (hence the silenced warning): the kernels of this file make no
+// other use of M0, which tests/test_isa_window_attn.py checks in the
+// generated code.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gsrc, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// max over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes of one head in an
+// MFMA accumulator layout) by two lane-row swaps, no LDS round trip:
+// permlane32_swap(x, x) leaves x[l] in one result and x[l ^ 32] in the other,
+// permlane16_swap(y, y) likewise y[l] and y[l ^ 16]. The results are taken
+// out of the returned pair as scalars before the float reinterpretation
+// (a bit cast of a subscripted element of that vector type reads element 0).
+__device__ __forceinline__ float max_over_heads_lanes(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned a0 = s32[0], a1 = s32[1];
+  const float y = fmaxf(__uint_as_float(a0), __uint_as_float(a1));
+  const unsigned v = __float_as_uint(y);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const unsigned b0 = s16[0], b1 = s16[1];
+  return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
+}
+
+template <int kPos>
+__global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
+  extern __shared__ __align__(16) unsigned char wlds[];          // the ring (kBLds bytes)
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int Hq = a.Hkv * kG;
+  const int P = clamp_ctx(a, b);
+  const int lo0 = P - (a.W - 1) > 0 ? P - (a.W - 1) : 0;
+  const int hi = P + a.K;
+  const size_t rs = (size_t)a.Hkv * kD;                                 // elements between keys
+  const uint16_t* kb = a.kc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
+  const uint16_t* vb = a.vc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
+  const int n_tiles = (hi - lo0 + kBT - 1) / kBT;
+  const int p0 = wv * kPos;                                           // this wave's first position
+  const int np = a.K - p0 < kPos ? a.K - p0 : kPos;                   // its positions (may be <= 0)
+  // slots p >= np repeat position K - 1 (computed, not written): the loop
+  // below runs the same code for every slot
+  int pos[kPos];
+#pragma unroll
+  for (int p = 0; p < kPos; ++p) pos[p] = p0 + p < a.K ? p0 + p : a.K - 1;
+
+  // Query fragments (B operand of the scores): lane (c, g) holds head kvh*16 + c,
+  // dims 32 ds + 8 g .. + 7 of every position of this wave
+  u32x4_t qf[kPos][4];
+#pragma unroll
+  for (int p = 0; p < kPos; ++p) {
+    const uint16_t* qrow = a.q + (((size_t)b * a.K + pos[p]) * Hq + kvh * kG + c) * kD;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) qf[p][ds] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * ds + 8 * g);
+  }
+  // the fragments are in before the ring starts (a wait for them inside the
+  // tile loop would also wait for every tile in flight): an empty use here
+  // makes the compiler wait for them at this point
+#pragma unroll
+  for (int p = 0; p < kPos; ++p)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) asm volatile("" ::"v"(qf[p][ds]));
+
+  // Tile n into ring slot n % kNB: this wave's kBRows keys of K and of V,
+  // 1 KB LDS-direct loads (4 key rows of 256 bytes a load). Lane i of a load
+  // fills physical chunk i % 16 of key row i / 16. A tile's rows sit at the
+  // same offsets in every tile (32 keys: the row swizzles repeat), so each
+  // lane's source addresses step by one tile of keys; the last tile clamps
+  // keys past the range to the last key (masked).
+  const int ph = lane & 15;
+  const uint16_t* gsrc[2][kBRows / 4];                 // [K, V][load] at tile 0
+#pragma unroll
+  for (int i = 0; i < kBRows / 4; ++i) {
+    const int kr = kBRows * wv + 4 * i + (lane >> 4);
+    gsrc[0][i] = kb + (size_t)(lo0 + kr) * rs + 8 * (ph ^ kswz_b(kr));
+    gsrc[1][i] = vb + (size_t)(lo0 + kr) * rs + 8 * (ph ^ vswz_b(kr));
+  }
+  const size_t tile_step = (size_t)kBT * rs;            // elements between tiles
+  auto issue = [&](int n, int slot) {
+    const int tb = lo0 + n * kBT;
+    unsigned char* kbuf = wlds + slot * 2 * kBTile;
+    unsigned char* vbuf = kbuf + kBTile;
+    if (tb + kBT <= hi) {                              // wave-uniform: every key in range
+#pragma unroll
+      for (int i = 0; i < kBRows / 4; ++i) {
+        const int r0 = kBRows * wv + 4 * i;            // first key row of this load
+        lds_dma16(gsrc[0][i] + n * tile_step, kbuf + r0 * 256);
+        lds_dma16(gsrc[1][i] + n * tile_step, vbuf + r0 * 256);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBRows / 4; ++i) {
+        const int r0 = kBRows * wv + 4 * i;
+        const int kr = r0 + (lane >> 4);
+        const int key = tb + kr < hi ? tb + kr : hi - 1;
+        lds_dma16(kb + (size_t)key * rs + 8 * (ph ^ kswz_b(kr)), kbuf + r0 * 256);
+        lds_dma16(vb + (size_t)key * rs + 8 * (ph ^ vswz_b(kr)), vbuf + r0 * 256);
+      }
+    }
+  };
+
+  f32x4_t acc[kPos][8];
+  float m[kPos], l[kPos];
+#pragma unroll
+  for (int p = 0; p < kPos; ++p) {
+    m[p] = -INFINITY;
+    l[p] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[p][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // the largest window start of a position: tiles below it, and the last
+  // tile, need masks
+  const int lo_max = P + a.K - 1 - (a.W - 1);
+  // lane-constant LDS offsets within a tile (the half h adds 16 rows, 4 KB):
+  // K fragment ds of key row c (logical chunk 4 ds + g), and the transposing
+  // V read of dims 16 dt + 4 (c % 4) .. + 3 of key 4 g + c / 4 (logical chunk
+  // 2 dt + (c % 4) / 2, half (c % 2) of it)
+  int kofs[4], vofs[8];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) kofs[ds] = c * 256 + 16 * ((4 * ds + g) ^ kswz_b(c));
+  const int vkr = 4 * g + (c >> 2), vq = c & 3;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) vofs[dt] = vkr * 256 + 16 * ((2 * dt + (vq >> 1)) ^ vswz_b(vkr)) + 8 * (vq & 1);
+
+  // one tile: wait for it, free the oldest slot, compute (slot known at compile time)
+  auto step = [&](int n, auto slot_tag) {
+    constexpr int slot = decltype(slot_tag)::value;
+    // this wave's loads of tile n have landed (the loads of the later tiles in
+    // flight are the newest), then every wave's: the tile is complete and the
+    // slot of tile n - 1 is free for tile n + kNB - 1
+    if (n + kNB - 2 < n_tiles) WA_WAIT_VMCNT(kBLoads * (kNB - 2));
+    else WA_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (n + kNB - 1 < n_tiles) issue(n + kNB - 1, (slot + kNB - 1) % kNB);
+    const int tb = lo0 + n * kBT;
+    const unsigned char* kbuf = wlds + slot * 2 * kBTile;
+    const unsigned char* vbuf = kbuf + kBTile;
+
+    // scores: S^T of each half and position (lane (c, g): keys 16 h + 4 g .. + 3, head c)
+    f32x4_t sc[2][kPos];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4_t kf[4];
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) kf[ds] = *reinterpret_cast<const u32x4_t*>(kbuf + 4096 * h + kofs[ds]);
+#pragma unroll
+      for (int p = 0; p < kPos; ++p) {
+        sc[h][p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) sc[h][p] = mfma_bf16(kf[ds], qf[p][ds], sc[h][p]);
+      }
+    }
+
+    // keys outside a position's range score -inf; a tile wholly below the
+    // range leaves P = 0 and the running state unchanged
+    const bool edge = tb < lo_max || tb + kBT > hi;
+    u32x4_t pb[kPos];
+#pragma unroll
+    for (int p = 0; p < kPos; ++p) {
+      float x[8];                                        // raw <q, k>: half h at 4 h + i
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * h + i] = sc[h][p][i];
+      if (edge) {
+        const int lo_p = P + pos[p] - (a.W - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = tb + 16 * h + 4 * g + i;
+            if (!(key >= lo_p && key < hi)) x[4 * h + i] = -INFINITY;
+          }
+      }
+      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mt = max_over_heads_lanes(mt) * a.scale_log2;
+      if (__any(mt > m[p])) {
+        // some head's running maximum grows: rescale (alpha = 1 for the
+        // others, 0 from the empty start); skipped once the maxima settle
+        const float mn = fmaxf(mt, m[p]);
+        const float alpha = __builtin_amdgcn_exp2f(m[p] - mn);
+        l[p] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[p][dt] *= alpha;
+        m[p] = mn;
+      }
+      const float mref = m[p] == -INFINITY ? 0.0f : m[p];   // no key seen yet: every e is 0
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.scale_log2, -mref));
+        l[p] += e[i];
+      }
+      pb[p] = u32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+    }
+
+    // O^T += V^T P^T: the A operand of dims 16 dt .. + 15 (lane: dim 16 dt + c,
+    // keys 4 g .. + 3 of each half) by one transposing read per half
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      v4i16_t vh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        vh[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vbuf + 4096 * h + vofs[dt]));
+      const u32x4_t va = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int p = 0; p < kPos; ++p) acc[p][dt] = mfma_bf16(va, pb[p], acc[p][dt]);
+    }
+  };
+
+  typedef std::integral_constant<int, 0> S0;
+  typedef std::integral_constant<int, 1> S1;
+  typedef std::integral_constant<int, 2> S2;
+  typedef std::integral_constant<int, 3> S3;
+  static_assert(kNB == 4, "the tile loop below is unrolled over the ring's 4 slots");
+#pragma unroll 1
+  for (int n = 0; n < kNB - 1 && n < n_tiles; ++n) issue(n, n);
+#pragma unroll 1
+  for (int n = 0; n < n_tiles; n += kNB) {
+    step(n, S0{});
+    if (n + 1 >= n_tiles) break;
+    step(n + 1, S1{});
+    if (n + 2 >= n_tiles) break;
+    step(n + 2, S2{});
+    if (n + 3 >= n_tiles) break;
+    step(n + 3, S3{});
+  }
+
+  // the outputs of this wave's positions: lane (c, g) holds O^T dims
+  // 16 dt + 4 g .. + 3 of head c; the sum over keys gathers the 4 lanes of head c
+#pragma unroll
+  for (int p = 0; p < kPos; ++p) {
+    if (p >= np) break;
+    float lt = l[p];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const size_t row = ((size_t)b * a.K + p0 + p) * Hq + kvh * kG + c;
+    const float inv = 1.0f / lt;
+    float* o = a.out + row * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t*>(o + 16 * dt + 4 * g) = acc[p][dt] * inv;
+    if (g == 0) a.lse[row] = (m[p] + log2f(lt)) * 0.69314718055994531f;
+  }
+}
+
 struct Plan {
   int S, keys_per_split;
+  bool block;   // the large-batch kernel (wa_block)
 };
 
 inline int check(int B, int K, int Hq, int Hkv, int D, int L, int W) {
@@ -421,6 +736,14 @@ inline Plan plan(int B, int K, int Hkv, int W) {
   Plan p;
   p.keys_per_split = (int)per;
   p.S = (int)((span + per - 1) / per);
+  p.block = false;
+  // enough (row, key/value head) pairs to fill the GPU with one workgroup
+  // each: the large-batch kernel, one split (no partials, no merge launch)
+  if (pairs >= kBlockMinPairs) {
+    p.block = true;
+    p.S = 1;
+    p.keys_per_split = (int)span;
+  }
   return p;
 }
 
@@ -428,6 +751,12 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline size_t workspace(int B, int K, int Hkv, int W, size_t* o_bytes) {
   const Plan p = plan(B, K, Hkv, W);
+  // the single-launch kernel keeps nothing between launches: a token size,
+  // so that 0 still means "unsupported"
+  if (p.block) {
+    if (o_bytes) *o_bytes = 0;
+    return 256;
+  }
   const size_t rows = (size_t)B * Hkv * p.S * K * kG;
   const size_t ob = align_up(rows * kD * sizeof(float), 256);
   if (o_bytes) *o_bytes = ob;
@@ -469,6 +798,15 @@ int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, co
   a.B = B; a.K = K; a.Hkv = Hkv; a.L = L; a.W = W; a.S = p.S; a.keys_per_split = p.keys_per_split;
   a.scale_log2 = scale * 1.44269504088896341f;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  if (p.block) {
+    // one split: the workgroups write o and lse themselves
+    const dim3 grid(1, Hkv, B), block(kBThreads);
+    switch ((K + kBWaves - 1) / kBWaves) {
+      case 1: hipLaunchKernelGGL(wa_block<1>, grid, block, kBLds, stream, a); break;
+      default: hipLaunchKernelGGL(wa_block<2>, grid, block, kBLds, stream, a); break;
+    }
+    return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+  }
   hipLaunchKernelGGL(wa_partials, dim3(p.S, Hkv, B), dim3(kPartThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
   if (p.S <= kFewSplits)

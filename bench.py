@@ -209,8 +209,9 @@ ATTN_SHAPES = {
 
 def measure_attention(name, reps=20, mall="cold"):
     """The drafter's non-causal windowed block attention (one layer) on
-    synthetic bf16 Q/K/V of the ``ATTN_SHAPES`` shape. Mean us per call (two
-    launches, events on the launch stream, MALL flushed before each).
+    synthetic bf16 Q/K/V of the ``ATTN_SHAPES`` shape. Mean us per call (one
+    launch from 256 (row, key/value head) pairs, two below; events on the
+    launch stream, MALL flushed before each).
     Algorithmic bytes: per (row, key/value head) the K and V rows of the
     window's key range (W - 1 + K keys), plus Q read and o, lse written."""
     import math

@@ -329,8 +329,10 @@ int dspark_verify_block(
  *
  * Scores are bf16 products accumulated in float32, the softmax is float32
  * in base 2, and the probabilities are rounded to bf16 for the product with
- * V. Two launches on `stream` (the key range split over workgroups, then a
- * log-sum-exp merge of the splits); graph-capturable; nothing is allocated.
+ * V. With B * Hkv >= 256 one launch on `stream` (one workgroup per row and
+ * key/value head over the whole key range); below that, two (the key range
+ * split over workgroups, then a log-sum-exp merge of the splits).
+ * Graph-capturable; nothing is allocated.
  * Errors: DSPARK_ERR_ARG (null or misaligned pointers, bad scale or sizes),
  * DSPARK_ERR_UNSUPPORTED (sizes outside the limits), DSPARK_ERR_WORKSPACE,
  * DSPARK_ERR_HIP. B == 0 enqueues nothing. */

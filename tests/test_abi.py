@@ -207,9 +207,14 @@ def _attn(lib, **kw):
 
 
 def test_window_attention_workspace_bytes(lib):
-    # B=88, 4 key/value heads: 3 splits of 1408 keys; partial outputs and (max, sum) per split
-    n = adt.dspark_window_attention_workspace_bytes(88, 7, 64, 4, 128, 8199, 4096)
-    assert n >= 88 * 4 * 3 * 7 * 16 * (128 + 2) * 4
+    # B=8, 4 key/value heads (32 pairs): the key range split over workgroups,
+    # partial outputs and (max, sum) per split
+    n = adt.dspark_window_attention_workspace_bytes(8, 7, 64, 4, 128, 8199, 4096)
+    assert n >= 8 * 4 * 2 * 7 * 16 * (128 + 2) * 4
+    # from 256 (row, key/value head) pairs one launch keeps nothing: a token size
+    assert adt.dspark_window_attention_workspace_bytes(88, 7, 64, 4, 128, 8199, 4096) == 256
+    assert adt.dspark_window_attention_workspace_bytes(64, 7, 64, 4, 128, 8199, 4096) == 256
+    assert adt.dspark_window_attention_workspace_bytes(63, 7, 64, 4, 128, 8199, 4096) > 256
     assert adt.dspark_window_attention_workspace_bytes(1, 7, 64, 4, 64, 8199, 4096) == 0    # D != 128
     assert adt.dspark_window_attention_workspace_bytes(1, 7, 48, 4, 128, 8199, 4096) == 0   # Hq != 16 Hkv
     assert adt.dspark_window_attention_workspace_bytes(1, 9, 64, 4, 128, 8199, 4096) == 0   # K > 8

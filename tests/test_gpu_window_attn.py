@@ -11,9 +11,10 @@ v_td^2); the test allows six of those, plus 1e-5 * sum_t w_t |v_td| for the
 float32 scores and normaliser and 1e-6 absolute. At W = 4096 that is a few
 1e-4 against outputs of ~0.03, so a missing or repeated key tile fails it.
 Cases: a window over part of the context, contexts around the window
-edge (P = 0, W-1, W, W+1), K = 3/7/8 and K = W, the pages' head layouts 16/1
-and 64/4, the 4096-token window, and the full-size benchmark shape (B=88,
-P=8192) on sampled (row, position, head) triples.
+edge (P = 0, W-1, W, W+1), K = 1..8 and K = W, the pages' head layouts 16/1
+and 64/4, the 4096-token window, both launch forms (below and from 256 (row,
+key/value head) pairs), and the full-size benchmark shape (B=88, P=8192) on
+sampled (row, position, head) triples.
 """
 
 from __future__ import annotations
@@ -96,6 +97,10 @@ def window_tolerance(q, kc, vc, P, W, scale, lse_ref):
 
 
 def check(o, lse, o_ref, lse_ref, tol_o):
+    bad = np.argwhere(~(np.abs(lse - lse_ref) <= 2e-4))
+    if len(bad):
+        say(f"lse mismatches at {len(bad)} (row, position, head) triples, first: "
+            f"{[(tuple(int(v) for v in t), float(lse[tuple(t)]), float(lse_ref[tuple(t)])) for t in bad[:6]]}")
     err_o = np.abs(o - o_ref)
     assert (err_o <= tol_o).all(), (float(err_o.max()), float(np.max(err_o / tol_o)))
     err_l = np.abs(lse - lse_ref)
@@ -113,6 +118,36 @@ def check(o, lse, o_ref, lse_ref, tol_o):
 ])
 def test_window_attention_parity(B, K, Hq, Hkv, L, W, P):
     q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=B * 100 + K + W)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(q, kc, vc, P, W, scale)
+    vq, vk, vv = _f64(q), _f64(kc), _f64(vc)
+    o_ref, lse_ref = wa.window_block_attention(vq, vk, vv, np.asarray(P), W, scale)
+    check(o, lse, o_ref, lse_ref, window_tolerance(vq, vk, vv, np.asarray(P), W, scale, lse_ref))
+
+
+def _ragged_contexts(B, K, L, W, seed):
+    """Contexts for B rows: 0, 1, around the window edge (W - 2 .. W + 1) and
+    the largest (L - K) where they fit, the rest drawn uniformly."""
+    fixed = [p for p in (0, 1, W - 2, W - 1, W, W + 1, L - K) if 0 <= p <= L - K]
+    rng = np.random.default_rng(seed)
+    return fixed + [int(x) for x in rng.integers(0, L - K + 1, size=B - len(fixed))]
+
+
+# B * Hkv >= 256 (row, key/value head) pairs: the single-launch kernel, whose
+# two waves split the K positions (ceil(K / 2) slots each, the spare slot of
+# an odd K repeating the last position); every output compared.
+@pytest.mark.parametrize("B,K,Hq,Hkv,L,W", [
+    (64, 7, 64, 4, 700, 256),     # the pages' head layout, 4 + 3 positions
+    (64, 8, 64, 4, 300, 100),     # K = 8, a window that is not a multiple of the tile
+    (96, 5, 48, 3, 500, 200),     # 3 + 2 positions
+    (256, 3, 16, 1, 200, 64),     # one key/value head
+    (128, 2, 32, 2, 400, 33),     # one position per wave
+    (300, 1, 16, 1, 150, 40),     # K = 1: the second wave repeats the first
+    (256, 8, 16, 1, 60, 8),       # K = W: every key tile is an edge tile
+])
+def test_window_attention_single_launch_parity(B, K, Hq, Hkv, L, W):
+    q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=B * 10 + K * 3 + W)
+    P = _ragged_contexts(B, K, L, W, seed=B + W)
     scale = 1.0 / math.sqrt(D)
     o, lse = run_gpu(q, kc, vc, P, W, scale)
     vq, vk, vv = _f64(q), _f64(kc), _f64(vc)
