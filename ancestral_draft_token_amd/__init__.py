@@ -27,13 +27,18 @@ DSPARK_ERR_WORKSPACE = -3
 DSPARK_ERR_HIP = -4
 DSPARK_ERR_SCRATCH = -5
 
+# key/value cache layouts of the window attention
+DSPARK_KV_LAYOUT_BLHD = 0   # [B, L, Hkv, D]
+DSPARK_KV_LAYOUT_BHLD = 1   # [B, Hkv, L, D]
+
 EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_draft_block_chunked", "dspark_draft_block_events", "dspark_launch_plan",
             "dspark_status_string", "dspark_verify_workspace_bytes", "dspark_verify_standard",
             "dspark_verify_block_workspace_bytes", "dspark_verify_block",
             "dspark_window_attention_workspace_bytes", "dspark_window_block_attention",
             "dspark_block_status", "dspark_set_wait_limit",
-            "dspark_draft_block_noalloc", "dspark_noalloc_scratch_bytes")
+            "dspark_draft_block_noalloc", "dspark_noalloc_scratch_bytes",
+            "dspark_window_block_attention_layout")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
                 4: "markov_bias_gumbel_argmax"}
@@ -87,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_window_attention_workspace_bytes.restype = Z
     lib.dspark_window_block_attention.argtypes = [P, P, P, P, I, I, I, I, I, I, I, ctypes.c_float, P, P, P, Z, P]
     lib.dspark_window_block_attention.restype = I
+    lib.dspark_window_block_attention_layout.argtypes = [P, P, P, P, I, I, I, I, I, I, I, ctypes.c_float, I,
+                                                         P, P, P, Z, P]
+    lib.dspark_window_block_attention_layout.restype = I
     lib.dspark_block_status.argtypes = [P, P]
     lib.dspark_block_status.restype = I
     lib.dspark_set_wait_limit.argtypes = [ctypes.c_uint]
@@ -247,13 +255,21 @@ def dspark_window_attention_workspace_bytes(B: int, K: int, Hq: int, Hkv: int, D
 
 def dspark_window_block_attention(q, k_cache, v_cache, ctx_len, B: int, K: int, Hq: int, Hkv: int, D: int, L: int,
                                   W: int, scale: float, out, lse, workspace, workspace_bytes: int, stream=None,
-                                  check: bool = True) -> int:
+                                  check: bool = True, layout: int | None = None) -> int:
     """Enqueue the drafter's non-causal windowed block attention; arguments as in
-    ``include/dspark.h``."""
+    ``include/dspark.h``. ``layout`` None calls dspark_window_block_attention
+    (caches [B, L, Hkv, D]); a DSPARK_KV_LAYOUT_* value calls
+    dspark_window_block_attention_layout with it."""
     lib = load_library()
-    rc = lib.dspark_window_block_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), int(B), int(K),
-                                           int(Hq), int(Hkv), int(D), int(L), int(W), float(scale), _ptr(out),
-                                           _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream_ptr(stream))
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), int(B), int(K), int(Hq), int(Hkv), int(D), int(L),
+            int(W), float(scale))
+    tail = (_ptr(out), _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream_ptr(stream))
+    if layout is None:
+        name = "dspark_window_block_attention"
+        rc = lib.dspark_window_block_attention(*head, *tail)
+    else:
+        name = "dspark_window_block_attention_layout"
+        rc = lib.dspark_window_block_attention_layout(*head, int(layout), *tail)
     if check and rc != DSPARK_OK:
-        raise DSparkError(rc, "dspark_window_block_attention")
+        raise DSparkError(rc, name)
     return rc

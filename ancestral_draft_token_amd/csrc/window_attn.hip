@@ -98,7 +98,15 @@ struct WaArgs {
   float* lse;               // [B,K,Hq]
   int B, K, Hkv, L, W, S, keys_per_split;
   float scale_log2;         // scale * log2(e)
+  size_t key_stride;        // cache elements between consecutive keys of one head
+  size_t head_stride;       // cache elements between the heads of one key
 };
+
+// The first element of row b, head kvh in a cache of either layout (a row
+// holds L * Hkv * D elements in both).
+__device__ __forceinline__ const uint16_t* cache_head(const uint16_t* cache, const WaArgs& a, int b, int kvh) {
+  return cache + (size_t)b * a.L * a.Hkv * kD + (size_t)kvh * a.head_stride;
+}
 
 __device__ __forceinline__ int clamp_ctx(const WaArgs& a, int b) {
   const int P = a.ctx_len[b];
@@ -119,9 +127,9 @@ __global__ __launch_bounds__(kPartThreads, 4) void wa_partials(WaArgs a) {
   const int hi = P + a.K;
   const int k_begin = lo0 + s * a.keys_per_split;
   const int k_end = k_begin + a.keys_per_split < hi ? k_begin + a.keys_per_split : hi;
-  const size_t rs = (size_t)a.Hkv * kD;                                 // elements between keys
-  const uint16_t* kb = a.kc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
-  const uint16_t* vb = a.vc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
+  const size_t rs = a.key_stride;                                       // elements between keys
+  const uint16_t* kb = cache_head(a.kc, a, b, kvh);
+  const uint16_t* vb = cache_head(a.vc, a, b, kvh);
   const size_t pslot = (((size_t)b * a.Hkv + kvh) * a.S + s) * a.K;    // (b, kvh, s, position 0)
 
   // the two draft positions of this wave and their query fragments:
@@ -404,8 +412,9 @@ __global__ __launch_bounds__(kD) void wa_combine_splits(WaArgs a) {
 //     keys) comes from two transposing LDS reads ds_read_b64_tr_b16 of the
 //     row-major V tile: lane r of a 16-lane group reads 4 dims of key r / 4
 //     and lane j receives dim j of the group's 4 keys.
-// Online softmax in base 2 per position and head over each 32-key tile, lazy
-// rescale; outputs are normalised and written by the wave that owns them.
+// Online softmax in base 2 per position and head, with a reference that moves
+// only when a score passes it by a margin (below); outputs are normalised and
+// written by the wave that owns them.
 // ---------------------------------------------------------------------------
 constexpr int kBT = 32;                        // keys per tile (each wave loads 8)
 constexpr int kBWaves = 4;
@@ -414,6 +423,7 @@ constexpr int kNB = 4;                         // tiles in the LDS ring
 constexpr int kBTile = kBT * kD * 2;           // bytes of one tensor's tile (8 KB)
 constexpr int kBLds = kNB * 2 * kBTile;        // 64 KB
 constexpr long long kBlockMinPairs = 256;      // (row, key/value head) pairs from which wa_block is used
+constexpr float kTau = 8.0f;                   // lazy softmax reference: e stays below 2^kTau
 static_assert(kKMax <= 2 * kBWaves, "positions per wave");
 constexpr int kBRows = kBT / kBWaves;          // key rows each wave loads per tile
 constexpr int kBLoads = 2 * kBRows / 4;        // its LDS-direct loads per tile (K and V, 4 rows each)
@@ -470,6 +480,17 @@ __device__ __forceinline__ float max_over_heads_lanes(float x) {
   return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
 }
 
+// One pass over the ring's slots: tiles n, n + 1, .. in slots kSlot, kSlot + 1,
+// .. (compile-time slots, so every LDS offset is an immediate), up to the
+// last tile.
+template <int kSlot, int kN, class F>
+__device__ __forceinline__ void ring_round(F& step, int n, int n_tiles) {
+  step(n, std::integral_constant<int, kSlot>{});
+  if constexpr (kSlot + 1 < kN) {
+    if (n + 1 < n_tiles) ring_round<kSlot + 1, kN>(step, n + 1, n_tiles);
+  }
+}
+
 template <int kPos>
 __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
   extern __shared__ __align__(16) unsigned char wlds[];          // the ring (kBLds bytes)
@@ -481,9 +502,9 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
   const int P = clamp_ctx(a, b);
   const int lo0 = P - (a.W - 1) > 0 ? P - (a.W - 1) : 0;
   const int hi = P + a.K;
-  const size_t rs = (size_t)a.Hkv * kD;                                 // elements between keys
-  const uint16_t* kb = a.kc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
-  const uint16_t* vb = a.vc + ((size_t)b * a.L * a.Hkv + kvh) * kD;
+  const size_t rs = a.key_stride;                                       // elements between keys
+  const uint16_t* kb = cache_head(a.kc, a, b, kvh);
+  const uint16_t* vb = cache_head(a.vc, a, b, kvh);
   const int n_tiles = (hi - lo0 + kBT - 1) / kBT;
   const int p0 = wv * kPos;                                           // this wave's first position
   const int np = a.K - p0 < kPos ? a.K - p0 : kPos;                   // its positions (may be <= 0)
@@ -548,15 +569,23 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
     }
   };
 
+  // Online softmax with a lazy reference: m is the running maximum (base-2
+  // units) as of its last update, and e = 2^(s log2(e) - m) may exceed 1 by
+  // up to 2^kTau before m moves again. A tile updates m (and rescales) only
+  // if one of its raw scores exceeds thr = (m + kTau) / (scale log2(e)): the
+  // common tile costs one compare per score instead of a reduction across
+  // lanes. Before the first key m = thr = -inf.
   f32x4_t acc[kPos][8];
-  float m[kPos], l[kPos];
+  float m[kPos], l[kPos], thr[kPos];
 #pragma unroll
   for (int p = 0; p < kPos; ++p) {
     m[p] = -INFINITY;
+    thr[p] = -INFINITY;
     l[p] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[p][dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  const float inv_scale_log2 = 1.0f / a.scale_log2;
 
   // the largest window start of a position: tiles below it, and the last
   // tile, need masks
@@ -624,17 +653,22 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
             if (!(key >= lo_p && key < hi)) x[4 * h + i] = -INFINITY;
           }
       }
-      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mt = max_over_heads_lanes(mt) * a.scale_log2;
-      if (__any(mt > m[p])) {
-        // some head's running maximum grows: rescale (alpha = 1 for the
-        // others, 0 from the empty start); skipped once the maxima settle
+      bool over = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) over |= x[i] > thr[p];
+      if (__any(over)) {
+        // a score past the threshold: the exact maximum of this tile per
+        // head, and the new reference (alpha = 1 for heads whose maximum
+        // did not grow, 0 from the empty start)
+        float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mt = max_over_heads_lanes(mt) * a.scale_log2;
         const float mn = fmaxf(mt, m[p]);
         const float alpha = __builtin_amdgcn_exp2f(m[p] - mn);
         l[p] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[p][dt] *= alpha;
         m[p] = mn;
+        thr[p] = (mn + kTau) * inv_scale_log2;
       }
       const float mref = m[p] == -INFINITY ? 0.0f : m[p];   // no key seen yet: every e is 0
       float e[8];
@@ -660,23 +694,10 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
     }
   };
 
-  typedef std::integral_constant<int, 0> S0;
-  typedef std::integral_constant<int, 1> S1;
-  typedef std::integral_constant<int, 2> S2;
-  typedef std::integral_constant<int, 3> S3;
-  static_assert(kNB == 4, "the tile loop below is unrolled over the ring's 4 slots");
 #pragma unroll 1
   for (int n = 0; n < kNB - 1 && n < n_tiles; ++n) issue(n, n);
 #pragma unroll 1
-  for (int n = 0; n < n_tiles; n += kNB) {
-    step(n, S0{});
-    if (n + 1 >= n_tiles) break;
-    step(n + 1, S1{});
-    if (n + 2 >= n_tiles) break;
-    step(n + 2, S2{});
-    if (n + 3 >= n_tiles) break;
-    step(n + 3, S3{});
-  }
+  for (int n = 0; n < n_tiles; n += kNB) ring_round<0, kNB>(step, n, n_tiles);
 
   // the outputs of this wave's positions: lane (c, g) holds O^T dims
   // 16 dt + 4 g .. + 3 of head c; the sum over keys gathers the 4 lanes of head c
@@ -775,13 +796,14 @@ size_t dspark_window_attention_workspace_bytes(int B, int K, int Hq, int Hkv, in
   return workspace(B, K, Hkv, W, nullptr);
 }
 
-int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
-                                  const int32_t* ctx_len, int B, int K, int Hq, int Hkv, int D, int L, int W,
-                                  float scale, float* out, float* lse, void* workspace_ptr,
-                                  size_t workspace_bytes, void* stream_ptr) {
+int dspark_window_block_attention_layout(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                         const int32_t* ctx_len, int B, int K, int Hq, int Hkv, int D, int L,
+                                         int W, float scale, int layout, float* out, float* lse,
+                                         void* workspace_ptr, size_t workspace_bytes, void* stream_ptr) {
   using namespace dspark_wa;
   int rc = check(B, K, Hq, Hkv, D, L, W);
   if (rc != DSPARK_OK) return rc;
+  if (layout != DSPARK_KV_LAYOUT_BLHD && layout != DSPARK_KV_LAYOUT_BHLD) return DSPARK_ERR_ARG;
   if (B == 0) return DSPARK_OK;
   if (!q || !k_cache || !v_cache || !ctx_len || !out || !lse) return DSPARK_ERR_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return DSPARK_ERR_ARG;
@@ -797,6 +819,8 @@ int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, co
   a.out = out; a.lse = lse;
   a.B = B; a.K = K; a.Hkv = Hkv; a.L = L; a.W = W; a.S = p.S; a.keys_per_split = p.keys_per_split;
   a.scale_log2 = scale * 1.44269504088896341f;
+  a.key_stride = layout == DSPARK_KV_LAYOUT_BLHD ? (size_t)Hkv * kD : (size_t)kD;
+  a.head_stride = layout == DSPARK_KV_LAYOUT_BLHD ? (size_t)kD : (size_t)L * kD;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   if (p.block) {
     // one split: the workgroups write o and lse themselves
@@ -815,6 +839,15 @@ int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, co
     hipLaunchKernelGGL(wa_combine_splits, dim3(Hq, K, B), dim3(kD), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DSPARK_ERR_HIP;
   return DSPARK_OK;
+}
+
+int dspark_window_block_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* ctx_len, int B, int K, int Hq, int Hkv, int D, int L, int W,
+                                  float scale, float* out, float* lse, void* workspace_ptr,
+                                  size_t workspace_bytes, void* stream_ptr) {
+  return dspark_window_block_attention_layout(q, k_cache, v_cache, ctx_len, B, K, Hq, Hkv, D, L, W, scale,
+                                              DSPARK_KV_LAYOUT_BLHD, out, lse, workspace_ptr, workspace_bytes,
+                                              stream_ptr);
 }
 
 }  // extern "C"

@@ -207,24 +207,29 @@ ATTN_SHAPES = {
 }
 
 
-def measure_attention(name, reps=20, mall="cold"):
+def measure_attention(name, reps=20, mall="cold", layout="bhld"):
     """The drafter's non-causal windowed block attention (one layer) on
     synthetic bf16 Q/K/V of the ``ATTN_SHAPES`` shape. Mean us per call (one
     launch from 256 (row, key/value head) pairs, two below; events on the
     launch stream, MALL flushed before each).
     Algorithmic bytes: per (row, key/value head) the K and V rows of the
-    window's key range (W - 1 + K keys), plus Q read and o, lse written."""
+    window's key range (W - 1 + K keys), plus Q read and o, lse written.
+    ``layout``: the cache layout, "bhld" ([B, Hkv, L, D], each head's keys
+    contiguous: the library's streaming layout) or "blhd" ([B, L, Hkv, D])."""
     import math
     import torch
-    from ancestral_draft_token_amd import dspark_window_attention_workspace_bytes, dspark_window_block_attention
+    from ancestral_draft_token_amd import (DSPARK_KV_LAYOUT_BHLD, DSPARK_KV_LAYOUT_BLHD,
+                                           dspark_window_attention_workspace_bytes, dspark_window_block_attention)
     c = ATTN_SHAPES[name]
     B, K, Hq, Hkv, W, P = c["B"], c["K"], c["Hq"], c["Hkv"], c["W"], c["P"]
     D, L = 128, c["P"] + c["K"]
     dev = "cuda:0"
     g = torch.Generator(device=dev).manual_seed(5)
     q = torch.randn((B, K, Hq, D), device=dev, generator=g).to(torch.bfloat16)
-    kc = torch.randn((B, L, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
-    vc = torch.randn((B, L, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    shape = (B, Hkv, L, D) if layout == "bhld" else (B, L, Hkv, D)
+    kc = torch.randn(shape, device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn(shape, device=dev, generator=g).to(torch.bfloat16)
+    code = DSPARK_KV_LAYOUT_BHLD if layout == "bhld" else DSPARK_KV_LAYOUT_BLHD
     ctx = torch.full((B,), P, dtype=torch.int32, device=dev)
     out = torch.empty((B, K, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, K, Hq), dtype=torch.float32, device=dev)
@@ -242,7 +247,7 @@ def measure_attention(name, reps=20, mall="cold"):
                 torch.amax(flush_buf, dim=0, out=flush_out)
             starts[i].record(stream)
             dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, 1.0 / math.sqrt(D), out, lse, ws,
-                                          wb, stream=stream)
+                                          wb, stream=stream, layout=code)
             ends[i].record(stream)
     torch.cuda.synchronize()
     us = statistics.mean(s_.elapsed_time(e) * 1e3 for s_, e in zip(starts[2:], ends[2:]))
@@ -251,7 +256,7 @@ def measure_attention(name, reps=20, mall="cold"):
     flops = 4 * B * K * Hq * D * keys
     del q, kc, vc, flush_buf
     torch.cuda.empty_cache()
-    return {"shape": dict(c, D=D), "us": round(us, 2), "bytes": algo,
+    return {"shape": dict(c, D=D), "cache_layout": layout, "us": round(us, 2), "bytes": algo,
             "achieved_gbs": round(algo / (us * 1e-6) / 1e9, 1),
             "roofline_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "tflops": round(flops / (us * 1e-6) / 1e12, 1), "data": "synthetic bf16 N(0,1)"}
@@ -477,10 +482,14 @@ def main():
                 print(f"[bench] verify {name}", file=sys.stderr, flush=True)
                 line["verify"][name] = measure_verify(inputs.WORKLOADS[name](), mall=args.mall)
     # the drafter's windowed block attention (a second workload of the pages)
+    # (head-major caches, the library's streaming layout; B=88 also with the
+    # position-major [B, L, Hkv, D] layout)
     line["attention"] = {}
     for name in (("b1", "b88") if not args.no_sweep else ("b88",)):
         print(f"[bench] window attention {name}", file=sys.stderr, flush=True)
         line["attention"][name] = measure_attention(name, mall=args.mall)
+    print("[bench] window attention b88, [B, L, Hkv, D] caches", file=sys.stderr, flush=True)
+    line["attention"]["b88_blhd"] = measure_attention("b88", mall=args.mall, layout="blhd")
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)

@@ -342,6 +342,23 @@ int dspark_window_block_attention(
     int B, int K, int Hq, int Hkv, int D, int L, int W, float scale,
     float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Key/value cache layouts of dspark_window_block_attention_layout. */
+#define DSPARK_KV_LAYOUT_BLHD 0   /* [B, L, Hkv, D]: the heads of one position adjacent */
+#define DSPARK_KV_LAYOUT_BHLD 1   /* [B, Hkv, L, D]: each head's positions contiguous */
+
+/* dspark_window_block_attention with the cache layout given: k_cache and
+ * v_cache are [B, L, Hkv, D] (DSPARK_KV_LAYOUT_BLHD, what
+ * dspark_window_block_attention takes) or [B, Hkv, L, D]
+ * (DSPARK_KV_LAYOUT_BHLD). The attention computed, the other arguments, the
+ * workspace size and the errors are the same; another layout value is
+ * DSPARK_ERR_ARG. In the head-major layout each (row, head) key range is one
+ * contiguous span, which the kernels stream faster (256-byte rows at a
+ * 1 KB stride become one run). */
+int dspark_window_block_attention_layout(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* ctx_len,
+    int B, int K, int Hq, int Hkv, int D, int L, int W, float scale, int layout,
+    float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* dspark_status_string(int status);
 

@@ -83,6 +83,12 @@ int main(void) {
           DSPARK_ERR_ARG);
     CHECK(dspark_window_block_attention(P, P, P, P, 2, 7, 64, 4, 128, 9100, 4096, 0.1f, P, P, P, 0, NULL) ==
           DSPARK_ERR_WORKSPACE);
+    CHECK(dspark_window_block_attention_layout(P, P, P, P, 2, 7, 64, 4, 128, 9100, 4096, 0.1f, 2, P, P, P, aws,
+                                               NULL) == DSPARK_ERR_ARG);
+    CHECK(dspark_window_block_attention_layout(P, P, P, P, 2, 7, 64, 4, 128, 9100, 4096, 0.1f,
+                                               DSPARK_KV_LAYOUT_BHLD, P, P, P, 0, NULL) == DSPARK_ERR_WORKSPACE);
+    CHECK(dspark_window_block_attention_layout(NULL, NULL, NULL, NULL, 0, 7, 64, 4, 128, 9100, 4096, 0.1f,
+                                               DSPARK_KV_LAYOUT_BHLD, NULL, NULL, NULL, 0, NULL) == DSPARK_OK);
 
     CHECK(dspark_block_status(NULL, NULL) == DSPARK_ERR_ARG);
     const unsigned prev = dspark_set_wait_limit(3);

@@ -197,13 +197,15 @@ def test_verify_empty_batch_enqueues_nothing(lib, rule):
     assert _verify(lib, rule, B=0, draft=None, q=None, p=None) == adt.DSPARK_OK
 
 
-def _attn(lib, **kw):
+def _attn(lib, layout=None, **kw):
     a = dict(q=16, k=16, v=16, ctx=16, B=2, K=7, Hq=64, Hkv=4, D=128, L=9000, W=4096, scale=0.088, out=16,
              lse=16, ws=16, ws_bytes=1 << 30)
     a.update(kw)
-    return lib.dspark_window_block_attention(a["q"], a["k"], a["v"], a["ctx"], a["B"], a["K"], a["Hq"], a["Hkv"],
-                                             a["D"], a["L"], a["W"], a["scale"], a["out"], a["lse"], a["ws"],
-                                             a["ws_bytes"], None)
+    head = (a["q"], a["k"], a["v"], a["ctx"], a["B"], a["K"], a["Hq"], a["Hkv"], a["D"], a["L"], a["W"], a["scale"])
+    tail = (a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+    if layout is None:
+        return lib.dspark_window_block_attention(*head, *tail)
+    return lib.dspark_window_block_attention_layout(*head, layout, *tail)
 
 
 def test_window_attention_workspace_bytes(lib):
@@ -235,8 +237,14 @@ def test_window_attention_workspace_bytes(lib):
     (dict(ws=None), adt.DSPARK_ERR_WORKSPACE),
     (dict(ws_bytes=8), adt.DSPARK_ERR_WORKSPACE),
 ])
-def test_window_attention_host_checks(lib, kw, status):
-    assert _attn(lib, **kw) == status
+@pytest.mark.parametrize("layout", [None, adt.DSPARK_KV_LAYOUT_BLHD, adt.DSPARK_KV_LAYOUT_BHLD])
+def test_window_attention_host_checks(lib, kw, status, layout):
+    assert _attn(lib, layout=layout, **kw) == status
+
+
+@pytest.mark.parametrize("layout", [-1, 2, 7])
+def test_window_attention_rejects_unknown_layout(lib, layout):
+    assert _attn(lib, layout=layout) == adt.DSPARK_ERR_ARG
 
 
 def test_window_attention_empty_batch_enqueues_nothing(lib):

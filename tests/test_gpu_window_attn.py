@@ -25,8 +25,8 @@ import numpy as np
 import pytest
 
 from oracle import window_attn as wa
-from ancestral_draft_token_amd import (dspark_init, dspark_window_attention_workspace_bytes,
-                                       dspark_window_block_attention)
+from ancestral_draft_token_amd import (DSPARK_KV_LAYOUT_BHLD, DSPARK_KV_LAYOUT_BLHD, dspark_init,
+                                       dspark_window_attention_workspace_bytes, dspark_window_block_attention)
 
 from gpu_util import require_gpu, say
 
@@ -49,18 +49,22 @@ def _inputs(B, K, Hq, Hkv, L, seed):
     return q, kc, vc
 
 
-def run_gpu(q, kc, vc, P, W, scale):
+def run_gpu(q, kc, vc, P, W, scale, layout=None):
+    """The attention on caches kc, vc given as [B, L, Hkv, D]; with layout
+    DSPARK_KV_LAYOUT_BHLD they are passed head-major ([B, Hkv, L, D] copies)."""
     import torch
     dspark_init()
     B, K, Hq, _ = q.shape
     L, Hkv = kc.shape[1], kc.shape[2]
+    if layout == DSPARK_KV_LAYOUT_BHLD:
+        kc, vc = kc.permute(0, 2, 1, 3).contiguous(), vc.permute(0, 2, 1, 3).contiguous()
     ctx = torch.tensor(P, dtype=torch.int32, device="cuda:0")
     out = torch.empty((B, K, Hq, D), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, K, Hq), dtype=torch.float32, device="cuda:0")
     wb = dspark_window_attention_workspace_bytes(B, K, Hq, Hkv, D, L, W)
     ws = torch.empty(wb, dtype=torch.uint8, device="cuda:0")
-    say(f"window attention B={B} K={K} Hq={Hq} Hkv={Hkv} L={L} W={W} P={list(P)[:8]}")
-    dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, scale, out, lse, ws, wb)
+    say(f"window attention B={B} K={K} Hq={Hq} Hkv={Hkv} L={L} W={W} P={list(P)[:8]} layout={layout}")
+    dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, scale, out, lse, ws, wb, layout=layout)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
 
@@ -128,7 +132,7 @@ def test_window_attention_parity(B, K, Hq, Hkv, L, W, P):
 def _ragged_contexts(B, K, L, W, seed):
     """Contexts for B rows: 0, 1, around the window edge (W - 2 .. W + 1) and
     the largest (L - K) where they fit, the rest drawn uniformly."""
-    fixed = [p for p in (0, 1, W - 2, W - 1, W, W + 1, L - K) if 0 <= p <= L - K]
+    fixed = [p for p in (0, 1, W - 2, W - 1, W, W + 1, L - K) if 0 <= p <= L - K][:B]
     rng = np.random.default_rng(seed)
     return fixed + [int(x) for x in rng.integers(0, L - K + 1, size=B - len(fixed))]
 
@@ -155,14 +159,16 @@ def test_window_attention_single_launch_parity(B, K, Hq, Hkv, L, W):
     check(o, lse, o_ref, lse_ref, window_tolerance(vq, vk, vv, np.asarray(P), W, scale, lse_ref))
 
 
-def test_window_attention_full_size_sampled():
+@pytest.mark.parametrize("layout", [None, DSPARK_KV_LAYOUT_BHLD])
+def test_window_attention_full_size_sampled(layout):
     """The benchmark shape: B=88 rows, 64/4 heads, K=7, W=4096, P=8192 for every
-    row; 48 sampled (row, position, head) triples against the oracle."""
+    row, in both cache layouts; 48 sampled (row, position, head) triples
+    against the oracle."""
     B, K, Hq, Hkv, W, P = 88, 7, 64, 4, 4096, 8192
     L = P + K
     q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=4242)
     scale = 1.0 / math.sqrt(D)
-    o, lse = run_gpu(q, kc, vc, [P] * B, W, scale)
+    o, lse = run_gpu(q, kc, vc, [P] * B, W, scale, layout=layout)
     rng = np.random.default_rng(9)
     rows = [(int(rng.integers(B)), int(rng.integers(K)), int(rng.integers(Hq))) for _ in range(48)]
     rows += [(0, 0, 0), (B - 1, K - 1, Hq - 1)]
@@ -180,6 +186,36 @@ def test_window_attention_full_size_sampled():
         assert abs(lse[b, k, h] - rl[0]) <= 2e-4, (b, k, h)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     say(f"full-size attention: {len(rows)} sampled triples ok")
+
+
+# the head-major cache layout, in both launch forms (split key range below
+# 256 pairs, one launch from 256)
+@pytest.mark.parametrize("B,K,Hq,Hkv,L,W", [
+    (7, 3, 64, 4, 400, 128),
+    (2, 7, 64, 4, 9100, 4096),
+    (64, 7, 64, 4, 700, 256),
+    (256, 8, 16, 1, 60, 8),
+])
+def test_window_attention_head_major_layout(B, K, Hq, Hkv, L, W):
+    q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=B * 7 + K + W)
+    P = _ragged_contexts(B, K, L, W, seed=B * 3 + W)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = run_gpu(q, kc, vc, P, W, scale, layout=DSPARK_KV_LAYOUT_BHLD)
+    vq, vk, vv = _f64(q), _f64(kc), _f64(vc)
+    o_ref, lse_ref = wa.window_block_attention(vq, vk, vv, np.asarray(P), W, scale)
+    check(o, lse, o_ref, lse_ref, window_tolerance(vq, vk, vv, np.asarray(P), W, scale, lse_ref))
+
+
+@pytest.mark.parametrize("B", [7, 64])
+def test_window_attention_layout_entry_matches_default_entry(B):
+    """dspark_window_block_attention_layout with [B, L, Hkv, D] runs the same
+    kernels as dspark_window_block_attention: bit-identical outputs."""
+    K, Hq, Hkv, L, W = 7, 64, 4, 500, 200
+    q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=B + 1)
+    P = _ragged_contexts(B, K, L, W, seed=B)
+    o0, l0 = run_gpu(q, kc, vc, P, W, 0.1)
+    o1, l1 = run_gpu(q, kc, vc, P, W, 0.1, layout=DSPARK_KV_LAYOUT_BLHD)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
 
 
 def test_window_attention_clamps_context_length():
