@@ -601,24 +601,9 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) vofs[dt] = vkr * 256 + 16 * ((2 * dt + (vq >> 1)) ^ vswz_b(vkr)) + 8 * (vq & 1);
 
-  // one tile: wait for it, free the oldest slot, compute (slot known at compile time)
-  auto step = [&](int n, auto slot_tag) {
-    constexpr int slot = decltype(slot_tag)::value;
-    // this wave's loads of tile n have landed (the loads of the later tiles in
-    // flight are the newest), then every wave's: the tile is complete and the
-    // slot of tile n - 1 is free for tile n + kNB - 1
-    if (n + kNB - 2 < n_tiles) WA_WAIT_VMCNT(kBLoads * (kNB - 2));
-    else WA_WAIT_VMCNT(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (n + kNB - 1 < n_tiles) issue(n + kNB - 1, (slot + kNB - 1) % kNB);
-    const int tb = lo0 + n * kBT;
-    const unsigned char* kbuf = wlds + slot * 2 * kBTile;
-    const unsigned char* vbuf = kbuf + kBTile;
-
-    // scores: S^T of each half and position (lane (c, g): keys 16 h + 4 g .. + 3, head c)
-    f32x4_t sc[2][kPos];
+  // scores of one tile whose K sits at kbuf: S^T per half and position
+  // (lane (c, g): keys 16 h + 4 g .. + 3, head c)
+  auto scores = [&](const unsigned char* kbuf, f32x4_t (&out)[2][kPos]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4_t kf[4];
@@ -626,41 +611,72 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
       for (int ds = 0; ds < 4; ++ds) kf[ds] = *reinterpret_cast<const u32x4_t*>(kbuf + 4096 * h + kofs[ds]);
 #pragma unroll
       for (int p = 0; p < kPos; ++p) {
-        sc[h][p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        out[h][p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) sc[h][p] = mfma_bf16(kf[ds], qf[p][ds], sc[h][p]);
+        for (int ds = 0; ds < 4; ++ds) out[h][p] = mfma_bf16(kf[ds], qf[p][ds], out[h][p]);
       }
     }
+  };
+
+  // The tiles are pipelined by one: step n finishes tile n (softmax and P V,
+  // from the scores the previous step left in sc) and computes the scores of
+  // tile n + 1, which do not depend on tile n's softmax, so the scheduler can
+  // interleave those matrix instructions with the softmax's vector work.
+  // Tile n + 1 must therefore be in LDS at step n: the step waits for it
+  // (tile n + 2 stays in flight), and then refills the slot tile n - 1 used.
+  f32x4_t sc[2][kPos];
+  auto step = [&](int n, auto slot_tag) {
+    constexpr int slot = decltype(slot_tag)::value;
+    if (n + 1 < n_tiles) {
+      // this wave's loads of tile n + 1 have landed, then every wave's; every
+      // wave is past step n - 1, the last to read slot (n - 1) % kNB
+      if (n + 2 < n_tiles) WA_WAIT_VMCNT(kBLoads);
+      else WA_WAIT_VMCNT(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (n + kNB - 1 < n_tiles) issue(n + kNB - 1, (slot + kNB - 1) % kNB);
+    }
+    const int tb = lo0 + n * kBT;
+    const unsigned char* vbuf = wlds + slot * 2 * kBTile + kBTile;
+    // the next tile's K (after the last tile: a stale slot, scores unused)
+    const unsigned char* knext = wlds + ((slot + 1) % kNB) * 2 * kBTile;
 
     // keys outside a position's range score -inf; a tile wholly below the
     // range leaves P = 0 and the running state unchanged
-    const bool edge = tb < lo_max || tb + kBT > hi;
-    u32x4_t pb[kPos];
+    float x[kPos][8];                                    // raw <q, k>: half h at 4 h + i
 #pragma unroll
-    for (int p = 0; p < kPos; ++p) {
-      float x[8];                                        // raw <q, k>: half h at 4 h + i
+    for (int p = 0; p < kPos; ++p)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * h + i] = sc[h][p][i];
-      if (edge) {
+        for (int i = 0; i < 4; ++i) x[p][4 * h + i] = sc[h][p][i];
+    if (tb < lo_max || tb + kBT > hi) {
+#pragma unroll
+      for (int p = 0; p < kPos; ++p) {
         const int lo_p = P + pos[p] - (a.W - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = tb + 16 * h + 4 * g + i;
-            if (!(key >= lo_p && key < hi)) x[4 * h + i] = -INFINITY;
+            if (!(key >= lo_p && key < hi)) x[p][4 * h + i] = -INFINITY;
           }
       }
-      bool over = false;
+    }
+    bool over = false;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) over |= x[i] > thr[p];
-      if (__any(over)) {
-        // a score past the threshold: the exact maximum of this tile per
-        // head, and the new reference (alpha = 1 for heads whose maximum
-        // did not grow, 0 from the empty start)
-        float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    for (int p = 0; p < kPos; ++p)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) over |= x[p][i] > thr[p];
+    if (__any(over)) {
+      // a score past its threshold: the exact maximum of this tile per
+      // position and head, and the new references (alpha = 1 where the
+      // maximum did not grow, 0 from the empty start)
+#pragma unroll
+      for (int p = 0; p < kPos; ++p) {
+        float mt = fmaxf(fmaxf(fmaxf(x[p][0], x[p][1]), fmaxf(x[p][2], x[p][3])),
+                         fmaxf(fmaxf(x[p][4], x[p][5]), fmaxf(x[p][6], x[p][7])));
         mt = max_over_heads_lanes(mt) * a.scale_log2;
         const float mn = fmaxf(mt, m[p]);
         const float alpha = __builtin_amdgcn_exp2f(m[p] - mn);
@@ -670,15 +686,22 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
         m[p] = mn;
         thr[p] = (mn + kTau) * inv_scale_log2;
       }
+    }
+    u32x4_t pb[kPos];
+#pragma unroll
+    for (int p = 0; p < kPos; ++p) {
       const float mref = m[p] == -INFINITY ? 0.0f : m[p];   // no key seen yet: every e is 0
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.scale_log2, -mref));
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[p][i], a.scale_log2, -mref));
         l[p] += e[i];
       }
       pb[p] = u32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
     }
+
+    // the next tile's scores
+    scores(knext, sc);
 
     // O^T += V^T P^T: the A operand of dims 16 dt .. + 15 (lane: dim 16 dt + c,
     // keys 4 g .. + 3 of each half) by one transposing read per half
@@ -694,8 +717,16 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
     }
   };
 
+  // prologue: kNB - 1 tiles in flight, the first one waited for and scored
 #pragma unroll 1
   for (int n = 0; n < kNB - 1 && n < n_tiles; ++n) issue(n, n);
+  if (n_tiles >= 3) WA_WAIT_VMCNT(2 * kBLoads);
+  else if (n_tiles == 2) WA_WAIT_VMCNT(kBLoads);
+  else WA_WAIT_VMCNT(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  scores(wlds, sc);
 #pragma unroll 1
   for (int n = 0; n < n_tiles; n += kNB) ring_round<0, kNB>(step, n, n_tiles);
 

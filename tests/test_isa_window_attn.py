@@ -81,9 +81,9 @@ def test_m0_only_in_the_lds_direct_loads(asm, slots):
 @pytest.mark.parametrize("slots", SLOTS)
 def test_vmcnt_waits_only_before_the_tile_barriers(asm, slots):
     """Once the first LDS-direct load is issued, every vmcnt wait is one of
-    the tile loop's own (for its oldest tile, the younger tiles' loads still
-    in flight: one fixed count; vmcnt(0) at the end of the range), and the
-    barrier follows it with no vector or LDS instruction in between."""
+    the ring's own (the prologue's for tile 0 with two tiles of 4 loads
+    behind it, the tile loop's with one, vmcnt(0) at the end of the range),
+    and the barrier follows it with no memory instruction in between."""
     body = [l.split(";")[0].strip() for l in _body(asm, slots)]
     first = next(n for n, l in enumerate(body) if l.startswith("global_load_lds"))
     waits = [n for n, l in enumerate(body) if n > first and "vmcnt" in l]
@@ -96,11 +96,10 @@ def test_vmcnt_waits_only_before_the_tile_barriers(asm, slots):
         for l in body[n + 1:]:
             if l.startswith("s_barrier"):
                 break
-            assert not re.match(r"(v_|ds_|global_|buffer_)", l), (body[n], l)
+            assert not re.match(r"(ds_|global_|buffer_|scratch_|flat_)", l), (body[n], l)
         else:
             raise AssertionError(f"no barrier after {body[n]}")
-    ring = counts - {0}
-    assert len(ring) == 1 and min(ring) >= 8, counts     # at least two tiles of 4 loads stay in flight
+    assert counts <= {0, 4, 8} and 4 in counts, counts
 
 
 @pytest.mark.parametrize("slots", SLOTS)
