@@ -480,6 +480,19 @@ __device__ __forceinline__ float max_over_heads_lanes(float x) {
   return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
 }
 
+// s_waitcnt for the LDS-direct loads of all but the newest `behind` tiles
+// (kBLoads loads a tile per wave; behind is at most kNB - 2)
+__device__ __forceinline__ void wait_tiles_behind(int behind) {
+  static_assert(kNB <= 6, "wait counts below");
+  switch (behind) {
+    case 4: WA_WAIT_VMCNT(4 * kBLoads); break;
+    case 3: WA_WAIT_VMCNT(3 * kBLoads); break;
+    case 2: WA_WAIT_VMCNT(2 * kBLoads); break;
+    case 1: WA_WAIT_VMCNT(kBLoads); break;
+    default: WA_WAIT_VMCNT(0); break;
+  }
+}
+
 // One pass over the ring's slots: tiles n, n + 1, .. in slots kSlot, kSlot + 1,
 // .. (compile-time slots, so every LDS offset is an immediate), up to the
 // last tile.
@@ -628,10 +641,11 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
   auto step = [&](int n, auto slot_tag) {
     constexpr int slot = decltype(slot_tag)::value;
     if (n + 1 < n_tiles) {
-      // this wave's loads of tile n + 1 have landed, then every wave's; every
-      // wave is past step n - 1, the last to read slot (n - 1) % kNB
-      if (n + 2 < n_tiles) WA_WAIT_VMCNT(kBLoads);
-      else WA_WAIT_VMCNT(0);
+      // this wave's loads of tile n + 1 have landed (the younger tiles, up to
+      // n + kNB - 2, may still be in flight), then every wave's; every wave is
+      // past step n - 1, the last to read slot (n - 1) % kNB
+      if (n + kNB - 2 < n_tiles) WA_WAIT_VMCNT((kNB - 3) * kBLoads);
+      else wait_tiles_behind(n_tiles - 1 - (n + 1));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -720,9 +734,7 @@ __global__ __launch_bounds__(kBThreads, 2) void wa_block(WaArgs a) {
   // prologue: kNB - 1 tiles in flight, the first one waited for and scored
 #pragma unroll 1
   for (int n = 0; n < kNB - 1 && n < n_tiles; ++n) issue(n, n);
-  if (n_tiles >= 3) WA_WAIT_VMCNT(2 * kBLoads);
-  else if (n_tiles == 2) WA_WAIT_VMCNT(kBLoads);
-  else WA_WAIT_VMCNT(0);
+  wait_tiles_behind((n_tiles < kNB - 1 ? n_tiles : kNB - 1) - 1);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");

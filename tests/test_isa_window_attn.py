@@ -94,12 +94,14 @@ def test_vmcnt_waits_only_before_the_tile_barriers(asm, slots):
         assert m, body[n]
         counts.add(int(m.group(1)))
         for l in body[n + 1:]:
-            if l.startswith("s_barrier"):
+            # the barrier, or a branch to it (the end-of-range waits sit in a
+            # switch), before any memory instruction
+            if l.startswith("s_barrier") or l.startswith("s_branch") or l.startswith("s_cbranch"):
                 break
             assert not re.match(r"(ds_|global_|buffer_|scratch_|flat_)", l), (body[n], l)
         else:
             raise AssertionError(f"no barrier after {body[n]}")
-    assert counts <= {0, 4, 8} and 4 in counts, counts
+    assert counts <= {0, 4, 8, 12, 16} and 4 in counts, counts
 
 
 @pytest.mark.parametrize("slots", SLOTS)
