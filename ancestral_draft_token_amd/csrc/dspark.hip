@@ -1709,6 +1709,16 @@ __device__ __forceinline__ ERowSrc mf_erow_src(const MfArgs& a, const int* s_d, 
   return ERowSrc{a.E + (ok ? (size_t)s_d[row] * a.r + j16 : 0), ok};
 }
 
+// The same with the row's token given (d of this thread's row of N-tile nt,
+// valid wherever the row exists).
+__device__ __forceinline__ ERowSrc mf_erow_src_tok(const MfArgs& a, int tok, int nt, int t_in) {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(t_in));
+  const int row = 16 * nt + t / 16, j16 = 16 * (t % 16);
+  const bool ok = row < a.B && j16 < a.r;
+  return ERowSrc{a.E + (ok ? (size_t)tok * a.r + j16 : 0), ok};
+}
+
 __device__ __forceinline__ ERow2 mf_load_erow(const ERowSrc& es) {
   return ERow2{*reinterpret_cast<const uint4*>(es.src), *reinterpret_cast<const uint4*>(es.src + 8), es.ok};
 }
@@ -1924,7 +1934,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // word. Wave 1 does it (wave 0 may own one more tile than the others):
   // lane = row (lane % 16) x wave (lane / 16), merged over the 4 rows of lanes.
   auto publish = [&](int k, int nt) {
-    if (wv == 1) {
+    // after a failed wait nothing more is published (the workgroup's rows may
+    // be computed from an unknown token): every wait for its words expires
+    if (wv == 1 && !s_fail) {
       // the lane's row is taken through an opaque instruction, so the address
       // arithmetic below is done here rather than hoisted out of the loops
       // (held across them it was spilled, and the reloads waited for every
@@ -1944,6 +1956,95 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     }
   };
 
+  // ---- the exchange. Level 2, after a position's last N-tile: the owner of
+  // row b (workgroup b, b + G, ...) reduces the G words of its row in wave 0
+  // alone (each lane polls G / 64 of them, the first loads of a group of four
+  // in flight together; no LDS, no barrier) and publishes the row's tagged
+  // winner. A winner is published only when all G words were seen: a wait
+  // that expires publishes nothing, so no workgroup can take a winner made of
+  // part of the words.
+  auto level2 = [&](int k) {
+    if (wv != 0) return;
+    const uint64_t tagw = res_tag(cpar, k);
+    const uint64_t tag = tagw >> kResTagShift;
+    const uint64_t* xr = a.xrow + (size_t)(k & 1) * kResMaxCUs * kExRows;
+    uint64_t* xw = a.xwin + (size_t)(k & 1) * kExRows;
+    bool failed = false;
+    for (int b = g; b < B; b += G) {
+      uint64_t x = 0;
+      bool lfail = a.spin_limit == 0;
+      for (int i0 = lane; i0 < G && !lfail; i0 += 4 * 64) {
+        // the words still missing are reloaded together: one round trip per pass
+        uint64_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = i0 + 64 * q < G ? ld_agent_u64(xr + (size_t)(i0 + 64 * q) * kExRows + b) : tagw;
+        for (unsigned reads = 1;; ++reads) {
+          bool all = true;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) all = all && (w[q] >> kResTagShift) == tag;
+          if (all) break;
+          if (reads >= a.spin_limit) { lfail = true; break; }
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if ((w[q] >> kResTagShift) != tag) w[q] = ld_agent_u64(xr + (size_t)(i0 + 64 * q) * kExRows + b);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x = umax64(x, w[q]);
+      }
+      x = wave_max_u64(x);
+      const bool wave_failed = __ballot(lfail) != 0ull;
+      failed = failed || wave_failed;
+      if (lane == 0 && !wave_failed) st_agent_u64(xw + b, tagw | (x & ((1ull << kResTagShift) - 1)));
+    }
+    if (failed && lane == 0) s_fail = 1;
+  };
+
+  // Level 3: d_{k-1} of this thread's row of N-tile nt (16 threads a row, each
+  // reading the row's winner word; one request per row), taken when the E
+  // rows of that N-tile are prefetched: the previous tokens at k = 0, else the
+  // row's winner of position k - 1. Workgroup 0 also writes it to tokens. A
+  // wait that expires marks the workgroup failed and gives token 0 (a valid
+  // address; the workgroup leaves at its next barrier).
+  auto row_tok = [&](int k, int nt) -> int {
+    int tt;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tt) : "v"(t));
+    const int row = 16 * nt + tt / 16;
+    if (row >= B) return 0;
+    if (k == 0) return s_d[row];
+    if (s_fail) return 0;   // failed already: no more waits
+    const uint64_t tag = res_tag(cpar, k - 1) >> kResTagShift;
+    const uint64_t* pw = a.xwin + (size_t)((k - 1) & 1) * kExRows + row;
+    bool lfail = a.spin_limit == 0;
+    uint64_t w = lfail ? 0 : ld_agent_u64(pw);
+    for (unsigned reads = 1; !lfail && (w >> kResTagShift) != tag; ++reads) {
+      if (reads >= a.spin_limit) { lfail = true; break; }
+      __builtin_amdgcn_s_sleep(1);
+      w = ld_agent_u64(pw);
+    }
+    if (lfail) {
+      s_fail = 1;
+      return 0;
+    }
+    const uint64_t low = w & ((1ull << kResTagShift) - 1);
+    const int tok = low ? clamp_token((int)(kResIdxMask - (low & kResIdxMask)), V) : 0;
+    if (g == 0 && tt % 16 == 0) a.tokens[(size_t)row * K + (k - 1)] = tok;
+    return tok;
+  };
+
+  // A wait that expired (seen by every thread after a barrier): workgroup 0
+  // marks positions k - 1 on (those whose tokens may be incomplete) with -1,
+  // and every slot of this workgroup is rewritten with an unused tag of this
+  // call.
+  auto fail_exit = [&](int k) {
+    if (t == 0) res_fail(a.ex, s_call);
+    if (g == 0)
+      for (int b = t; b < B; b += kMfThreads)
+        for (int kk = k > 0 ? k - 1 : 0; kk < K; ++kk) a.tokens[(size_t)b * K + kk] = -1;
+    res_retire(a.ex, g, G, B, 0, 0, cpar, t, kMfThreads);
+  };
+
   // Base logits of each tile, one register set per tile (compile-time indices
   // after unrolling, so nothing is copied while a load is in flight): tile
   // i + kMfAhead is loaded during tile i, and the first kMfAhead tiles of the
@@ -1956,9 +2057,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
 
   for (int k = 0; k < K; ++k) {
     for (int nt = 0; nt < NT; ++nt) {
-      // source of the E rows of N-tile nt + 2 (tokens are fixed within a position),
-      // read before the barrier so its latency overlaps the wait
-      const ERowSrc es = mf_erow_src(a, s_d, nt + 2, t);
+      // source of the E rows of N-tile nt + 2 (its rows' tokens of position
+      // k - 1), read before the barrier so its latency overlaps the wait
+      const ERowSrc es = mf_erow_src_tok(a, row_tok(k, nt + 2), nt + 2, t);
       __syncthreads();   // E buffer nt & 1 is complete; s_rk[(nt - 1) & 1] is complete
       if (nt > 0) publish(k, nt - 1);
 
@@ -2049,84 +2150,32 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       bp = bpn;
     }
     __syncthreads();
-    publish(k, NT - 1);
-
-    // ---- exchange level 2: the owner of row b (workgroup b, b + G, ...) reduces its G
-    // words in wave 0 alone (each lane polls G / 64 of them, the first loads of a
-    // group of four in flight together; no LDS, no barrier) and publishes the winner.
-    // A winner is published only when all G words were seen: a wait that expires
-    // publishes nothing, so no workgroup can take a winner made of part of the words.
-    const uint64_t tagw = res_tag(cpar, k);
-    const uint64_t tag = tagw >> kResTagShift;
-    uint64_t* xr = a.xrow + (size_t)(k & 1) * kResMaxCUs * kExRows;
-    uint64_t* xw = a.xwin + (size_t)(k & 1) * kExRows;
-    bool failed = false;
-    if (wv == 0) {
-      for (int b = g; b < B; b += G) {
-        uint64_t x = 0;
-        bool lfail = a.spin_limit == 0;
-        for (int i0 = lane; i0 < G && !lfail; i0 += 4 * 64) {
-          // the words still missing are reloaded together: one round trip per pass
-          uint64_t w[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            w[j] = i0 + 64 * j < G ? ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kExRows + b) : tagw;
-          for (unsigned reads = 1;; ++reads) {
-            bool all = true;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) all = all && (w[j] >> kResTagShift) == tag;
-            if (all) break;
-            if (reads >= a.spin_limit) { lfail = true; break; }
-            __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if ((w[j] >> kResTagShift) != tag) w[j] = ld_agent_u64(xr + (size_t)(i0 + 64 * j) * kExRows + b);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x = umax64(x, w[j]);
-        }
-        x = wave_max_u64(x);
-        const bool wave_failed = __ballot(lfail) != 0ull;
-        failed = failed || wave_failed;
-        if (lane == 0 && !wave_failed) st_agent_u64(xw + b, tagw | (x & ((1ull << kResTagShift) - 1)));
-      }
-    }
-    // ---- level 3: every workgroup reads the B winners
-    for (int b = t; b < B; b += kMfThreads) {
-      const uint64_t* pw = xw + b;
-      if (a.spin_limit == 0) { failed = true; break; }
-      uint64_t w = ld_agent_u64(pw);
-      for (unsigned reads = 1; (w >> kResTagShift) != tag; ++reads) {
-        if (reads >= a.spin_limit) { failed = true; break; }
-        __builtin_amdgcn_s_sleep(1);
-        w = ld_agent_u64(pw);
-      }
-      const uint64_t low = w & ((1ull << kResTagShift) - 1);
-      s_d[b] = low ? clamp_token((int)(kResIdxMask - (low & kResIdxMask)), V) : 0;
-    }
-    if (failed) {
-      s_fail = 1;
-      res_fail(a.ex, s_call);
-    }
-    __syncthreads();
     if (s_fail) {
-      // an expired wait: this position and the later ones get no token
-      if (g == 0)
-        for (int b = t; b < B; b += kMfThreads)
-          for (int kk = k; kk < K; ++kk) a.tokens[(size_t)b * K + kk] = -1;
-      res_retire(a.ex, g, G, B, k + 1, k, cpar, t, kMfThreads);
+      fail_exit(k);
       return;
     }
-    if (g == 0)
-      for (int b = t; b < B; b += kMfThreads) a.tokens[(size_t)b * K + k] = s_d[b];
+    publish(k, NT - 1);
+    // the owners' reductions: rows of the earlier N-tiles were published long
+    // ago (no wait); only the owners of the last N-tile's rows wait for the
+    // slowest workgroup, and nobody waits for them before N-tile NT - 3 of
+    // the next position
+    level2(k);
     if (k + 1 < K) {
       // E rows of the next position's N-tiles 0 and 1 (both loads in flight
-      // before either store)
-      const ERow2 e0 = mf_load_erow(a, s_d, 0, t);
-      epre = mf_load_erow(a, s_d, 1, t);
+      // before either store); the buffers were last read before the barrier above
+      const ERow2 e0 = mf_load_erow(mf_erow_src_tok(a, row_tok(k + 1, 0), 0, t));
+      epre = mf_load_erow(mf_erow_src_tok(a, row_tok(k + 1, 1), 1, t));
       mf_store_erow(lds_e, t, e0);
       mf_store_erow(lds_e + 16 * kMfERow, t, epre);
     }
+  }
+  // the last position's tokens (workgroup 0)
+  if (g == 0)
+    for (int nt = 0; nt < NT; ++nt) (void)row_tok(K, nt);
+  __syncthreads();
+  if (s_fail) {
+    fail_exit(K);
+    return;
   }
   res_retire(a.ex, g, G, B, K, K, cpar, t, kMfThreads);
 }
