@@ -13,9 +13,12 @@ Three summaries:
     follow from them.
 
 Usage (from the repository root, after the rocprofv3 runs):
-  python -m ancestral_draft_token_amd.profiling kernels <stats.csv> <out.md> <command...>
-  python -m ancestral_draft_token_amd.profiling traffic <fetch.csv> <write.csv> <workload> <mall> <out.json> <command...>
-  python -m ancestral_draft_token_amd.profiling counters <out.md> <workload> <pmc.csv>[,<pmc.csv>...] <command...>
+  python -m ancestral_draft_token_amd.profiling [opts] kernels <stats.csv> <out.md> <command...>
+  python -m ancestral_draft_token_amd.profiling [opts] traffic <fetch.csv> <write.csv> <workload> <mall> <out.json> <command...>
+  python -m ancestral_draft_token_amd.profiling [opts] counters <out.md> <workload> <pmc.csv>[,<pmc.csv>...] <command...>
+opts: --kernel <name part> (the kernel summarised; default the sampler's
+markov_bias_gumbel_argmax) and --source <file under csrc/> (whose hash the
+summary records; default dspark.hip).
 """
 
 from __future__ import annotations
@@ -32,15 +35,15 @@ COPY_BYTES = 512 << 20       # the calibration copy in bench.py --pmc-run: reads
 DOMINANT = "markov_bias_gumbel_argmax"
 
 
-def source_hash() -> str:
-    with open(os.path.join(PKG, "csrc", "dspark.hip"), "rb") as f:
+def source_hash(source: str = "dspark.hip") -> str:
+    with open(os.path.join(PKG, "csrc", source), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def kernel_summary(stats_csv: str, out_md: str, command: str) -> None:
+def kernel_summary(stats_csv: str, out_md: str, command: str, source: str = "dspark.hip") -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel summary", "", f"command: `{command}`", "",
-             f"source sha256[:16] of csrc/dspark.hip: {source_hash()}", "",
+             f"source sha256[:16] of csrc/{source}: {source_hash(source)}", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"].replace("|", "/")
@@ -65,7 +68,7 @@ def _per_dispatch(path: str, counter: str):
 
 
 def traffic_summary(fetch_csv: str, write_csv: str, workload: str, mall: str, out_json: str,
-                    command: str = "") -> dict:
+                    command: str = "", kernel: str = DOMINANT, source: str = "dspark.hip") -> dict:
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
     kib = COPY_BYTES / 1024.0
@@ -78,9 +81,9 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, mall: str, ou
     copy_f = statistics.median(fmap[d] for d in calib)
     copy_w = statistics.median(wmap[d] for d in calib)
     f_scale, w_scale = kib / copy_f, kib / copy_w
-    dom = [d for d, n, _ in write if DOMINANT in n]
+    dom = [d for d, n, _ in write if kernel in n]
     rec = {
-        "workload": workload, "mall": mall, "kernel": DOMINANT, "source_sha": source_hash(),
+        "workload": workload, "mall": mall, "kernel": kernel, "source": source, "source_sha": source_hash(source),
         "command": command,
         "copy_bytes": COPY_BYTES, "copy_dispatches": calib,
         "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
@@ -92,7 +95,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, mall: str, ou
     rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     others = {}
     for d, n, v in write:
-        if d in calib or DOMINANT in n or d not in fmap:
+        if d in calib or kernel in n or d not in fmap:
             continue
         name = n.split("(")[0][:70]
         others.setdefault(name, []).append((fmap[d] * f_scale * 1024.0, v * w_scale * 1024.0))
@@ -119,20 +122,21 @@ SIMDS = 256 * 4   # MI355X: 256 compute units of 4 SIMDs
 XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (each counts the shader clock)
 
 
-def counter_summary(out_md: str, workload: str, csvs, command: str = "") -> dict:
-    """Median per dispatch of every counter of the dominant kernel, over the runs given."""
+def counter_summary(out_md: str, workload: str, csvs, command: str = "", kernel: str = DOMINANT,
+                    source: str = "dspark.hip") -> dict:
+    """Median per dispatch of every counter of the kernel, over the runs given."""
     med = {}
     disp = 0
     for path in csvs:
         names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
         for c in names:
-            vals = [v for _, n, v in _per_dispatch(path, c) if DOMINANT in n]
+            vals = [v for _, n, v in _per_dispatch(path, c) if kernel in n]
             if vals:
                 med[c] = statistics.median(vals)
                 disp = max(disp, len(vals))
     lines = ["# rocprofv3 counter summary", "", f"command: `{command}`", "",
-             f"source sha256[:16] of csrc/dspark.hip: {source_hash()}", "",
-             f"workload: {workload}; kernel: {DOMINANT}; dispatches: {disp}; "
+             f"source sha256[:16] of csrc/{source}: {source_hash(source)}", "",
+             f"workload: {workload}; kernel: {kernel}; dispatches: {disp}; "
              "values are the median per dispatch, summed over the device", "",
              "| counter | per dispatch |", "|---|---|"]
     for c, v in sorted(med.items()):
@@ -155,12 +159,19 @@ def counter_summary(out_md: str, workload: str, csvs, command: str = "") -> dict
 
 
 if __name__ == "__main__":
-    if sys.argv[1] == "kernels":
-        kernel_summary(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
-    elif sys.argv[1] == "traffic":
-        print(json.dumps(traffic_summary(*sys.argv[2:7], command=" ".join(sys.argv[7:])), indent=1))
-    elif sys.argv[1] == "counters":
-        print(json.dumps(counter_summary(sys.argv[2], sys.argv[3], sys.argv[4].split(","),
-                                         command=" ".join(sys.argv[5:])), indent=1))
+    argv = sys.argv[1:]
+    opts = {"kernel": DOMINANT, "source": "dspark.hip"}
+    while argv and argv[0] in ("--kernel", "--source"):
+        opts[argv[0][2:]] = argv[1]
+        argv = argv[2:]
+    if not argv:
+        raise SystemExit(__doc__)
+    if argv[0] == "kernels":
+        kernel_summary(argv[1], argv[2], " ".join(argv[3:]), source=opts["source"])
+    elif argv[0] == "traffic":
+        print(json.dumps(traffic_summary(*argv[1:6], command=" ".join(argv[6:]), **opts), indent=1))
+    elif argv[0] == "counters":
+        print(json.dumps(counter_summary(argv[1], argv[2], argv[3].split(","), command=" ".join(argv[4:]), **opts),
+                         indent=1))
     else:
         raise SystemExit(__doc__)

@@ -211,7 +211,8 @@ def measure_attention(name, reps=20, mall="cold", layout="bhld"):
     """The drafter's non-causal windowed block attention (one layer) on
     synthetic bf16 Q/K/V of the ``ATTN_SHAPES`` shape. Mean us per call (one
     launch from 256 (row, key/value head) pairs, two below; events on the
-    launch stream, MALL flushed before each).
+    launch stream, MALL flushed before each), and the mean over calls run
+    back to back between one pair of events.
     Algorithmic bytes: per (row, key/value head) the K and V rows of the
     window's key range (W - 1 + K keys), plus Q read and o, lse written.
     ``layout``: the cache layout, "bhld" ([B, Hkv, L, D], each head's keys
@@ -251,15 +252,55 @@ def measure_attention(name, reps=20, mall="cold", layout="bhld"):
             ends[i].record(stream)
     torch.cuda.synchronize()
     us = statistics.mean(s_.elapsed_time(e) * 1e3 for s_, e in zip(starts[2:], ends[2:]))
+    # back to back: one pair of events around `reps` calls, so the ~5 us an
+    # event pair costs is spread over them (the 770 MB a B=88 call reads is
+    # three times the MALL, so consecutive calls still stream from HBM)
+    b2b0, b2b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        b2b0.record(stream)
+        for _ in range(reps):
+            dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, 1.0 / math.sqrt(D), out, lse, ws,
+                                          wb, stream=stream, layout=code)
+        b2b1.record(stream)
+    torch.cuda.synchronize()
+    us_b2b = b2b0.elapsed_time(b2b1) * 1e3 / reps
     keys = min(P + K, W - 1 + K)
     algo = B * Hkv * keys * D * 2 * 2 + B * K * Hq * D * 2 + B * K * Hq * (D + 1) * 4
     flops = 4 * B * K * Hq * D * keys
     del q, kc, vc, flush_buf
     torch.cuda.empty_cache()
-    return {"shape": dict(c, D=D), "cache_layout": layout, "us": round(us, 2), "bytes": algo,
-            "achieved_gbs": round(algo / (us * 1e-6) / 1e9, 1),
-            "roofline_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "tflops": round(flops / (us * 1e-6) / 1e12, 1), "data": "synthetic bf16 N(0,1)"}
+    res = {"shape": dict(c, D=D), "cache_layout": layout, "us": round(us, 2), "bytes": algo,
+           "achieved_gbs": round(algo / (us * 1e-6) / 1e9, 1),
+           "roofline_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "tflops": round(flops / (us * 1e-6) / 1e12, 1), "data": "synthetic bf16 N(0,1)",
+           "us_back_to_back": round(us_b2b, 2),
+           "roofline_frac_back_to_back": round(algo / (us_b2b * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    # measured HBM bytes of the kernel from the committed counter summary, if
+    # it was taken on the current source
+    tr = attention_traffic(name, layout, mall)
+    if tr is not None:
+        res["traffic"] = tr
+        res["traffic_frac"] = round(tr / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    return res
+
+
+def attention_workload(name, layout):
+    return f"window_attention_{name}_w4096_{layout}"
+
+
+def attention_traffic(name, layout, mall):
+    """Counter bytes per call of the single-launch attention kernel (wa_block)
+    from profiles/traffic_<workload>_<mall>.json, or None (no summary, or the
+    kernel source changed since it was taken)."""
+    from ancestral_draft_token_amd.profiling import source_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{attention_workload(name, layout)}_{mall}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_hash("window_attn.hip"):
+        return None
+    return int(rec["bytes_per_launch"])
 
 
 def traffic_for(w, args):
@@ -389,6 +430,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-run", action="store_true",
                     help="for rocprofv3 --pmc: a calibration copy of known size, then a few replays")
+    ap.add_argument("--attention-run", metavar="SHAPE:LAYOUT",
+                    help="for rocprofv3: a calibration copy of known size, then --steps calls of the window "
+                         "attention alone (SHAPE b1 or b88, LAYOUT bhld or blhd); prints their timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the draft-block sampler is built and measured on "
@@ -403,7 +447,7 @@ def main():
         sys.exit(1)
 
     w = inputs.WORKLOADS[args.workload]()
-    if args.pmc_run:
+    if args.pmc_run or args.attention_run:
         from ancestral_draft_token_amd.profiling import COPY_BYTES
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -411,6 +455,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        if args.attention_run:
+            shape, layout = args.attention_run.split(":")
+            r = measure_attention(shape, reps=max(3, args.steps), mall=args.mall, layout=layout)
+            print(json.dumps({"attention": attention_workload(shape, layout), **r}), flush=True)
+            return
         b = Bench(w, mall=args.mall)
         b.steps(max(3, args.steps))
         torch.cuda.synchronize()

@@ -50,8 +50,9 @@
  * the launch: no other kernel may hold a compute unit while it runs, and two
  * such calls must never run at the same time on one device (calls ordered on
  * one stream are fine). The waits are bounded: if one expires (a compute unit
- * was held elsewhere), the positions from the one that failed on get token -1
- * and NaN proposals, and dspark_block_status reports it. Nothing hangs.
+ * was held elsewhere), the block's positions from one at or before the first
+ * it could not complete get token -1 and NaN proposals, and
+ * dspark_block_status reports it. Nothing hangs.
  *
  * Concurrency: calls on different streams must use different workspaces
  * and outputs, and resident calls must not overlap (above).
@@ -204,13 +205,13 @@ int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds);
 
 /* Whether a bounded device wait of the most recent resident-plan block on the
  * current device expired. Enqueues one tiny kernel on `stream` that writes
- * 1 (a wait expired: that block's tokens from the failed position on are -1
- * and their proposals NaN) or 0 (it did not, or no resident block has run on
- * the device) into *status, a DEVICE int32. Enqueue it on the stream of the
- * block it reports on, after the block; graph-capturable. Plans without
- * device waits (per-position plans) cannot fail this way and do not change
- * it. Returns DSPARK_ERR_ARG for a null pointer, DSPARK_ERR_HIP if the launch
- * fails, else DSPARK_OK. */
+ * 1 (a wait expired: that block's tokens from a position at or before the
+ * first incomplete one on are -1 and their proposals NaN) or 0 (it did not,
+ * or no resident block has run on the device) into *status, a DEVICE int32.
+ * Enqueue it on the stream of the block it reports on, after the block;
+ * graph-capturable. Plans without device waits (per-position plans) cannot
+ * fail this way and do not change it. Returns DSPARK_ERR_ARG for a null
+ * pointer, DSPARK_ERR_HIP if the launch fails, else DSPARK_OK. */
 int dspark_block_status(int32_t* status, void* stream);
 
 /* Sets how many times a resident kernel reads an exchange word before its wait
