@@ -41,7 +41,9 @@
  * failed check returns a negative status and enqueues nothing. A failed
  * kernel launch returns DSPARK_ERR_HIP. No C++ exception crosses the ABI.
  * Device data never causes an error: an out-of-range prev_token is clamped
- * into [0, V), and a drawn token is always in [0, V).
+ * into [0, V), and a drawn token is always in [0, V). The one exception is
+ * a resident-plan block whose bounded device wait expired (below): its
+ * positions from the failure on hold token -1 and NaN proposals.
  *
  * Device waits (resident plans, see dspark_launch_plan): one persistent
  * launch runs the whole block, one workgroup per compute unit, and the
