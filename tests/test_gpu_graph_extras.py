@@ -95,23 +95,28 @@ def test_verification_graph_replay(rule):
     say(f"verify_{rule}: replays equal eager; new offset followed")
 
 
-def test_window_attention_graph_replay():
+# (3 rows: the split form with its merge launch; 64 rows x 4 heads = 256
+# pairs: the single launch, also with head-major caches)
+@pytest.mark.parametrize("B,layout", [(3, None), (64, None), (64, 1)])
+def test_window_attention_graph_replay(B, layout):
     import torch
     dspark_init()
-    B, K, Hq, Hkv, D, W = 3, 7, 64, 4, 128, 256
+    K, Hq, Hkv, D, W = 7, 64, 4, 128, 256
     L = 900
     g0 = torch.Generator(device="cuda:0").manual_seed(3)
     q = torch.randn((B, K, Hq, D), device="cuda:0", generator=g0).to(torch.bfloat16)
-    kc = torch.randn((B, L, Hkv, D), device="cuda:0", generator=g0).to(torch.bfloat16)
-    vc = torch.randn((B, L, Hkv, D), device="cuda:0", generator=g0).to(torch.bfloat16)
-    ctx = torch.tensor([300, 500, 893], dtype=torch.int32, device="cuda:0")
+    shape = (B, Hkv, L, D) if layout == 1 else (B, L, Hkv, D)
+    kc = torch.randn(shape, device="cuda:0", generator=g0).to(torch.bfloat16)
+    vc = torch.randn(shape, device="cuda:0", generator=g0).to(torch.bfloat16)
+    ctx = torch.tensor(([300, 500, 893] * 22)[:B], dtype=torch.int32, device="cuda:0")
     o = torch.empty((B, K, Hq, D), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, K, Hq), dtype=torch.float32, device="cuda:0")
     wb = dspark_window_attention_workspace_bytes(B, K, Hq, Hkv, D, L, W)
     ws = torch.empty(wb, dtype=torch.uint8, device="cuda:0")
     scale = 1.0 / math.sqrt(D)
-    call = lambda: dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, scale, o, lse, ws, wb)
-    say("window attention eager")
+    call = lambda: dspark_window_block_attention(q, kc, vc, ctx, B, K, Hq, Hkv, D, L, W, scale, o, lse, ws, wb,
+                                                 layout=layout)
+    say(f"window attention eager B={B} layout={layout}")
     call()
     torch.cuda.synchronize()
     eager = [o.clone(), lse.clone()]
