@@ -1,8 +1,9 @@
 """Benchmark of the DSpark ancestral draft block on one MI355X.
 
 One step = one replay of the hipGraph that holds the whole K-position block
-(K fused per-position kernels, K pick_and_gather launches, one proposal
-kernel) over one batch of synthetic inputs already resident in HBM.
+(for B <= 128 one persistent kernel for all K positions and the proposal
+kernel; other plans K fused per-position kernels, their pick launches and the
+proposal kernel) over one batch of synthetic inputs already resident in HBM.
 
 Default workload: single-request decode, B=1, K=7, V=200064, r=256, bf16
 base logits -- the drafting-alone setup of the pages ("brb-nv/TensorRT-LLM
@@ -26,6 +27,13 @@ import os
 import statistics
 import sys
 import time
+
+# The HIP runtime launches a graph either from AQL packets it captured when
+# the graph was instantiated (this ROCm's default) or node by node. On MI355X
+# here the second is ~3.7 us faster per replay: a one-kernel graph 10.3
+# against 14.0 us, the B=1 block 82 against 86 us, with the same kernels. The
+# benchmark takes it unless the caller chose; it must be set before HIP starts.
+os.environ.setdefault("DEBUG_CLR_GRAPH_PACKET_CAPTURE", "0")
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -484,7 +492,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "B_real": w.n_real_rows, "K": w.K, "V": w.V,
                    "r": w.r, "base": w.base_dtype, "mall": args.mall,
-                   "graph": "one hipGraph per block", "launches": r["plan"]},
+                   "graph": "one hipGraph per block", "launches": r["plan"],
+                   "hip_graph_packet_capture": os.environ.get("DEBUG_CLR_GRAPH_PACKET_CAPTURE")},
         "us_median": round(r["us_median"], 2),
         "us_p10": round(r["us_p10"], 2),
         "us_p90": round(r["us_p90"], 2),
