@@ -40,6 +40,29 @@ def test_tiny_reference():
     full_check(inputs.tiny())
 
 
+def test_first_resident_call_of_a_process():
+    """The B = 1 block as the first resident launch of a fresh process (call
+    index 0, every exchange slot still holding its initial zero): no slot may
+    be taken for a published word, and the block must match the oracle."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = (f"import sys; sys.path[:0] = [{os.path.dirname(here)!r}, {here!r}]\n"
+            "from ancestral_draft_token_amd import inputs\n"
+            "from ancestral_draft_token_amd import dspark_launch_plan\n"
+            "from oracle import parity\n"
+            "from gpu_util import run_gpu\n"
+            "w = inputs.tiny()\n"
+            "assert 4 in dspark_launch_plan(w.B, w.K, w.V, w.r), 'a resident plan expected'\n"
+            "p = run_gpu(w)\n"
+            "print(parity.check(w, *p.outputs()).as_dict(), flush=True)\n"
+            "print('first call ok', flush=True)\n")
+    say("first resident call of a fresh process (subprocess)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "first call ok" in r.stdout, r.stdout[-2000:] + r.stderr[-4000:]
+
+
 @pytest.mark.parametrize("chunk_cols", [4096, 1408, 128, 256])
 def test_tiny_chunkings(chunk_cols):
     """One and three vocabulary chunks (4096 and 1408 columns), and the finest ones."""
