@@ -38,7 +38,8 @@ EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_window_attention_workspace_bytes", "dspark_window_block_attention",
             "dspark_block_status", "dspark_set_wait_limit",
             "dspark_draft_block_noalloc", "dspark_noalloc_scratch_bytes",
-            "dspark_window_block_attention_layout")
+            "dspark_window_block_attention_layout", "dspark_packed_w_bytes", "dspark_pack_w",
+            "dspark_draft_block_packed")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
                 4: "markov_bias_gumbel_argmax"}
@@ -103,6 +104,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_draft_block_noalloc.restype = I
     lib.dspark_noalloc_scratch_bytes.argtypes = []
     lib.dspark_noalloc_scratch_bytes.restype = Z
+    lib.dspark_packed_w_bytes.argtypes = [I, I]
+    lib.dspark_packed_w_bytes.restype = Z
+    lib.dspark_pack_w.argtypes = [P, I, I, P, Z, P]
+    lib.dspark_pack_w.restype = I
+    lib.dspark_draft_block_packed.argtypes = [P, I, P, P, P, Z, P, P, P, P, P, I, I, I, I] + out_args + [P, I]
+    lib.dspark_draft_block_packed.restype = I
     _lib = lib
     return lib
 
@@ -151,7 +158,7 @@ def _stream_ptr(stream) -> Optional[int]:
 def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, offset, temperature,
                        n_real, B: int, K: int, V: int, r: int, tokens, logits_f32, draft_probs,
                        workspace, workspace_bytes: int, stream=None, chunk_cols: Optional[int] = None,
-                       events=None, check: bool = True) -> int:
+                       events=None, check: bool = True, W_packed=None, packed_bytes: int = 0) -> int:
     """Enqueue one draft block; arguments as in ``include/dspark.h``.
 
     Tensor arguments may be torch device tensors or raw device addresses
@@ -159,13 +166,21 @@ def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, off
     hipStream_t, or None for torch's current stream. Returns the status; with
     ``check`` a nonzero status raises. ``events`` (a ctypes array of
     hipEvent_t handles, at least 2K + 2) selects ``dspark_draft_block_events``.
+    ``W_packed`` (from ``dspark_pack_w``, with its ``packed_bytes``) selects
+    ``dspark_draft_block_packed`` (events optional; no explicit chunking).
     """
     lib = load_library()
     args = [_ptr(base_logits), int(base_dtype), _ptr(E), _ptr(W), _ptr(prev_token), _ptr(seed),
             _ptr(offset), _ptr(temperature), _ptr(n_real), int(B), int(K), int(V), int(r)]
     outs = [_ptr(tokens), _ptr(logits_f32), _ptr(draft_probs), _ptr(workspace), int(workspace_bytes),
             _stream_ptr(stream)]
-    if events is not None:
+    if W_packed is not None:
+        if chunk_cols is not None:
+            raise ValueError("a packed W goes with the library's own chunking")
+        ev = (ctypes.cast(events, ctypes.c_void_p), len(events)) if events is not None else (None, 0)
+        rc = lib.dspark_draft_block_packed(*args[:4], _ptr(W_packed), int(packed_bytes), *args[4:], *outs, *ev)
+        where = "dspark_draft_block_packed"
+    elif events is not None:
         rc = lib.dspark_draft_block_events(*args, *outs, ctypes.cast(events, ctypes.c_void_p), len(events))
         where = "dspark_draft_block_events"
     elif chunk_cols is None:
@@ -176,6 +191,20 @@ def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, off
         where = "dspark_draft_block_chunked"
     if check and rc != DSPARK_OK:
         raise DSparkError(rc, where)
+    return rc
+
+
+def dspark_packed_w_bytes(V: int, r: int) -> int:
+    """Bytes of W packed for the resident kernels on the current device (0: nothing to pack)."""
+    return int(load_library().dspark_packed_w_bytes(int(V), int(r)))
+
+
+def dspark_pack_w(W, V: int, r: int, W_packed, packed_bytes: int, stream=None, check: bool = True) -> int:
+    """Enqueue the packing of W [r, V] (bf16) into ``W_packed``; see ``include/dspark.h``."""
+    rc = load_library().dspark_pack_w(_ptr(W), int(V), int(r), _ptr(W_packed), int(packed_bytes),
+                                      _stream_ptr(stream))
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_pack_w")
     return rc
 
 

@@ -30,6 +30,11 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # no packed-FP32 instructions: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the library's only atomics (a workgroup's arrival, a failure record) run
+    # on one thread; the backend's combining of atomics across a wave would
+    # make each wait at once for its result, and so for every load issued
+    # before it (the W stream of the resident kernels' setup)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

@@ -289,20 +289,25 @@ struct RowState {
   uint32_t key0, key1, ctr2, ctr3;
 };
 
-__device__ __forceinline__ RowState row_state(const float* temperature, const int64_t* seed,
-                                              const int64_t* offset, int b, int n_real) {
+// A row's sampling state from its temperature, Philox key (seed) and slot
+// offset; row b is padding when b >= n_real.
+__device__ __forceinline__ RowState row_state_of(float T, int64_t seed, int64_t offset, int b, int n_real) {
   RowState rs;
-  const float T = temperature[b];
   rs.greedy = !(T > 0.0f);
   rs.invT = rs.greedy ? 0.0f : __fdiv_rn(1.0f, T);
   rs.pad = b >= n_real;
-  const uint64_t sd = (uint64_t)seed[b];
-  const uint64_t of = (uint64_t)offset[b];
+  const uint64_t sd = (uint64_t)seed;
+  const uint64_t of = (uint64_t)offset;
   rs.key0 = (uint32_t)sd;
   rs.key1 = (uint32_t)(sd >> 32);
   rs.ctr2 = (uint32_t)of;
   rs.ctr3 = (uint32_t)(of >> 32);
   return rs;
+}
+
+__device__ __forceinline__ RowState row_state(const float* temperature, const int64_t* seed,
+                                              const int64_t* offset, int b, int n_real) {
+  return row_state_of(temperature[b], seed[b], offset[b], b, n_real);
 }
 
 __device__ __forceinline__ RowState row_state(const StepArgs& a, int b, int n_real) {
@@ -928,6 +933,12 @@ constexpr int kResRowsMax = 4;
 constexpr size_t kResLdsW = (size_t)kResPairs * kResLdsUnits * 32;   // 139,264 bytes
 constexpr size_t kResLdsE = (size_t)kResRowsMax * kResRank * 2;      // 2,048 bytes
 constexpr size_t kResLdsBytes = kResLdsW + kResLdsE;
+// packed W (dspark_pack_w): 16-byte units per workgroup and kernel, and those
+// of the register part (the rest is the kernel's LDS image)
+constexpr size_t kPackWgU4 = (size_t)kResSlice * kResRank * 2 / 16;   // 25,088
+constexpr int kPackRegU4 = 16384;
+static_assert(kResPairs * 2 * kResThreads == kPackRegU4, "small-batch register units");
+static_assert((size_t)kPackRegU4 * 16 + kResLdsW == kPackWgU4 * 16, "small-batch block size");
 constexpr int kResTagShift = 50;                           // word: tag | ord(z) | index
 constexpr uint64_t kResIdxMask = (1ull << 18) - 1;         // V <= 2^18
 constexpr int kResMaxCUs = 512;
@@ -1009,6 +1020,9 @@ __global__ void res_status(ResExchange* ex, unsigned G, int32_t* out) {
   out[0] = (a >= G && f == a / G) ? 1 : 0;
 }
 
+typedef __attribute__((address_space(1))) void* lds_gptr_t;   // global source of an LDS-direct load
+typedef __attribute__((address_space(3))) void* lds_lptr_t;   // its LDS destination
+
 struct ResArgs {
   const void* base;
   const uint16_t* E;
@@ -1022,6 +1036,7 @@ struct ResArgs {
   int32_t* tokens;
   ResExchange* ex;     // the device's exchange state
   Stat* stat_part;     // [K][B][G] per-workgroup softmax statistics
+  const uint4* Wp;     // packed W, this kernel's layout (kPacked), else unused
   int B, K, V, r, slice;
   unsigned spin_limit; // reads of a word before its wait expires (0: expires at once)
 };
@@ -1148,7 +1163,7 @@ __device__ __forceinline__ void epilogue4_noise(const RowState& rs, uint32_t v0,
   st = stat_merge(st, Stat{m4, l4});
 }
 
-template <int RB, bool kBf16Base>
+template <int RB, bool kBf16Base, bool kPacked>
 __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resident(ResArgs a) {
   extern __shared__ __align__(16) unsigned char res_lds[];
   uint32_t* lds_w = reinterpret_cast<uint32_t*>(res_lds);               // [16][272][8]
@@ -1161,8 +1176,6 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
 
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int g = blockIdx.x, G = gridDim.x;
-  unsigned long long call0 = 0;
-  if (t == 0) call0 = res_arrive(a.ex, G);
   const int V = a.V, r = a.r, K = a.K, B = a.B;
   const int js = lane & 7;                    // rank slice: rows 32 js .. 32 js + 31
   const bool j_ok = 32 * js < r;
@@ -1174,52 +1187,49 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
   const int n_lds_units = max(0, ngroups - kResRegGroups) * 8;
   const bool lds_ok = t < n_lds_units;        // this thread's LDS unit (if any) is unit t
   const int cg_l = kResRegGroups + (t >> 3);
-  const int n_real = a.n_real ? *a.n_real : B;
 
   // epilogue lane mapping after the reduce-scatter
   const int er = RB == 4 ? (js >> 1) : RB == 2 ? (js >> 2) : 0;
   const int eh = js & 1;
   const bool e_act = (RB == 4 ? true : RB == 2 ? ((js >> 1) & 1) == 0 : js < 2) && er < B;
-
-  // row states (uniform scalar loads) and this lane's row
-  RowState rows[RB];
-#pragma unroll
-  for (int rr = 0; rr < RB; ++rr)
-    rows[rr] = rr < B ? row_state(a.temperature, a.seed, a.offset, rr, n_real) : RowState{};
-  RowState rs = rows[0];
-#pragma unroll
-  for (int rr = 1; rr < RB; ++rr)
-    if (er == rr) rs = rows[rr];
-  if (t == 0) s_fail = 0;
-
   const uint32_t v_r = (uint32_t)(col0 + 8 * cg_r + 4 * eh);   // epilogue columns, VGPR unit
   const uint32_t v_l = (uint32_t)(col0 + 8 * cg_l + 4 * eh);   // epilogue columns, LDS unit
   const bool ep_r = e_act && reg_ok;
   const bool ep_l = e_act && lds_ok;
 
-  // ---- (1) this thread's VGPR unit of W: 32 rank rows x 8 columns, 8 rows per
-  // batch (512 threads x 8 x 16 B = 64 KB in flight per workgroup)
-  uint32_t wr[8][kResPairs];
-  {
-    const bool ok = reg_ok && j_ok;
-    const uint16_t* src = a.W + (ok ? (size_t)(32 * js) * V + col0 + 8 * cg_r : 0);
-    const size_t stride = ok ? (size_t)V : 0;
+  // the rows' inputs: position 0's tokens d_{-1}, temperatures, Philox keys
+  // and offsets, the padding count; then this lane's row state
+  int tok_in[RB];
+  float t_in[RB];
+  int64_t sd_in[RB], of_in[RB];
+  int n_real = B;
+  auto load_inputs = [&]() {
 #pragma unroll
-    for (int b8 = 0; b8 < 4; ++b8) {
-      uint4 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (8 * b8 + i) * stride);
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        uint32_t pr[8];
-        pack_pairs(raw[2 * pp], raw[2 * pp + 1], pr);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) wr[c][4 * b8 + pp] = pr[c];
-      }
+    for (int rr = 0; rr < RB; ++rr) {
+      const bool in = rr < B;
+      tok_in[rr] = in ? a.prev_token[rr] : 0;
+      t_in[rr] = in ? a.temperature[rr] : 0.0f;
+      sd_in[rr] = in ? a.seed[rr] : 0;
+      of_in[rr] = in ? a.offset[rr] : 0;
     }
-  }
+    n_real = a.n_real ? *a.n_real : B;
+  };
+  RowState rs;
+  int d0[RB];
+  auto set_rows = [&]() {
+    RowState rows[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      rows[rr] = rr < B ? row_state_of(t_in[rr], sd_in[rr], of_in[rr], rr, n_real) : RowState{};
+      d0[rr] = rr < B ? clamp_token(tok_in[rr], V) : 0;
+    }
+    rs = rows[0];
+#pragma unroll
+    for (int rr = 1; rr < RB; ++rr)
+      if (er == rr) rs = rows[rr];
+  };
 
-  // ---- (2) noise and base logits of a position for this lane's epilogue quads
+  // ---- noise and base logits of a position for this lane's epilogue quads
   float gq[2][4];
   Base4<kBf16Base> bq[2];
   auto prepare = [&](int k) {
@@ -1233,27 +1243,7 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     load_base4<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
   };
 
-  // ---- (3) the LDS units of W, 8 rank rows at a time
-  if (lds_ok) {
-    const uint16_t* src = a.W + (j_ok ? (size_t)(32 * js) * V + col0 + 8 * cg_l : 0);
-    const size_t stride = j_ok ? (size_t)V : 0;
-#pragma unroll
-    for (int b8 = 0; b8 < 4; ++b8) {
-      uint4 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (8 * b8 + i) * stride);
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        uint32_t pr[8];
-        pack_pairs(raw[2 * pp], raw[2 * pp + 1], pr);
-        uint4* dst = reinterpret_cast<uint4*>(lds_w + ((size_t)(4 * b8 + pp) * kResLdsUnits + t) * 8);
-        dst[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
-        dst[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
-      }
-    }
-  }
-
-  // ---- (4) embedding rows of position 0: E[clamp(prev_token)]
+  // ---- the embedding rows E[d] of a position's tokens, into LDS
   auto gather_e = [&](const int* d) {
     const uint32_t* E32 = reinterpret_cast<const uint32_t*>(a.E);
     for (int i = t; i < RB * (kResRank / 2); i += kResThreads) {
@@ -1263,14 +1253,103 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       lds_e[rr * (kResRank / 2) + jj] = v;
     }
   };
-  {
-    int d0[RB];
+
+  // ---- setup: W on chip for the block (this thread's VGPR unit of 32 rank
+  // rows x 8 columns as bf16 pairs, and the LDS units), the rows' inputs, this
+  // workgroup's arrival (its count names the call), and position 0's E rows,
+  // noise and base logits. The order is each W form's fastest as measured.
+  uint32_t wr[8][kResPairs];
+  unsigned long long arrival = 0;
+  if constexpr (kPacked) {
+    // The rows' inputs first, as scalar loads (uniform, read before any other
+    // memory access), whose waits are not tied to the W stream's; then the W
+    // stream before anything else, since every vector load behind it waits
+    // for all of it (loads complete in order for their counter)
+    load_inputs();
+    // packed W: unit (i, t) of this workgroup's block holds columns 4h .. 4h + 3
+    // (h = i % 2) of pair i / 2, already paired (512 x 16 B per instruction);
+    // the LDS image follows, copied by LDS-direct loads (each wave instruction
+    // 1 KB, lane i's 16 bytes at 16 i), waited for before the first barrier
+    const uint4* src = a.Wp + (size_t)g * kPackWgU4 + t;
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) d0[rr] = rr < B ? clamp_token(a.prev_token[rr], V) : 0;
+    for (int i = 0; i < 2 * kResPairs; ++i) {
+      const uint4 v = src[(size_t)i * kResThreads];
+      wr[4 * (i & 1) + 0][i >> 1] = v.x;
+      wr[4 * (i & 1) + 1][i >> 1] = v.y;
+      wr[4 * (i & 1) + 2][i >> 1] = v.z;
+      wr[4 * (i & 1) + 3][i >> 1] = v.w;
+    }
+    unsigned char* dst = reinterpret_cast<unsigned char*>(lds_w) + (size_t)64 * wv * 16;
+#pragma unroll
+    for (int j = 0; j < (int)(kResLdsW / 16 / kResThreads); ++j)
+      __builtin_amdgcn_global_load_lds((lds_gptr_t)(src + kPackRegU4 + (size_t)j * kResThreads),
+                                       (lds_lptr_t)(dst + (size_t)j * kResThreads * 16), 16, 0, 0);
+    set_rows();
+    // position 0's E rows, noise and base logits, and the arrival, all issued
+    // before any is waited for (only the first barrier needs them)
+    uint32_t e0 = 0u;
+    if (t < RB * (kResRank / 2)) {
+      const int rr = t / (kResRank / 2), jj = t % (kResRank / 2);
+      int tok = d0[0];
+#pragma unroll
+      for (int q = 1; q < RB; ++q)
+        if (rr == q) tok = d0[q];
+      if (rr < B && jj < r / 2) e0 = reinterpret_cast<const uint32_t*>(a.E)[(size_t)tok * (r / 2) + jj];
+    }
+    prepare(0);
+    if (t == 0) arrival = __hip_atomic_fetch_add(&a.ex->arrivals, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < RB * (kResRank / 2)) lds_e[t] = e0;
+  } else {
+    // W [r, V] itself: the arrival and the rows' inputs first, then W (8 rank
+    // rows of the VGPR unit per batch, 512 threads x 8 x 16 B = 64 KB in flight
+    // per workgroup, paired in registers; then the LDS units the same way)
+    if (t == 0) arrival = __hip_atomic_fetch_add(&a.ex->arrivals, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    load_inputs();
+    set_rows();
+    {
+      const bool ok = reg_ok && j_ok;
+      const uint16_t* src = a.W + (ok ? (size_t)(32 * js) * V + col0 + 8 * cg_r : 0);
+      const size_t stride = ok ? (size_t)V : 0;
+#pragma unroll
+      for (int b8 = 0; b8 < 4; ++b8) {
+        uint4 raw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (8 * b8 + i) * stride);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          uint32_t pr[8];
+          pack_pairs(raw[2 * pp], raw[2 * pp + 1], pr);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) wr[c][4 * b8 + pp] = pr[c];
+        }
+      }
+    }
+    if (lds_ok) {
+      const uint16_t* src = a.W + (j_ok ? (size_t)(32 * js) * V + col0 + 8 * cg_l : 0);
+      const size_t stride = j_ok ? (size_t)V : 0;
+#pragma unroll
+      for (int b8 = 0; b8 < 4; ++b8) {
+        uint4 raw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(src + (8 * b8 + i) * stride);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          uint32_t pr[8];
+          pack_pairs(raw[2 * pp], raw[2 * pp + 1], pr);
+          uint4* dst = reinterpret_cast<uint4*>(lds_w + ((size_t)(4 * b8 + pp) * kResLdsUnits + t) * 8);
+          dst[0] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+          dst[1] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+        }
+      }
+    }
     gather_e(d0);
+    prepare(0);
   }
-  prepare(0);
-  if (t == 0) s_call = call0;
+  if (t == 0) {
+    s_fail = 0;
+    s_call = arrival / (unsigned long long)G;   // as res_arrive
+  }
+  if constexpr (kPacked) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS-direct loads have landed
   __syncthreads();
   // the call's parity, wave-uniform (a scalar register); the full index is
   // read from LDS only where a wait expires
@@ -1488,11 +1567,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // AGPRs on its own and copies each one back to VGPRs before every use (four
 // VALU moves per instruction).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) void* lds_gptr_t;   // global source of an LDS-direct load
-typedef __attribute__((address_space(3))) void* lds_lptr_t;   // its LDS destination
 __device__ __forceinline__ u32x4_t in_agpr(u32x4_t v) {
   u32x4_t r;
   asm volatile("; W fragment kept in AGPRs %0" : "=a"(r) : "0"(v));
+  return r;
+}
+// The same for a fragment loaded from memory: not volatile, so the scheduler
+// may issue every load before the first of these (a volatile one would keep
+// each load's wait in program order: one memory round trip per fragment).
+__device__ __forceinline__ u32x4_t in_agpr_loaded(u32x4_t v) {
+  u32x4_t r;
+  asm("; W fragment kept in AGPRs %0" : "=a"(r) : "0"(v));
   return r;
 }
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, uint4 b, f32x4_t c) {
@@ -1536,6 +1621,75 @@ struct LdsChain {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Packed W. W is a weight: the same for every block. dspark_pack_w writes it
+// once in the order in which the two resident kernels hold it on chip, one
+// contiguous block of 401,408 bytes per workgroup and kernel, so that each
+// kernel's setup is one coalesced stream (and its LDS part a linear copy by
+// LDS-direct loads) instead of 16-byte pieces from 256 rank rows 400 KB apart.
+// Region 0, the small-batch kernel (slice a multiple of 8 columns): 32 x 512
+// units, unit (i, t) = thread t's 16 bytes of its W pairs, i = 2 p + h (pair
+// p, columns 4h .. 4h + 3 of the thread's 8), then the LDS image [16][272][8]
+// dwords. Region 1, the MFMA kernel (slice a multiple of 16): 64 x 256 units,
+// unit (f, t) = thread t's A fragment f = 8 mt + ks, then the LDS-tile image
+// [17][8][64] fragments. A fragment of M-tile T, K-step ks, lane L holds the 8
+// bf16 of column 16 T + L % 16, rank rows 32 ks + 8 (L / 16) .. + 7; a pair
+// dword rows 2p (low half) and 2p + 1. Past the rank or the slice: zeros.
+static_assert(kMfTilesPerWave * kMfKSteps * kMfThreads == kPackRegU4, "MFMA register units");
+static_assert((size_t)kPackRegU4 * 16 + kMfLdsW == kPackWgU4 * 16, "MFMA block size");
+
+struct PackArgs {
+  const uint16_t* W;   // [r, V]
+  uint4* out;          // [2][G][kPackWgU4]
+  int V, r, G, slice8, slice16;
+};
+
+__device__ __forceinline__ uint32_t packed_w_at(const PackArgs& a, int row, int col0, int ncols, int c) {
+  return (row < a.r && c < ncols) ? (uint32_t)a.W[(size_t)row * a.V + col0 + c] : 0u;
+}
+
+__global__ __launch_bounds__(256) void pack_w(PackArgs a) {
+  const size_t per = (size_t)a.G * kPackWgU4;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= 2 * per) return;
+  const bool mf = idx >= per;
+  const size_t j = mf ? idx - per : idx;
+  const int g = (int)(j / kPackWgU4), x = (int)(j % kPackWgU4);
+  uint32_t d[4];
+  if (!mf) {
+    const int col0 = g * a.slice8, ncols = max(0, min(a.slice8, a.V - col0));
+    int js, cg, pr, h;
+    if (x < kPackRegU4) {            // thread t's VGPR unit: rank slice t % 8, column group 8 (t / 64) + t % 64 / 8
+      const int i = x / kResThreads, t = x % kResThreads;
+      js = t & 7; cg = 8 * (t >> 6) + ((t & 63) >> 3); pr = i >> 1; h = i & 1;
+    } else {                         // LDS unit u: rank slice u % 8, column group 64 + u / 8
+      const int y = x - kPackRegU4, u = (y % (2 * kResLdsUnits)) >> 1;
+      pr = y / (2 * kResLdsUnits); h = y & 1; js = u & 7; cg = kResRegGroups + (u >> 3);
+    }
+    const int row = 32 * js + 2 * pr;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = 8 * cg + 4 * h + jj;
+      d[jj] = packed_w_at(a, row, col0, ncols, c) | (packed_w_at(a, row + 1, col0, ncols, c) << 16);
+    }
+  } else {
+    const int col0 = g * a.slice16, ncols = max(0, min(a.slice16, a.V - col0));
+    int T, ks, L;
+    if (x < kPackRegU4) {            // thread t's fragment f: M-tile 8 (t / 64) + f / 8, K-step f % 8
+      const int f = x / kMfThreads, t = x % kMfThreads;
+      T = kMfTilesPerWave * (t >> 6) + f / kMfKSteps; ks = f % kMfKSteps; L = t & 63;
+    } else {                         // LDS-tile fragment: M-tile 32 + fr / 8, K-step fr % 8
+      const int y = x - kPackRegU4, fr = y >> 6;
+      L = y & 63; T = kMfRegTiles + fr / kMfKSteps; ks = fr % kMfKSteps;
+    }
+    const int c = 16 * T + (L & 15), row = 32 * ks + 8 * (L >> 4);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      d[e2] = packed_w_at(a, row + 2 * e2, col0, ncols, c) | (packed_w_at(a, row + 2 * e2 + 1, col0, ncols, c) << 16);
+  }
+  a.out[idx] = make_uint4(d[0], d[1], d[2], d[3]);
+}
+
 struct MfArgs {
   const void* base;
   const uint16_t* E;
@@ -1553,6 +1707,7 @@ struct MfArgs {
   const void* zeros;   // that were spilled to vector lanes and reloaded every tile)
   Stat* stat_part;     // [K][B][G]
   float* sink;         // [kMfSinkFloats] stores of lanes without a real row or column
+  const u32x4_t* Wp;   // packed W, this kernel's layout (kPacked), else unused
   int B, K, V, r, slice;
   unsigned spin_limit; // reads of a word before its wait expires (0: expires at once)
 };
@@ -1734,7 +1889,7 @@ __device__ __forceinline__ void mf_store_erow(unsigned char* ebuf, int t, const 
   dst[1] = make_uint4(v.hi.x & m, v.hi.y & m, v.hi.z & m, v.hi.w & m);
 }
 
-template <bool kBf16Base, bool kRagged>
+template <bool kBf16Base, bool kRagged, bool kPacked>
 __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resident_mfma(MfArgs a) {
   extern __shared__ __align__(16) unsigned char mf_lds[];
   unsigned char* lds_w = mf_lds;                         // [17][8][64][16 B] fragments
@@ -1767,6 +1922,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
     s_d[b] = clamp_token(a.prev_token[b], V);
   }
 
+
   // ---- (1) VGPR M-tiles 8w..8w+7, in two rounds of four K-steps. In each,
   // rank rows 128 h .. 128 h + 127 of the slice's first 512 columns are copied
   // into the (not yet used) LDS-tile region by LDS-direct loads (one 1 KB row
@@ -1775,7 +1931,30 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
   // region; then every wave gathers its A fragments from there (lane l:
   // column l % 16 of the tile, rank rows 8 (l / 16) .. + 7).
   u32x4_t wf[kMfTilesPerWave][kMfKSteps];   // A fragments, kept in AGPRs
-  {
+  if constexpr (kPacked) {
+    // packed W: thread t's fragment f = 8 mt + ks is unit (f, t) of this
+    // workgroup's block (256 x 16 B per instruction); the LDS-tile image
+    // follows it, copied by LDS-direct loads (each wave instruction 1 KB, lane
+    // i's 16 bytes at 16 i), issued first (they need no registers) and waited
+    // for before the barrier below
+    const u32x4_t* src = a.Wp + (size_t)g * kPackWgU4 + t;
+    unsigned char* dst = lds_w + (size_t)64 * wv * 16;
+#pragma unroll
+    for (int j = 0; j < (int)(kMfLdsW / 16 / kMfThreads); ++j)
+      __builtin_amdgcn_global_load_lds((lds_gptr_t)(src + kPackRegU4 + (size_t)j * kMfThreads),
+                                       (lds_lptr_t)(dst + (size_t)j * kMfThreads * 16), 16, 0, 0);
+    // the two fragments that stay in VGPRs first, then the 62 kept in AGPRs
+    constexpr int kLastMt = kMfTilesPerWave - 1;
+#pragma unroll
+    for (int ks = kMfKSteps - 2; ks < kMfKSteps; ++ks)
+      wf[kLastMt][ks] = src[(size_t)(kLastMt * kMfKSteps + ks) * kMfThreads];
+#pragma unroll
+    for (int mt = 0; mt < kMfTilesPerWave; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < kMfKSteps; ++ks)
+        if (!(mt == kLastMt && ks >= kMfKSteps - 2))
+          wf[mt][ks] = in_agpr_loaded(src[(size_t)(mt * kMfKSteps + ks) * kMfThreads]);
+  } else {
     constexpr int kStageRow = 2 * 16 * kMfRegTiles + 16;       // bytes per staged row (1 KB + pad)
     constexpr int kRoundRows = kResRank / 2;                   // 128
     constexpr int kRowsPerWave = kRoundRows / kMfWaves;        // 32
@@ -1818,51 +1997,52 @@ __global__ __launch_bounds__(kMfThreads, 1) void markov_bias_gumbel_argmax_resid
       }
       __syncthreads();   // the staging area is overwritten next
     }
-  }
 
-  // ---- (2) LDS M-tiles 32..48: each 16-byte load (8 columns of one rank row)
-  // is scattered into the fragment layout (element e of lane l at byte l*16 + 2e).
-  // Consecutive threads take consecutive rank rows (so the 2-byte stores of a
-  // wave spread over the LDS banks); each thread issues its loads in batches
-  // of 17 before storing any (one memory latency per batch, not per item).
-  // Beyond the rank or the slice a valid address is read and the value zeroed
-  // when stored.
-  {
-    constexpr int kItems = kMfLdsTiles * kResRank * 2;         // 8704
-    constexpr int kPerThread = kItems / kMfThreads;            // 34
-    constexpr int kBatch = 17;
-    static_assert(kItems % kMfThreads == 0 && kPerThread % kBatch == 0, "item split");
+    // ---- (2) LDS M-tiles 32..48: each 16-byte load (8 columns of one rank row)
+    // is scattered into the fragment layout (element e of lane l at byte l*16 + 2e).
+    // Consecutive threads take consecutive rank rows (so the 2-byte stores of a
+    // wave spread over the LDS banks); each thread issues its loads in batches
+    // of 17 before storing any (one memory latency per batch, not per item).
+    // Beyond the rank or the slice a valid address is read and the value zeroed
+    // when stored.
+    {
+      constexpr int kItems = kMfLdsTiles * kResRank * 2;         // 8704
+      constexpr int kPerThread = kItems / kMfThreads;            // 34
+      constexpr int kBatch = 17;
+      static_assert(kItems % kMfThreads == 0 && kPerThread % kBatch == 0, "item split");
 #pragma unroll
-    for (int b0 = 0; b0 < kPerThread; b0 += kBatch) {
-      uint4 v[kBatch];
+      for (int b0 = 0; b0 < kPerThread; b0 += kBatch) {
+        uint4 v[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int q = t + (b0 + u) * kMfThreads;
-        const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
-        const int j = rem / 2, h = rem % 2;
-        const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
-        const bool ok = j < r && c8 < ncols;
-        v[u] = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)j * V + col0 + c8 : 0));
-      }
+        for (int u = 0; u < kBatch; ++u) {
+          const int q = t + (b0 + u) * kMfThreads;
+          const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
+          const int j = rem / 2, h = rem % 2;
+          const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
+          const bool ok = j < r && c8 < ncols;
+          v[u] = *reinterpret_cast<const uint4*>(a.W + (ok ? (size_t)j * V + col0 + c8 : 0));
+        }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int q = t + (b0 + u) * kMfThreads;
-        const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
-        const int j = rem / 2, h = rem % 2;
-        const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
-        const uint32_t m = (j < r && c8 < ncols) ? ~0u : 0u;
-        const uint32_t w4[4] = {v[u].x & m, v[u].y & m, v[u].z & m, v[u].w & m};
-        unsigned char* frag = lds_w + ((size_t)ti * kMfKSteps + j / 32) * 1024;
-        const int lbase = 8 * h + 16 * ((j % 32) / 8);
+        for (int u = 0; u < kBatch; ++u) {
+          const int q = t + (b0 + u) * kMfThreads;
+          const int ti = q / (kResRank * 2), rem = q % (kResRank * 2);
+          const int j = rem / 2, h = rem % 2;
+          const int c8 = 16 * (kMfRegTiles + ti) + 8 * h;
+          const uint32_t m = (j < r && c8 < ncols) ? ~0u : 0u;
+          const uint32_t w4[4] = {v[u].x & m, v[u].y & m, v[u].z & m, v[u].w & m};
+          unsigned char* frag = lds_w + ((size_t)ti * kMfKSteps + j / 32) * 1024;
+          const int lbase = 8 * h + 16 * ((j % 32) / 8);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint16_t val = (uint16_t)(w4[c / 2] >> (16 * (c % 2)));
-          *reinterpret_cast<uint16_t*>(frag + (lbase + c) * 16 + 2 * (j % 8)) = val;
+          for (int c = 0; c < 8; ++c) {
+            const uint16_t val = (uint16_t)(w4[c / 2] >> (16 * (c % 2)));
+            *reinterpret_cast<uint16_t*>(frag + (lbase + c) * 16 + 2 * (j % 8)) = val;
+          }
         }
       }
     }
   }
 
+  if constexpr (kPacked) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS-direct loads have landed
   __syncthreads();
 
   // ---- (3) the E rows of N-tiles 0 and 1 of position 0. Every N-tile nt
@@ -2598,13 +2778,13 @@ DeviceInfo g_devices[kMaxDevices];
 // value of its capture).
 unsigned g_wait_limit = kDefaultWaitLimit;
 
-template <int RB, bool kBf16>
+template <int RB, bool kBf16, bool kPacked>
 bool prepare_resident_kernel() {
-  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident<RB, kBf16>);
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident<RB, kBf16, kPacked>);
   int occ = 0;
   const bool ok =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResLdsBytes) == hipSuccess &&
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident<RB, kBf16>,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident<RB, kBf16, kPacked>,
                                                    kResThreads, kResLdsBytes) == hipSuccess;
   // a probe that fails only rules the plan out: clear the error it leaves
   // behind, or the caller's next HIP call would report it
@@ -2612,13 +2792,13 @@ bool prepare_resident_kernel() {
   return ok && occ >= 1;
 }
 
-template <bool kBf16, bool kRagged>
+template <bool kBf16, bool kRagged, bool kPacked>
 bool prepare_mfma_kernel() {
-  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>);
+  const void* fn = reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged, kPacked>);
   int occ = 0;
   const bool ok =
       hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMfLdsBytes) == hipSuccess &&
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged>,
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, markov_bias_gumbel_argmax_resident_mfma<kBf16, kRagged, kPacked>,
                                                    kMfThreads, kMfLdsBytes) == hipSuccess;
   if (!ok) (void)hipGetLastError();
   return ok && occ >= 1;
@@ -2633,12 +2813,17 @@ int init_device() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return DSPARK_ERR_HIP;
   bool ok = cus > 0 && cus <= kResMaxCUs;
-  ok = ok && prepare_resident_kernel<1, false>() && prepare_resident_kernel<1, true>();
-  ok = ok && prepare_resident_kernel<2, false>() && prepare_resident_kernel<2, true>();
-  ok = ok && prepare_resident_kernel<4, false>() && prepare_resident_kernel<4, true>();
+  ok = ok && prepare_resident_kernel<1, false, false>() && prepare_resident_kernel<1, true, false>();
+  ok = ok && prepare_resident_kernel<2, false, false>() && prepare_resident_kernel<2, true, false>();
+  ok = ok && prepare_resident_kernel<4, false, false>() && prepare_resident_kernel<4, true, false>();
+  ok = ok && prepare_resident_kernel<1, false, true>() && prepare_resident_kernel<1, true, true>();
+  ok = ok && prepare_resident_kernel<2, false, true>() && prepare_resident_kernel<2, true, true>();
+  ok = ok && prepare_resident_kernel<4, false, true>() && prepare_resident_kernel<4, true, true>();
   bool mok = cus > 0 && cus <= kResMaxCUs;
-  mok = mok && prepare_mfma_kernel<false, false>() && prepare_mfma_kernel<true, false>();
-  mok = mok && prepare_mfma_kernel<false, true>() && prepare_mfma_kernel<true, true>();
+  mok = mok && prepare_mfma_kernel<false, false, false>() && prepare_mfma_kernel<true, false, false>();
+  mok = mok && prepare_mfma_kernel<false, true, false>() && prepare_mfma_kernel<true, true, false>();
+  mok = mok && prepare_mfma_kernel<false, false, true>() && prepare_mfma_kernel<true, false, true>();
+  mok = mok && prepare_mfma_kernel<false, true, true>() && prepare_mfma_kernel<true, true, true>();
   // the device's own copy of the exchange state: its address from the symbol
   // (the name itself is no device address in host code)
   void* ex = nullptr;
@@ -2756,14 +2941,40 @@ inline size_t plan_layout(const Plan& plan, int B, int K, int r, Workspace* ws, 
 
 // workspace == nullptr with use_scratch: the call lays its workspace out in the
 // device's scratch array (dspark_draft_block_noalloc).
+// Packed-W geometry on the current device: the two kernels' slices (multiples
+// of 8 and of 16 columns) and the bytes of both regions; 0 bytes when no
+// resident plan can run these sizes (then there is nothing to pack).
+struct PackGeom {
+  int G, slice8, slice16;
+  size_t bytes;
+};
+inline PackGeom packed_w_geom(int V, int r) {
+  PackGeom pg{0, 0, 0, 0};
+  if (V <= 0 || r <= 0 || V % 8 != 0 || r % 32 != 0 || r > kResRank || V > (int)kResIdxMask + 1) return pg;
+  if (init_device() != DSPARK_OK) return pg;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return pg;
+  const int G = g_devices[dev].cus;
+  if (G <= 0 || G > kResMaxCUs) return pg;
+  pg.G = G;
+  pg.slice8 = ((V + G - 1) / G + 7) / 8 * 8;
+  pg.slice16 = ((V + G - 1) / G + 15) / 16 * 16;
+  if (pg.slice16 > kResSlice) return pg;
+  pg.bytes = 2 * (size_t)G * kPackWgU4 * 16;
+  return pg;
+}
+inline size_t packed_w_bytes(int V, int r) { return packed_w_geom(V, r).bytes; }
+
 int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const uint16_t* W,
                      const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
                      const float* temperature, const int32_t* n_real, int B, int K, int V, int r,
                      int chunk_cols, int32_t* tokens, float* logits, float* q, void* workspace,
                      size_t workspace_bytes, void* stream_ptr, void* const* events = nullptr,
-                     int n_events = 0, bool use_scratch = false) {
+                     int n_events = 0, bool use_scratch = false, const void* W_packed = nullptr,
+                     size_t packed_bytes = 0) {
   int rc = check_sizes(B, K, V, r);
   if (rc != DSPARK_OK) return rc;
+  const bool packed = W_packed != nullptr;
   if (base_dtype != DSPARK_F32 && base_dtype != DSPARK_BF16) return DSPARK_ERR_ARG;
   if (chunk_cols < 0 || chunk_cols % kTile != 0) return DSPARK_ERR_UNSUPPORTED;
   const bool explicit_chunk = chunk_cols != 0;
@@ -2774,10 +2985,13 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
     return DSPARK_ERR_ARG;
   if (!aligned16(base) || !aligned16(E) || !aligned16(W) || !aligned16(logits) || !aligned16(q))
     return DSPARK_ERR_ARG;
+  if (packed && !aligned16(W_packed)) return DSPARK_ERR_ARG;
   if (!use_scratch) {
     const size_t need = workspace_layout(B, K, V, r, nullptr, nullptr);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
   }
+  // the packed copy must be this device's, for these sizes (its size says so)
+  if (packed && packed_bytes != packed_w_bytes(V, r)) return DSPARK_ERR_ARG;
 
   Plan plan;
   rc = make_plan(B, K, V, r, explicit_chunk ? chunk_cols : 0, &plan);
@@ -2820,14 +3034,21 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
       const dim3 mblock(kMfThreads);
       // columns come in whole tiles of 16 unless the vocabulary is ragged
       const bool ragged = V % 16 != 0;
-      if (bf16 && !ragged)
-        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, false>), grid, mblock, kMfLdsBytes, stream, ma);
-      else if (!ragged)
-        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, false>), grid, mblock, kMfLdsBytes, stream, ma);
-      else if (bf16)
-        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<true, true>), grid, mblock, kMfLdsBytes, stream, ma);
-      else
-        hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<false, true>), grid, mblock, kMfLdsBytes, stream, ma);
+      ma.Wp = packed ? reinterpret_cast<const u32x4_t*>(W_packed) + (size_t)G * kPackWgU4 : nullptr;
+#define DSPARK_LAUNCH_MF(BF, RG, PK) \
+  hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident_mfma<BF, RG, PK>), grid, mblock, kMfLdsBytes, stream, ma)
+      if (packed) {
+        if (bf16 && !ragged) DSPARK_LAUNCH_MF(true, false, true);
+        else if (!ragged) DSPARK_LAUNCH_MF(false, false, true);
+        else if (bf16) DSPARK_LAUNCH_MF(true, true, true);
+        else DSPARK_LAUNCH_MF(false, true, true);
+      } else {
+        if (bf16 && !ragged) DSPARK_LAUNCH_MF(true, false, false);
+        else if (!ragged) DSPARK_LAUNCH_MF(false, false, false);
+        else if (bf16) DSPARK_LAUNCH_MF(true, true, false);
+        else DSPARK_LAUNCH_MF(false, true, false);
+      }
+#undef DSPARK_LAUNCH_MF
     } else {
       ResArgs ra;
       ra.base = base; ra.E = E; ra.W = W; ra.prev_token = prev_token; ra.seed = seed; ra.offset = offset;
@@ -2836,16 +3057,19 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
       ra.B = B; ra.K = K; ra.V = V; ra.r = r; ra.slice = slice;
       ra.spin_limit = g_wait_limit;
       const dim3 block(kResThreads);
-      if (B == 1) {
-        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, true>), grid, block, kResLdsBytes, stream, ra);
-        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<1, false>), grid, block, kResLdsBytes, stream, ra);
-      } else if (B == 2) {
-        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, true>), grid, block, kResLdsBytes, stream, ra);
-        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<2, false>), grid, block, kResLdsBytes, stream, ra);
-      } else {
-        if (bf16) hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, true>), grid, block, kResLdsBytes, stream, ra);
-        else hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<4, false>), grid, block, kResLdsBytes, stream, ra);
-      }
+      ra.Wp = packed ? reinterpret_cast<const uint4*>(W_packed) : nullptr;
+#define DSPARK_LAUNCH_RES(RBV, BF, PK) \
+  hipLaunchKernelGGL((markov_bias_gumbel_argmax_resident<RBV, BF, PK>), grid, block, kResLdsBytes, stream, ra)
+#define DSPARK_LAUNCH_RES_B(PK)                                                       \
+  do {                                                                                \
+    if (B == 1) { if (bf16) DSPARK_LAUNCH_RES(1, true, PK); else DSPARK_LAUNCH_RES(1, false, PK); } \
+    else if (B == 2) { if (bf16) DSPARK_LAUNCH_RES(2, true, PK); else DSPARK_LAUNCH_RES(2, false, PK); } \
+    else { if (bf16) DSPARK_LAUNCH_RES(4, true, PK); else DSPARK_LAUNCH_RES(4, false, PK); } \
+  } while (0)
+      if (packed) DSPARK_LAUNCH_RES_B(true);
+      else DSPARK_LAUNCH_RES_B(false);
+#undef DSPARK_LAUNCH_RES_B
+#undef DSPARK_LAUNCH_RES
     }
     if (hipGetLastError() != hipSuccess || !mark()) return DSPARK_ERR_HIP;
   }
@@ -3027,10 +3251,15 @@ int dspark_init(void) {
       reinterpret_cast<const void*>(&vblock_partials<1>),
       reinterpret_cast<const void*>(&vblock_partials<2>),
       reinterpret_cast<const void*>(&vblock_finish),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true>),
-      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, true, false>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, false, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, false, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<false, true, true>),
+      reinterpret_cast<const void*>(&markov_bias_gumbel_argmax_resident_mfma<true, true, true>),
+      reinterpret_cast<const void*>(&pack_w),
   };
   for (const void* kfn : kernels)
     if (hipFuncGetAttributes(&attr, kfn) != hipSuccess) return DSPARK_ERR_HIP;
@@ -3109,6 +3338,35 @@ int dspark_draft_block_events(const void* base_logits, int base_dtype, const uin
   return dspark::draft_block_impl(base_logits, base_dtype, E, W, prev_token, seed, offset, temperature,
                                   n_real, B, K, V, r, 0, tokens, logits_f32, draft_probs, workspace,
                                   workspace_bytes, stream, events, n_events);
+}
+
+size_t dspark_packed_w_bytes(int V, int r) { return dspark::packed_w_bytes(V, r); }
+
+int dspark_pack_w(const uint16_t* W, int V, int r, void* W_packed, size_t packed_bytes, void* stream) {
+  using namespace dspark;
+  if (V <= 0 || r <= 0) return DSPARK_ERR_ARG;
+  const PackGeom pg = packed_w_geom(V, r);
+  if (pg.bytes == 0) return DSPARK_ERR_UNSUPPORTED;
+  if (!W || !W_packed || packed_bytes < pg.bytes || !aligned16(W_packed)) return DSPARK_ERR_ARG;
+  PackArgs pa;
+  pa.W = W; pa.out = static_cast<uint4*>(W_packed);
+  pa.V = V; pa.r = r; pa.G = pg.G; pa.slice8 = pg.slice8; pa.slice16 = pg.slice16;
+  const size_t units = pg.bytes / 16;
+  hipLaunchKernelGGL(pack_w, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream), pa);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+int dspark_draft_block_packed(const void* base_logits, int base_dtype, const uint16_t* E, const uint16_t* W,
+                              const void* W_packed, size_t packed_bytes, const int32_t* prev_token,
+                              const int64_t* seed, const int64_t* offset, const float* temperature,
+                              const int32_t* n_real, int B, int K, int V, int r, int32_t* tokens,
+                              float* logits_f32, float* draft_probs, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int n_events) {
+  if (!W_packed) return DSPARK_ERR_ARG;
+  return dspark::draft_block_impl(base_logits, base_dtype, E, W, prev_token, seed, offset, temperature,
+                                  n_real, B, K, V, r, 0, tokens, logits_f32, draft_probs, workspace,
+                                  workspace_bytes, stream, events, events ? n_events : 0, false, W_packed,
+                                  packed_bytes);
 }
 
 int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds) {

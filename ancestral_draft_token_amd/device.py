@@ -12,13 +12,14 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (DSPARK_BF16, DSPARK_F32, dspark_draft_block, dspark_init, dspark_workspace_bytes)
+from . import (DSPARK_BF16, DSPARK_F32, dspark_draft_block, dspark_init, dspark_pack_w, dspark_packed_w_bytes,
+               dspark_workspace_bytes)
 from .inputs import Workload
 
 
 class DeviceProblem:
     def __init__(self, w: Workload, device: str = "cuda:0", chunk_cols: Optional[int] = None,
-                 workspace: Optional[torch.Tensor] = None):
+                 workspace: Optional[torch.Tensor] = None, packed: bool = False):
         self.w = w
         self.device = torch.device(device)
         self.chunk_cols = chunk_cols
@@ -50,6 +51,14 @@ class DeviceProblem:
             self.workspace = workspace
         else:
             self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        # W packed once for the resident kernels (a weight: the same for every block)
+        self.W_packed, self.packed_bytes = None, 0
+        if packed and chunk_cols is None:
+            self.packed_bytes = dspark_packed_w_bytes(V, r)
+            if self.packed_bytes:
+                self.W_packed = torch.empty(self.packed_bytes, dtype=torch.uint8, device=dev)
+                dspark_pack_w(self.W, V, r, self.W_packed, self.packed_bytes)
+                torch.cuda.synchronize(dev)
 
     def enqueue(self, stream=None, **overrides) -> int:
         """Enqueue one block on ``stream`` (torch stream / raw handle / None = current)."""
@@ -60,6 +69,8 @@ class DeviceProblem:
                   tokens=self.tokens, logits_f32=self.logits, draft_probs=self.q,
                   workspace=self.workspace, workspace_bytes=self.ws_bytes, stream=stream,
                   chunk_cols=self.chunk_cols)
+        if self.W_packed is not None:
+            kw.update(W_packed=self.W_packed, packed_bytes=self.packed_bytes)
         kw.update(overrides)
         return dspark_draft_block(**kw)
 

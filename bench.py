@@ -78,13 +78,15 @@ def algorithmic_bytes(w, resident):
 
 
 class Bench:
-    def __init__(self, w, mall="cold"):
+    def __init__(self, w, mall="cold", packed=True):
         import torch
         from ancestral_draft_token_amd.device import DeviceProblem
         self.torch = torch
         self.w = w
         self.mall = mall
-        self.p = DeviceProblem(w)
+        # W packed once for the resident kernels (dspark_pack_w), outside the
+        # timed region: a weight, laid out at load time
+        self.p = DeviceProblem(w, packed=packed)
         self.stream = torch.cuda.Stream()
         self.flush_buf = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda:0")
         self.flush_out = torch.empty((), dtype=torch.float32, device="cuda:0")
@@ -396,8 +398,8 @@ def kernel_roofline(w, r, args):
     return out
 
 
-def measure(w, steps, warmup, mall, kernel_reps=5):
-    b = Bench(w, mall=mall)
+def measure(w, steps, warmup, mall, kernel_reps=5, packed=True):
+    b = Bench(w, mall=mall, packed=packed)
     b.steps(warmup)
     torch = b.torch
     torch.cuda.synchronize()
@@ -435,6 +437,8 @@ def main():
     ap.add_argument("--workload", default="b1", choices=["tiny", "b1", "b8", "b44", "b88"])
     ap.add_argument("--mall", default="cold", choices=["cold", "warm"])
     ap.add_argument("--no-sweep", action="store_true", help="skip the B=8/44/88 lines in 'also'")
+    ap.add_argument("--w-layout", default="packed", choices=["packed", "plain"],
+                    help="W as packed once by dspark_pack_w (default) or read from [r, V] itself")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--pmc-run", action="store_true",
                     help="for rocprofv3 --pmc: a calibration copy of known size, then a few replays")
@@ -455,6 +459,7 @@ def main():
         sys.exit(1)
 
     w = inputs.WORKLOADS[args.workload]()
+    packed = args.w_layout == "packed"
     if args.pmc_run or args.attention_run:
         from ancestral_draft_token_amd.profiling import COPY_BYTES
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
@@ -468,14 +473,14 @@ def main():
             r = measure_attention(shape, reps=max(3, args.steps), mall=args.mall, layout=layout)
             print(json.dumps({"attention": attention_workload(shape, layout), **r}), flush=True)
             return
-        b = Bench(w, mall=args.mall)
+        b = Bench(w, mall=args.mall, packed=packed)
         b.steps(max(3, args.steps))
         torch.cuda.synchronize()
         print(f"[bench] pmc run done: {w.name}", file=sys.stderr, flush=True)
         return
     print(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}, MALL {args.mall}",
           file=sys.stderr, flush=True)
-    r = measure(w, args.steps, args.warmup, args.mall)
+    r = measure(w, args.steps, args.warmup, args.mall, packed=packed)
     copy = copy_bandwidth()
     line = {
         "metric": METRIC,
@@ -493,6 +498,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "B_real": w.n_real_rows, "K": w.K, "V": w.V,
                    "r": w.r, "base": w.base_dtype, "mall": args.mall,
                    "graph": "one hipGraph per block", "launches": r["plan"],
+                   "w_layout": args.w_layout,
                    "hip_graph_packet_capture": os.environ.get("DEBUG_CLR_GRAPH_PACKET_CAPTURE")},
         "us_median": round(r["us_median"], 2),
         "us_p10": round(r["us_p10"], 2),
@@ -512,7 +518,7 @@ def main():
                 continue
             wo = inputs.WORKLOADS[name]()
             print(f"[bench] also {wo.name}", file=sys.stderr, flush=True)
-            ro = measure(wo, max(20, args.steps), max(5, args.warmup), args.mall)
+            ro = measure(wo, max(20, args.steps), max(5, args.warmup), args.mall, packed=packed)
             also[name] = {"workload": wo.name, "us_per_block": round(ro["us_per_block"], 2),
                           "us_median": round(ro["us_median"], 2),
                           "block_roofline_frac": round(ro["block_gbs"] / HBM_PEAK_GBS, 4),
@@ -526,7 +532,7 @@ def main():
             line["roofline_b88"] = also["b88"]["roofline"]
         if args.mall == "cold":
             print(f"[bench] warm MALL {w.name}", file=sys.stderr, flush=True)
-            rw = measure(w, max(10, args.steps // 2), 3, "warm")
+            rw = measure(w, max(10, args.steps // 2), 3, "warm", packed=packed)
             line["warm"] = {"workload": w.name, "mall": "warm", "us_per_block": round(rw["us_per_block"], 2),
                             "block_roofline_frac": round(rw["block_gbs"] / HBM_PEAK_GBS, 4),
                             "kernels_us": {k: round(v, 2) for k, v in rw["kernels_us"].items()}}

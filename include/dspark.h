@@ -178,6 +178,45 @@ int dspark_draft_block_events(
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int n_events);
 
+/* W packed for the resident kernels. W is a weight, the same for every
+ * block, so it can be laid out once in the order in which the two resident
+ * kernels (see dspark_launch_plan) hold it on chip: for each kernel, one
+ * contiguous block per compute unit of this device with that unit's slice of
+ * W (784 columns x 256 rank rows, bf16, zero past r and past V), then each
+ * kernel's setup is one coalesced stream instead of 16-byte pieces of 256
+ * rank rows. The bias it computes is the pages' E[d] . W ("brb-nv/TensorRT-LLM
+ * pull 27", section "2. One fused kernel per draft position"), bit for bit the
+ * same as from W itself.
+ *
+ * dspark_packed_w_bytes: bytes of the packed copy for V, r on the current
+ * device (2 x 401,408 x its compute units: 205.5 MB on 256), or 0 when no
+ * resident plan can run these sizes (r > 256, V > 2^18, V > 784 x units, or
+ * V % 8 or r % 32 not 0): nothing to pack then.
+ *
+ * dspark_pack_w: enqueues on `stream` the writing of W [r, V] (device bf16)
+ * into W_packed (device, 16-byte aligned, at least dspark_packed_w_bytes).
+ * The copy belongs to this device's compute-unit count: pack on the device
+ * that will use it, and again after W changes. DSPARK_ERR_UNSUPPORTED when
+ * the size is 0, DSPARK_ERR_ARG for null or misaligned pointers or a short
+ * buffer, DSPARK_ERR_HIP if the launch fails. */
+size_t dspark_packed_w_bytes(int V, int r);
+int dspark_pack_w(const uint16_t* W, int V, int r, void* W_packed, size_t packed_bytes, void* stream);
+
+/* dspark_draft_block with W also given packed (dspark_pack_w on this device,
+ * packed_bytes exactly dspark_packed_w_bytes(V, r), else DSPARK_ERR_ARG): the
+ * resident plans read W_packed, the per-position plans W. Same launches and
+ * results as dspark_draft_block, bit for bit. `events` may be NULL; if not, it
+ * and n_events are as for dspark_draft_block_events. */
+int dspark_draft_block_packed(
+    const void* base_logits, int base_dtype,
+    const uint16_t* E, const uint16_t* W, const void* W_packed, size_t packed_bytes,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, const int32_t* n_real,
+    int B, int K, int V, int r,
+    int32_t* tokens, float* logits_f32, float* draft_probs,
+    void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int n_events);
+
 /* Kinds of kernel launch a block is made of. */
 typedef enum {
     DSPARK_LAUNCH_FUSED_POSITION = 0,  /* markov_bias_gumbel_argmax for one position */

@@ -64,6 +64,22 @@ int main(void) {
           DSPARK_ERR_UNSUPPORTED);
     CHECK(dspark_draft_block_events(P, 0, P, P, P, P, P, P, NULL, 2, 7, 4096, 32, P, P, P, P, ws, NULL, NULL, 0) ==
           DSPARK_ERR_ARG);
+    /* packed W: sizes no resident plan runs, bad arguments, the packed block's own checks */
+    const int pVs[] = {-8, 0, 4, 4100, 262152, 1 << 24};
+    const int prs[] = {-32, 0, 48, 288, 1024};
+    for (size_t l = 0; l < sizeof pVs / sizeof *pVs; ++l)
+        for (size_t m = 0; m < sizeof prs / sizeof *prs; ++m) {
+            CHECK(dspark_packed_w_bytes(pVs[l], prs[m]) == 0);
+            CHECK(dspark_pack_w(P, pVs[l], prs[m], P, 1 << 20, NULL) != DSPARK_OK);
+        }
+    CHECK(dspark_draft_block_packed(P, 0, P, P, NULL, 0, P, P, P, P, NULL, 2, 7, 4096, 32, P, P, P, P, ws, NULL, NULL, 0) ==
+          DSPARK_ERR_ARG);
+    CHECK(dspark_draft_block_packed(P, 0, P, P, M, 1, P, P, P, P, NULL, 2, 7, 4096, 32, P, P, P, P, ws, NULL, NULL, 0) ==
+          DSPARK_ERR_ARG);
+    CHECK(dspark_draft_block_packed(P, 0, P, P, P, 1, P, P, P, P, NULL, 2, 7, 4100, 32, P, P, P, P, ws, NULL, NULL, 0) ==
+          DSPARK_ERR_UNSUPPORTED);
+    CHECK(dspark_draft_block_packed(P, 0, P, P, P, 1, P, P, P, P, NULL, 2, 7, 4096, 32, P, P, P, NULL, ws, NULL, NULL, 0) ==
+          DSPARK_ERR_WORKSPACE);
     CHECK(dspark_launch_plan(2, 7, 4100, 32, NULL, 0) == DSPARK_ERR_UNSUPPORTED);
     CHECK(dspark_launch_plan(0, 7, 4096, 32, NULL, 0) == 0);
 

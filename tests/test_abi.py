@@ -125,6 +125,29 @@ def test_noalloc_host_checks(lib):
     assert adt.dspark_draft_block_noalloc(**dict(args, B=0, tokens=None)) == adt.DSPARK_OK
 
 
+def test_packed_w_host_checks(lib):
+    """The packed-W entries' checks that need no device: sizes no resident plan
+    runs pack to nothing, bad arguments fail, and the packed block checks its
+    own pointer before the rest (here every call returns before a HIP call)."""
+    assert adt.dspark_packed_w_bytes(4100, 32) == 0          # V % 8 != 0
+    assert adt.dspark_packed_w_bytes(4096, 48) == 0          # r % 32 != 0
+    assert adt.dspark_packed_w_bytes(4096, 512) == 0         # r > 256
+    assert adt.dspark_packed_w_bytes(1 << 19, 32) == 0       # V > 2^18
+    assert adt.dspark_packed_w_bytes(0, 32) == 0
+    assert adt.dspark_pack_w(FAKE, 0, 32, FAKE, 1 << 20, stream=0, check=False) == adt.DSPARK_ERR_ARG
+    assert adt.dspark_pack_w(FAKE, 4096, -32, FAKE, 1 << 20, stream=0, check=False) == adt.DSPARK_ERR_ARG
+    assert adt.dspark_pack_w(FAKE, 4096, 512, FAKE, 1 << 20, stream=0, check=False) == adt.DSPARK_ERR_UNSUPPORTED
+    assert lib.dspark_draft_block_packed(FAKE, 0, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, None, 2, 7, 4096, 32,
+                                         FAKE, FAKE, FAKE, FAKE, 1 << 20, None, None, 0) == adt.DSPARK_ERR_ARG
+    assert call(W_packed=FAKE, packed_bytes=1, V=4100) == adt.DSPARK_ERR_UNSUPPORTED
+    assert call(W_packed=FAKE + 8, packed_bytes=1) == adt.DSPARK_ERR_ARG
+    assert call(W_packed=FAKE, packed_bytes=1, E=None) == adt.DSPARK_ERR_ARG
+    assert call(W_packed=FAKE, packed_bytes=1, workspace=None) == adt.DSPARK_ERR_WORKSPACE
+    assert call(W_packed=FAKE, packed_bytes=1, B=0, tokens=None) == adt.DSPARK_OK
+    with pytest.raises(ValueError):
+        call(W_packed=FAKE, packed_bytes=1, chunk_cols=128)
+
+
 def test_block_status_checks_its_pointer(lib):
     assert lib.dspark_block_status(None, None) == adt.DSPARK_ERR_ARG
 

@@ -45,7 +45,8 @@ import pytest
 from ancestral_draft_token_amd import _build
 
 KERNEL = "markov_bias_gumbel_argmax_resident_mfma"
-VARIANTS = ["ILb0ELb0EE", "ILb1ELb0EE", "ILb0ELb1EE", "ILb1ELb1EE"]   # <bf16 base, ragged vocabulary>
+# <bf16 base, ragged vocabulary, packed W>
+VARIANTS = [f"ILb{b}ELb{g}ELb{p}EE" for p in (0, 1) for g in (0, 1) for b in (0, 1)]
 
 
 @pytest.fixture(scope="module")
