@@ -195,10 +195,13 @@ int dspark_draft_block_events(
  *
  * dspark_pack_w: enqueues on `stream` the writing of W [r, V] (device bf16)
  * into W_packed (device, 16-byte aligned, at least dspark_packed_w_bytes).
- * The copy belongs to this device's compute-unit count: pack on the device
- * that will use it, and again after W changes. DSPARK_ERR_UNSUPPORTED when
- * the size is 0, DSPARK_ERR_ARG for null or misaligned pointers or a short
- * buffer, DSPARK_ERR_HIP if the launch fails. */
+ * The copy belongs to this V, this r and this device's compute-unit count:
+ * pack on the device that will use it, with the sizes the blocks will use,
+ * and again after W changes. Its size depends on the compute-unit count
+ * only, so a copy packed for another V or r is not detected (its blocks are
+ * wrong); one packed on a device with another count is (DSPARK_ERR_ARG).
+ * DSPARK_ERR_UNSUPPORTED when the size is 0, DSPARK_ERR_ARG for null or
+ * misaligned pointers or a short buffer, DSPARK_ERR_HIP if the launch fails. */
 size_t dspark_packed_w_bytes(int V, int r);
 int dspark_pack_w(const uint16_t* W, int V, int r, void* W_packed, size_t packed_bytes, void* stream);
 
