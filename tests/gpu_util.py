@@ -30,12 +30,14 @@ def say(msg: str):
             f.write(f"[gpu] {msg}\n")
 
 
-def run_gpu(w, chunk_cols=None):
-    """Run one block on cuda:0; return (problem, tokens, logits, q) as host arrays."""
+def run_gpu(w, chunk_cols=None, packed=False):
+    """Run one block on cuda:0 (W packed once when ``packed``); return the problem."""
     import torch
     from ancestral_draft_token_amd.device import DeviceProblem
-    say(f"run {w.name} B={w.B} K={w.K} V={w.V} r={w.r} base={w.base_dtype} chunk={chunk_cols}")
-    p = DeviceProblem(w, chunk_cols=chunk_cols)
+    say(f"run {w.name} B={w.B} K={w.K} V={w.V} r={w.r} base={w.base_dtype} chunk={chunk_cols} packed={packed}")
+    p = DeviceProblem(w, chunk_cols=chunk_cols, packed=packed)
+    if packed:
+        assert p.W_packed is not None, "no packed W for this workload"
     p.enqueue()
     torch.cuda.synchronize()
     return p

@@ -44,16 +44,17 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["w", "w_packed"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_expired_wait_is_reported_and_recovers(name):
+def test_expired_wait_is_reported_and_recovers(name, packed):
     from ancestral_draft_token_amd import dspark_launch_plan, dspark_set_wait_limit
     make, rows = CASES[name]
     w = make()
     assert 4 in dspark_launch_plan(w.B, w.K, w.V, w.r), "the workload must take a resident plan"
     prev = dspark_set_wait_limit(0)
     try:
-        say(f"{name}: every device wait expires at once")
-        p = run_gpu(w)
+        say(f"{name}: every device wait expires at once (packed W: {packed})")
+        p = run_gpu(w, packed=packed)
     finally:
         dspark_set_wait_limit(prev)
     assert status_now() == 1
@@ -61,7 +62,7 @@ def test_expired_wait_is_reported_and_recovers(name):
     assert bool(p.q.isnan().all())
     del p
     say(f"{name}: the next call with the default limit")
-    p2 = run_gpu(w)
+    p2 = run_gpu(w, packed=packed)
     assert status_now() == 0
     assert bool(((p2.tokens >= 0) & (p2.tokens < w.V)).all())
     sub, order = w.subset_rows(rows)
