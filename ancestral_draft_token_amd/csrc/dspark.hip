@@ -229,6 +229,32 @@ __device__ __forceinline__ void wave_merge_key_stat(uint64_t& key, Stat& st) {
   row_merge4(key, st);
 }
 
+// The statistics half of wave_merge_key_stat: the same steps in the same
+// order, so the merged (m, l) are bit for bit those it gives.
+__device__ __forceinline__ void wave_merge_stat(Stat& st) {
+#define DSPARK_DPP_MERGE_STAT(ctrl)                                                              \
+  {                                                                                              \
+    const int om = __builtin_amdgcn_update_dpp(0, __float_as_int(st.m), ctrl, 0xF, 0xF, false); \
+    const int ol = __builtin_amdgcn_update_dpp(0, __float_as_int(st.l), ctrl, 0xF, 0xF, false); \
+    st = stat_merge(st, Stat{__int_as_float(om), __int_as_float(ol)});                           \
+  }
+  DSPARK_DPP_MERGE_STAT(0xB1)    // quad_perm(1,0,3,2): lane ^ 1
+  DSPARK_DPP_MERGE_STAT(0x4E)    // quad_perm(2,3,0,1): lane ^ 2
+  DSPARK_DPP_MERGE_STAT(0x141)   // row_half_mirror
+  DSPARK_DPP_MERGE_STAT(0x140)   // row_mirror
+#undef DSPARK_DPP_MERGE_STAT
+#define DSPARK_SWAP_MERGE_STAT(swap)                                                      \
+  {                                                                                      \
+    const auto mm = swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);    \
+    const auto ll = swap(__float_as_uint(st.l), __float_as_uint(st.l), false, false);    \
+    st = stat_merge(Stat{__uint_as_float(mm[0]), __uint_as_float(ll[0])},                 \
+                    Stat{__uint_as_float(mm[1]), __uint_as_float(ll[1])});                \
+  }
+  DSPARK_SWAP_MERGE_STAT(__builtin_amdgcn_permlane16_swap)
+  DSPARK_SWAP_MERGE_STAT(__builtin_amdgcn_permlane32_swap)
+#undef DSPARK_SWAP_MERGE_STAT
+}
+
 // Maximum of a 64-bit value over the lanes of a wave with equal lane % RB
 // (RB = 1, 2 or 4), every lane getting its class's maximum: rotations within
 // 16-lane rows by RB, 2 RB, ... (which keep the class), then the lane swaps
@@ -342,6 +368,21 @@ __device__ __forceinline__ void load_base4(Base4<kBf16Base>& bv, const void* bas
     const f32x4v_t x = kNt ? __builtin_nontemporal_load(p) : *p;
     bv.f = make_float4(x.x, x.y, x.z, x.w);
   }
+}
+
+// The base logit of one column (its bf16 in h.x, or its float in f.x).
+template <bool kBf16Base>
+__device__ __forceinline__ void load_base1(Base4<kBf16Base>& bv, const void* base, size_t off) {
+  if (kBf16Base) {
+    bv.h.x = (uint32_t)__builtin_nontemporal_load(static_cast<const uint16_t*>(base) + off);
+  } else {
+    bv.f.x = __builtin_nontemporal_load(static_cast<const float*>(base) + off);
+  }
+}
+
+template <bool kBf16Base>
+__device__ __forceinline__ float widen_base1(const Base4<kBf16Base>& bv) {
+  return kBf16Base ? __uint_as_float(bv.h.x << 16) : bv.f.x;
 }
 
 template <bool kBf16Base>
@@ -1075,7 +1116,8 @@ __device__ __forceinline__ float dpp_xor1(float x) {
 
 // Reduce-scatter of acc[RB][8] over the 8 rank-slice lanes of a column group
 // (lanes differing in bits 0..2): lane js ends with the sums of 4 columns
-// (4 * (js & 1) ..) of row er (RB = 4: js >> 1; RB = 2: js >> 2; RB = 1: 0).
+// (4 * (js & 1) ..) of row er (RB = 4: js >> 1; RB = 2: js >> 2), or with
+// the sum of column js alone (RB = 1).
 // The three exchange steps pair lanes of opposite bit 2 (by the mirror),
 // then of opposite bit 1, then of opposite bit 0; the mirror pairs 0-7, 1-6,
 // 2-5, 3-4, and the three steps still add every slice exactly once.
@@ -1110,11 +1152,25 @@ __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js
 #pragma unroll
     for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], dpp_xor2(h[c]));
   } else {
-    float h[8];
+    // one row: every step halves the columns a lane keeps, so lane js ends
+    // with column js (bit 2 of js chose the half at the mirror, bit 1 the
+    // quarter, bit 0 the column); bias[0] only
+    float h[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) h[c] = __fadd_rn(acc[0][c], dpp_mirror8(acc[0][c]));
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b2 ? acc[0][4 + i] : acc[0][i];
+      const float send = b2 ? acc[0][i] : acc[0][4 + i];
+      h[i] = __fadd_rn(keep, dpp_mirror8(send));
+    }
+    float q[2];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], dpp_xor2(h[c]));
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b1 ? h[2 + i] : h[i];
+      const float send = b1 ? h[i] : h[2 + i];
+      q[i] = __fadd_rn(keep, dpp_xor2(send));
+    }
+    bias[0] = __fadd_rn(b0 ? q[1] : q[0], dpp_xor1(b0 ? q[0] : q[1]));
+    return;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1122,6 +1178,34 @@ __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js
     const float send = b0 ? h2[i] : h2[4 + i];
     bias[i] = __fadd_rn(keep, dpp_xor1(send));
   }
+}
+
+// Gumbel noise of column v at position k: component v % 4 of the block of
+// columns v - v % 4 .., the value noise4 gives that column.
+__device__ __forceinline__ float noise1(const RowState& rs, int k, uint32_t v) {
+  const uint4 x = philox4x32_10(make_uint4(v >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
+  const uint32_t c = v & 3u;
+  return gumbel_from_bits(c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w);
+}
+
+// The epilogue of one column in the same two parts (the arithmetic of one
+// column of epilogue4_key and epilogue4_stat).
+__device__ __forceinline__ void epilogue1_key(const RowState& rs, uint32_t v, float base, float bias, float g,
+                                              float* logit_out, uint64_t& best, float& s) {
+  const float lg = __fadd_rn(base, bias);
+  *logit_out = lg;
+  if (rs.greedy) {
+    best = umax64(best, score_key(lg, v));
+    return;
+  }
+  s = __fmul_rn(lg, rs.invT);
+  best = umax64(best, score_key(__fadd_rn(s, g), v));
+}
+
+__device__ __forceinline__ void epilogue1_stat(float s, Stat& st) {
+  const float m = fmaxf(-INFINITY, s);   // NaN counts as -inf, as in epilogue4_stat
+  const float l = m != -INFINITY ? __expf(__fsub_rn(s, m)) : 0.0f;
+  st = stat_merge(st, Stat{m, l});
 }
 
 // Gumbel noise of the 4 columns v0..v0+3 at position k.
@@ -1133,10 +1217,12 @@ __device__ __forceinline__ void noise4(const RowState& rs, int k, uint32_t v0, f
   g[3] = gumbel_from_bits(x.w);
 }
 
-// The epilogue of 4 columns with the noise already drawn (same arithmetic as epilogue4).
-__device__ __forceinline__ void epilogue4_noise(const RowState& rs, uint32_t v0, const float base[4],
-                                                const float bias[4], const float g[4], float* logits_out,
-                                                uint64_t& best, Stat& st) {
+// The epilogue of 4 columns with the noise already drawn, in two parts (the
+// same arithmetic as epilogue4): the logits and the argmax key first, keeping
+// the scaled logits s, and the softmax statistics of s later.
+__device__ __forceinline__ void epilogue4_key(const RowState& rs, uint32_t v0, const float base[4],
+                                              const float bias[4], const float g[4], float* logits_out,
+                                              uint64_t& best, float s[4]) {
   float lg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(base[i], bias[i]);
@@ -1146,15 +1232,18 @@ __device__ __forceinline__ void epilogue4_noise(const RowState& rs, uint32_t v0,
     for (int i = 0; i < 4; ++i) best = umax64(best, score_key(lg[i], v0 + i));
     return;
   }
-  float s[4];
-  float m4 = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     s[i] = __fmul_rn(lg[i], rs.invT);
     const float z = __fadd_rn(s[i], g[i]);
     best = umax64(best, score_key(z, v0 + i));
-    m4 = fmaxf(m4, s[i]);
   }
+}
+
+__device__ __forceinline__ void epilogue4_stat(const float s[4], Stat& st) {
+  float m4 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m4 = fmaxf(m4, s[i]);
   float l4 = 0.0f;
   if (m4 != -INFINITY) {
 #pragma unroll
@@ -1189,11 +1278,13 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
   const int cg_l = kResRegGroups + (t >> 3);
 
   // epilogue lane mapping after the reduce-scatter
+  // (RB = 1: every lane, column js of its group; else 4 columns 4 eh .. of row er)
   const int er = RB == 4 ? (js >> 1) : RB == 2 ? (js >> 2) : 0;
   const int eh = js & 1;
-  const bool e_act = (RB == 4 ? true : RB == 2 ? ((js >> 1) & 1) == 0 : js < 2) && er < B;
-  const uint32_t v_r = (uint32_t)(col0 + 8 * cg_r + 4 * eh);   // epilogue columns, VGPR unit
-  const uint32_t v_l = (uint32_t)(col0 + 8 * cg_l + 4 * eh);   // epilogue columns, LDS unit
+  const bool e_act = (RB == 4 ? true : RB == 2 ? ((js >> 1) & 1) == 0 : true) && er < B;
+  const int ecol = RB == 1 ? js : 4 * eh;
+  const uint32_t v_r = (uint32_t)(col0 + 8 * cg_r + ecol);   // epilogue column(s), VGPR unit
+  const uint32_t v_l = (uint32_t)(col0 + 8 * cg_l + ecol);   // epilogue column(s), LDS unit
   const bool ep_r = e_act && reg_ok;
   const bool ep_l = e_act && lds_ok;
 
@@ -1232,15 +1323,31 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
   // ---- noise and base logits of a position for this lane's epilogue quads
   float gq[2][4];
   Base4<kBf16Base> bq[2];
-  auto prepare = [&](int k) {
+  auto make_noise = [&](int k) {
     if (e_act && !rs.greedy) {
-      noise4(rs, k, v_r, gq[0]);
-      if (lds_ok) noise4(rs, k, v_l, gq[1]);
+      if constexpr (RB == 1) {
+        gq[0][0] = noise1(rs, k, v_r);
+        if (lds_ok) gq[1][0] = noise1(rs, k, v_l);
+      } else {
+        noise4(rs, k, v_r, gq[0]);
+        if (lds_ok) noise4(rs, k, v_l, gq[1]);
+      }
     }
+  };
+  auto load_base = [&](int k) {
     const size_t row_off = ((size_t)er * K + k) * (size_t)V;
     const bool br = ep_r && !rs.pad, bl = ep_l && !rs.pad;
-    load_base4<kBf16Base>(bq[0], a.base, br ? row_off + v_r : 0);
-    load_base4<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
+    if constexpr (RB == 1) {
+      load_base1<kBf16Base>(bq[0], a.base, br ? row_off + v_r : 0);
+      load_base1<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
+    } else {
+      load_base4<kBf16Base>(bq[0], a.base, br ? row_off + v_r : 0);
+      load_base4<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
+    }
+  };
+  auto prepare = [&](int k) {
+    make_noise(k);
+    load_base(k);
   };
 
   // ---- the embedding rows E[d] of a position's tokens, into LDS
@@ -1415,44 +1522,44 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       reduce_scatter<RB>(acc, js, bias_l);
     }
 
-    // ---- epilogue of the lane's quads
+    // ---- epilogue of the lane's quads: logits and argmax keys now; the scaled
+    // logits are kept for the softmax statistics, which only the proposal reads
     uint64_t best = 0;
-    Stat st{-INFINITY, 0.0f};
+    float sr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     {
       float* out = a.logits + ((size_t)er * K + k) * (size_t)V;
-      if (ep_r) {
-        float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (!rs.pad) widen_base4<kBf16Base>(bq[0], base);
-        epilogue4_noise(rs, v_r, base, bias_r, gq[0], out + v_r, best, st);
-      }
-      if (ep_l) {
-        float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (!rs.pad) widen_base4<kBf16Base>(bq[1], base);
-        epilogue4_noise(rs, v_l, base, bias_l, gq[1], out + v_l, best, st);
+      if constexpr (RB == 1) {
+        if (ep_r)
+          epilogue1_key(rs, v_r, rs.pad ? 0.0f : widen_base1<kBf16Base>(bq[0]), bias_r[0], gq[0][0], out + v_r,
+                        best, sr[0]);
+        if (ep_l)
+          epilogue1_key(rs, v_l, rs.pad ? 0.0f : widen_base1<kBf16Base>(bq[1]), bias_l[0], gq[1][0], out + v_l,
+                        best, sl[0]);
+      } else {
+        if (ep_r) {
+          float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (!rs.pad) widen_base4<kBf16Base>(bq[0], base);
+          epilogue4_key(rs, v_r, base, bias_r, gq[0], out + v_r, best, sr);
+        }
+        if (ep_l) {
+          float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (!rs.pad) widen_base4<kBf16Base>(bq[1], base);
+          epilogue4_key(rs, v_l, base, bias_l, gq[1], out + v_l, best, sl);
+        }
       }
     }
 
-    // ---- this workgroup's partial per row: lanes, then waves in order
+    // ---- this workgroup's key per row (lanes, then waves), published at once
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
-      uint64_t kk = (er == rr) ? best : 0ull;
-      Stat ss = (er == rr) ? st : Stat{-INFINITY, 0.0f};
-      wave_merge_key_stat(kk, ss);
-      if (lane == 0) {
-        s_key[wv][rr] = kk;
-        s_stat[wv][rr] = ss;
-      }
+      const uint64_t kk = wave_max_u64((er == rr) ? best : 0ull);
+      if (lane == 0) s_key[wv][rr] = kk;
     }
     __syncthreads();
     if (t < B) {
       uint64_t kk = s_key[0][t];
-      Stat ss = s_stat[0][t];
 #pragma unroll
-      for (int w = 1; w < kResWaves; ++w) {
-        kk = umax64(kk, s_key[w][t]);
-        ss = stat_merge(ss, s_stat[w][t]);
-      }
-      a.stat_part[((size_t)k * B + t) * G + g] = ss;
+      for (int w = 1; w < kResWaves; ++w) kk = umax64(kk, s_key[w][t]);
       // a workgroup without columns has no candidate (kk == 0): it publishes the
       // tag alone, which every real candidate beats
       const uint64_t ord = kk >> 32;
@@ -1460,36 +1567,79 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       st_agent_u64(&a.ex->xrow[k & 1][g][t], res_tag(cpar, k) | (ord << 18) | idx);
     }
 
-    // ---- position k+1's noise and base do not depend on d_k: prepare them now
-    if (k + 1 < K) prepare(k + 1);
-
     // ---- exchange: every workgroup's word for every row. Thread t polls row
     // t % RB (RB is a power of two dividing the thread count) of workgroups
     // t / RB, t / RB + 512 / RB, ...; rows >= B are padding and not polled.
+    // The first read of the first word goes out now: the statistics and
+    // position k+1's noise and base are computed while it is in flight, and
+    // the second read follows it by that time.
+    const int xr = t % RB;
+    const bool polls = xr < B && t / RB < G && a.spin_limit != 0;
+    const uint64_t* pw_first = &a.ex->xrow[k & 1][t / RB][xr];
+    uint64_t w_first = 0;
+    if (polls) w_first = ld_agent_u64(pw_first);
+
+    // ---- softmax statistics per row: lanes, then waves through LDS (merged
+    // by the workgroup once the exchange is done)
+    {
+      Stat st{-INFINITY, 0.0f};
+      if (!rs.greedy) {
+        if constexpr (RB == 1) {
+          if (ep_r) epilogue1_stat(sr[0], st);
+          if (ep_l) epilogue1_stat(sl[0], st);
+        } else {
+          if (ep_r) epilogue4_stat(sr, st);
+          if (ep_l) epilogue4_stat(sl, st);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        Stat ss = (er == rr) ? st : Stat{-INFINITY, 0.0f};
+        wave_merge_stat(ss);
+        if (lane == 0) s_stat[wv][rr] = ss;
+      }
+    }
+    auto store_stat = [&]() {
+      if (t < B) {
+        Stat ss = s_stat[0][t];
+#pragma unroll
+        for (int w = 1; w < kResWaves; ++w) ss = stat_merge(ss, s_stat[w][t]);
+        a.stat_part[((size_t)k * B + t) * G + g] = ss;
+      }
+    };
+
+    // ---- position k+1's noise does not depend on d_k: drawn now (its base
+    // logits are loaded with the E rows, after the exchange, so that no load
+    // is issued between the two reads of the first word)
+    if (k + 1 < K) make_noise(k + 1);
+
     uint64_t xb = 0;
     bool failed = false;
-    const int xr = t % RB;
     const uint64_t tag = res_tag(cpar, k) >> kResTagShift;
-    if (xr < B) {
-      for (int gg = t / RB; gg < G; gg += kResThreads / RB) {
-        const uint64_t* pw = &a.ex->xrow[k & 1][gg][xr];
-        if (a.spin_limit == 0) { failed = true; break; }
-        // two reads of the word in flight, staggered by ~1500 cycles and
-        // checked in turn, so a word that lands is seen about half a round trip
-        // later on average (three in flight were no better: more traffic)
-        uint64_t w0 = ld_agent_u64(pw);
-        __builtin_amdgcn_s_sleep(24);
-        uint64_t w1 = ld_agent_u64(pw);
-        uint64_t w = 0;
-        for (unsigned reads = 2;; reads += 2) {
-          if ((w0 >> kResTagShift) == tag) { w = w0; break; }
-          if ((w1 >> kResTagShift) == tag) { w = w1; break; }
-          if (reads >= a.spin_limit) { failed = true; break; }
-          w0 = ld_agent_u64(pw);
-          w1 = ld_agent_u64(pw);
+    // two reads of a word in flight, staggered (the first word by the work
+    // above, the others by ~1500 cycles) and checked in turn, so a word that
+    // lands is seen about half a round trip later on average (three in
+    // flight were no better: more traffic)
+    auto poll_word = [&](const uint64_t* pw, uint64_t w0, uint64_t w1) -> bool {
+      for (unsigned reads = 2;; reads += 2) {
+        if ((w0 >> kResTagShift) == tag) { xb = umax64(xb, w0); return true; }
+        if ((w1 >> kResTagShift) == tag) { xb = umax64(xb, w1); return true; }
+        if (reads >= a.spin_limit) return false;
+        w0 = ld_agent_u64(pw);
+        w1 = ld_agent_u64(pw);
+      }
+    };
+    if (xr < B && t / RB < G) {
+      if (!polls) {
+        failed = true;   // a limit of 0: every wait expires at once, without reading
+      } else {
+        failed = !poll_word(pw_first, w_first, ld_agent_u64(pw_first));
+        for (int gg = t / RB + kResThreads / RB; !failed && gg < G; gg += kResThreads / RB) {
+          const uint64_t* pw = &a.ex->xrow[k & 1][gg][xr];
+          const uint64_t w0 = ld_agent_u64(pw);
+          __builtin_amdgcn_s_sleep(24);
+          failed = !poll_word(pw, w0, ld_agent_u64(pw));
         }
-        if (failed) break;
-        xb = umax64(xb, w);
       }
     }
     if (failed) {
@@ -1501,7 +1651,10 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     if (lane < RB) s_x[wv][lane] = xb;
     __syncthreads();
     if (s_fail) {
-      // an expired wait: this position and the later ones get no token
+      // an expired wait: this position and the later ones get no token (this
+      // position's statistics are still stored: other workgroups may have
+      // drawn its token)
+      store_stat();
       if (g == 0 && t < B)
         for (int kk = k; kk < K; ++kk) a.tokens[(size_t)t * K + kk] = -1;
       res_retire(a.ex, g, G, B, k + 1, 0, cpar, t, kResThreads);
@@ -1516,8 +1669,26 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       d[rr] = clamp_token((int)(kResIdxMask - (x & kResIdxMask)), V);
     }
     if (g == 0 && t < B) a.tokens[(size_t)t * K + k] = d[t % RB];
+    // the E rows of the tokens just drawn and position k+1's base logits:
+    // loaded now; the E rows are stored to LDS after the statistics are
+    // merged (which run while the loads are in flight), and the base logits
+    // are first needed by the next epilogue
+    const bool e_thr = t < RB * (kResRank / 2);
+    uint32_t ev = 0u;
     if (k + 1 < K) {
-      gather_e(d);
+      if (e_thr) {
+        const int rr = t / (kResRank / 2), jj = t % (kResRank / 2);
+        int tok = d[0];
+#pragma unroll
+        for (int q = 1; q < RB; ++q)
+          if (rr == q) tok = d[q];
+        if (rr < B && jj < r / 2) ev = reinterpret_cast<const uint32_t*>(a.E)[(size_t)tok * (r / 2) + jj];
+      }
+      load_base(k + 1);
+    }
+    store_stat();
+    if (k + 1 < K) {
+      if (e_thr) lds_e[t] = ev;   // row t / 128, pair t % 128
       __syncthreads();
     }
   }
