@@ -85,6 +85,23 @@ def test_ragged_shapes(case):
     full_check(w)
 
 
+@pytest.mark.parametrize("case", [
+    dict(temperature=0.0),
+    dict(temperature=2.5, base_dtype="bf16"),
+    dict(n_real=0),
+    dict(n_real=0, pad_base="nan", base_dtype="bf16"),
+    dict(V=2056, r=96, temperature=0.4),
+], ids=["greedy", "t2.5_bf16", "padding", "padding_nan_bf16", "v2056_r96"])
+def test_single_row_cases(case):
+    """One row (the small-batch kernel's one-column-per-lane form): greedy and
+    hot rows, a padding row with zero or NaN base logits, a vocabulary and a
+    rank that leave most workgroups partly or wholly without columns."""
+    from ancestral_draft_token_amd import dspark_launch_plan
+    w = inputs.tiny(fixed_seed=None, fixed_offset=None, data_seed=5, **case)
+    assert 4 in dspark_launch_plan(w.B, w.K, w.V, w.r), "a resident plan expected"
+    full_check(w)
+
+
 def test_prev_token_out_of_range_is_clamped():
     w = inputs.tiny(B=3, K=3, fixed_seed=None, fixed_offset=None)
     w.prev_token[:] = [-7, w.V, 2**30]
