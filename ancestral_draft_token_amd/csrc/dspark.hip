@@ -945,7 +945,7 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Resident path (B <= 4): one persistent launch runs all K positions, and each
+// Resident path (B <= 2): one persistent launch runs all K positions, and each
 // workgroup keeps its slice of W on chip for the whole block, so W is read
 // from HBM once per block instead of once per position.
 //
@@ -970,9 +970,11 @@ constexpr int kResRegGroups = kResWaves * 8;               // 64 groups in VGPRs
 constexpr int kResLdsUnits = (kResGroups - kResRegGroups) * 8;  // 272 units in LDS
 constexpr int kResRank = 256;                              // 8 rank slices of 32 rows
 constexpr int kResPairs = 16;                              // bf16 pairs per unit column
-constexpr int kResRowsMax = 4;
+// rows of this kernel: from three rows the MFMA form below is faster (B=3:
+// 100 us a block against 144, B=4: 102 against 146; B=2: 89.7 against ~99)
+constexpr int kResRowsMax = 2;
 constexpr size_t kResLdsW = (size_t)kResPairs * kResLdsUnits * 32;   // 139,264 bytes
-constexpr size_t kResLdsE = (size_t)kResRowsMax * kResRank * 2;      // 2,048 bytes
+constexpr size_t kResLdsE = (size_t)kResRowsMax * kResRank * 2;      // 1,024 bytes
 constexpr size_t kResLdsBytes = kResLdsW + kResLdsE;
 // packed W (dspark_pack_w): 16-byte units per workgroup and kernel, and those
 // of the register part (the rest is the kernel's LDS image)
@@ -1278,10 +1280,11 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
   const int cg_l = kResRegGroups + (t >> 3);
 
   // epilogue lane mapping after the reduce-scatter
-  // (RB = 1: every lane, column js of its group; else 4 columns 4 eh .. of row er)
-  const int er = RB == 4 ? (js >> 1) : RB == 2 ? (js >> 2) : 0;
+  // (RB = 1: every lane, column js of its group; RB = 2: 4 columns 4 eh .. of row er)
+  static_assert(RB == 1 || RB == 2, "rows of the small-batch resident kernel");
+  const int er = RB == 2 ? (js >> 2) : 0;
   const int eh = js & 1;
-  const bool e_act = (RB == 4 ? true : RB == 2 ? ((js >> 1) & 1) == 0 : true) && er < B;
+  const bool e_act = (RB == 2 ? ((js >> 1) & 1) == 0 : true) && er < B;
   const int ecol = RB == 1 ? js : 4 * eh;
   const uint32_t v_r = (uint32_t)(col0 + 8 * cg_r + ecol);   // epilogue column(s), VGPR unit
   const uint32_t v_l = (uint32_t)(col0 + 8 * cg_l + ecol);   // epilogue column(s), LDS unit
@@ -1696,7 +1699,7 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
 }
 
 // ---------------------------------------------------------------------------
-// Resident path, MFMA form (4 < B <= 128). Same block structure as the VALU
+// Resident path, MFMA form (2 < B <= 128). Same block structure as the VALU
 // resident kernel: one persistent launch, one 512-thread workgroup per CU
 // owning up to 784 columns, W on chip for the whole block. Here the slice is
 // held as bf16 A-operand fragments of v_mfma_f32_16x16x32_bf16 (A = W^T: 16
@@ -2986,10 +2989,8 @@ int init_device() {
   bool ok = cus > 0 && cus <= kResMaxCUs;
   ok = ok && prepare_resident_kernel<1, false, false>() && prepare_resident_kernel<1, true, false>();
   ok = ok && prepare_resident_kernel<2, false, false>() && prepare_resident_kernel<2, true, false>();
-  ok = ok && prepare_resident_kernel<4, false, false>() && prepare_resident_kernel<4, true, false>();
   ok = ok && prepare_resident_kernel<1, false, true>() && prepare_resident_kernel<1, true, true>();
   ok = ok && prepare_resident_kernel<2, false, true>() && prepare_resident_kernel<2, true, true>();
-  ok = ok && prepare_resident_kernel<4, false, true>() && prepare_resident_kernel<4, true, true>();
   bool mok = cus > 0 && cus <= kResMaxCUs;
   mok = mok && prepare_mfma_kernel<false, false, false>() && prepare_mfma_kernel<true, false, false>();
   mok = mok && prepare_mfma_kernel<false, true, false>() && prepare_mfma_kernel<true, true, false>();
@@ -3234,8 +3235,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
 #define DSPARK_LAUNCH_RES_B(PK)                                                       \
   do {                                                                                \
     if (B == 1) { if (bf16) DSPARK_LAUNCH_RES(1, true, PK); else DSPARK_LAUNCH_RES(1, false, PK); } \
-    else if (B == 2) { if (bf16) DSPARK_LAUNCH_RES(2, true, PK); else DSPARK_LAUNCH_RES(2, false, PK); } \
-    else { if (bf16) DSPARK_LAUNCH_RES(4, true, PK); else DSPARK_LAUNCH_RES(4, false, PK); } \
+    else { if (bf16) DSPARK_LAUNCH_RES(2, true, PK); else DSPARK_LAUNCH_RES(2, false, PK); } \
   } while (0)
       if (packed) DSPARK_LAUNCH_RES_B(true);
       else DSPARK_LAUNCH_RES_B(false);

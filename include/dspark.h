@@ -236,7 +236,7 @@ typedef enum {
  *   - resident (r <= 256, V <= 2^18, V <= 784 x the device's CU count, at
  *     most 512 CUs, and B <= 128): RESIDENT_BLOCK, PROPOSAL. One persistent
  *     launch runs all K positions; each workgroup keeps its slice of W on chip
- *     for the block (B <= 4: a VALU GEMV with 512 threads; 4 < B <= 128: bf16
+ *     for the block (B <= 2: a VALU GEMV with 512 threads; 2 < B <= 128: bf16
  *     MFMA tiles with 256 threads). It needs every workgroup resident at once
  *     (one per compute unit); its device-side waits are bounded, and if one
  *     expires the affected tokens are -1 instead of hanging (see "Device

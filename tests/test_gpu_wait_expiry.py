@@ -37,7 +37,7 @@ def status_now():
 
 
 CASES = {
-    # the VALU resident kernel (B <= 4) and the MFMA resident kernel (4 < B <= 128)
+    # the VALU resident kernel (B <= 2) and the MFMA resident kernel (2 < B <= 128)
     "b1": (inputs.single_request, [0]),
     "b8": (inputs.small_batch, [0, 3, 7]),
     "b44": (inputs.mixed_batch, [0, 1, 43]),
