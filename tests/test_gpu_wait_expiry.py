@@ -41,6 +41,8 @@ CASES = {
     "b1": (inputs.single_request, [0]),
     "b8": (inputs.small_batch, [0, 3, 7]),
     "b44": (inputs.mixed_batch, [0, 1, 43]),
+    # six N-tiles: with packed W the owners' reductions are pipelined
+    "b88": (inputs.WORKLOADS["b88"], [0, 40, 87, 88, 95]),
 }
 
 
