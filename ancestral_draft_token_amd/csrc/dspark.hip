@@ -954,13 +954,15 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
 // bf16 pairs (rows 2p, 2p+1 packed in one dword); groups 0..63 live in VGPRs
 // (thread = one unit), groups 64..97 in LDS. The bias GEMV is v_dot2 of those
 // pairs with the embedding pairs, then a reduce-scatter over the 8 rank
-// slices leaves each lane 4 consecutive columns of one row, so one Philox
-// block serves its epilogue. Positions are separated by an exchange: each
-// workgroup publishes its per-row argmax partial as one 64-bit word tagged
-// with the position, and every workgroup polls all words (a bounded wait)
-// and reduces them in the same order, so all agree on d_k. The Gumbel noise
-// and base logits of position k+1 do not depend on d_k and are prepared while
-// the exchange is in flight.
+// slices leaves each lane one column (one row) or 4 consecutive columns of one
+// row (two rows; one Philox block serves them). Positions are separated by an
+// exchange: each workgroup publishes its per-row argmax key as one 64-bit word
+// tagged with the position as soon as it is merged, and every workgroup polls
+// all words (a bounded wait) and reduces them in the same order, so all agree
+// on d_k. The softmax statistics (read only by the proposal) and the Gumbel
+// noise of position k+1 do not depend on d_k and are computed while the
+// first reads are in flight; the base logits of k+1 are loaded with the E
+// rows of d_k.
 // ---------------------------------------------------------------------------
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / 64;
