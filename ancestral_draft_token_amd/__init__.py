@@ -39,7 +39,7 @@ EXPORTED = ("dspark_init", "dspark_workspace_bytes", "dspark_draft_block",
             "dspark_block_status", "dspark_set_wait_limit",
             "dspark_draft_block_noalloc", "dspark_noalloc_scratch_bytes",
             "dspark_window_block_attention_layout", "dspark_packed_w_bytes", "dspark_pack_w",
-            "dspark_draft_block_packed")
+            "dspark_draft_block_packed", "dspark_draft_block_slots")
 
 LAUNCH_KINDS = {0: "markov_bias_gumbel_argmax", 1: "pick_and_gather", 2: "proposal_softmax",
                 4: "markov_bias_gumbel_argmax"}
@@ -110,6 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_pack_w.restype = I
     lib.dspark_draft_block_packed.argtypes = [P, I, P, P, P, Z, P, P, P, P, P, I, I, I, I] + out_args + [P, I]
     lib.dspark_draft_block_packed.restype = I
+    lib.dspark_draft_block_slots.argtypes = [P, I, P, P, P, Z, P, P, P, P, P, P, I, I, I, I, I] + out_args
+    lib.dspark_draft_block_slots.restype = I
     _lib = lib
     return lib
 
@@ -191,6 +193,26 @@ def dspark_draft_block(base_logits, base_dtype: int, E, W, prev_token, seed, off
         where = "dspark_draft_block_chunked"
     if check and rc != DSPARK_OK:
         raise DSparkError(rc, where)
+    return rc
+
+
+def dspark_draft_block_slots(base_logits, base_dtype: int, E, W, prev_token, seed, offset, temperature,
+                             n_real, slot_index, n_slots: int, B: int, K: int, V: int, r: int, tokens,
+                             logits_f32, draft_probs, workspace, workspace_bytes: int, stream=None,
+                             W_packed=None, packed_bytes: int = 0, check: bool = True) -> int:
+    """Enqueue one draft block whose proposals go to ``draft_probs`` rows
+    ``slot_index[b]`` (``[n_slots, K, V]``); arguments as in ``include/dspark.h``
+    (``W_packed`` optional). Returns the status; with ``check`` a nonzero
+    status raises."""
+    lib = load_library()
+    rc = lib.dspark_draft_block_slots(
+        _ptr(base_logits), int(base_dtype), _ptr(E), _ptr(W), _ptr(W_packed),
+        int(packed_bytes) if W_packed is not None else 0, _ptr(prev_token), _ptr(seed), _ptr(offset),
+        _ptr(temperature), _ptr(n_real), _ptr(slot_index), int(n_slots), int(B), int(K), int(V), int(r),
+        _ptr(tokens), _ptr(logits_f32), _ptr(draft_probs), _ptr(workspace), int(workspace_bytes),
+        _stream_ptr(stream))
+    if check and rc != DSPARK_OK:
+        raise DSparkError(rc, "dspark_draft_block_slots")
     return rc
 
 

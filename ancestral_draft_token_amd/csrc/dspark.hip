@@ -824,6 +824,8 @@ struct PropArgs {
   const Stat* last_stat;
   const Stat* part_stat;      // [K,B,n_part] per-workgroup statistics (n_part > 0)
   float* q;
+  const int32_t* slot;        // [B] row b's proposals go to q row slot[b] (NULL: row b)
+  int n_slots;                // rows of q (slots outside [0, n_slots) write none)
   int B, K, V, n_chunks;
   int blocks_per_row;
   int last_from_partials;
@@ -843,6 +845,11 @@ __device__ __forceinline__ void proposal_block(const PropArgs& a, int b, int k, 
   const size_t row = (size_t)bk * a.V;
   const int c0 = cb * prop_cols<kVec>() + 4 * t;
   auto in_row = [&](int v) { return !kChecked || v < a.V; };
+  // where the row's proposals go: its own row, or its slot (a slot out of
+  // range writes none; the token and statistics below are still kept)
+  const int sb = a.slot ? a.slot[b] : b;
+  const bool q_ok = sb >= 0 && sb < a.n_slots;
+  float* const qrow = a.q + ((size_t)(q_ok ? sb : 0) * a.K + k) * a.V;
 
   // the first statistics partial of this thread is loaded before the logits,
   // so the merge waits for it alone (loads complete in order)
@@ -898,7 +905,7 @@ __device__ __forceinline__ void proposal_block(const PropArgs& a, int b, int k, 
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       const int v = c0 + j * kThreads * 4;
-      if (in_row(v)) *reinterpret_cast<fx4_t*>(a.q + row + v) = fx4_t{nan, nan, nan, nan};
+      if (q_ok && in_row(v)) *reinterpret_cast<fx4_t*>(qrow + v) = fx4_t{nan, nan, nan, nan};
     }
     return;
   }
@@ -906,10 +913,10 @@ __device__ __forceinline__ void proposal_block(const PropArgs& a, int b, int k, 
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       const int v = c0 + j * kThreads * 4;
-      if (in_row(v)) {
+      if (q_ok && in_row(v)) {
         const fx4_t out{v == tok ? 1.0f : 0.0f, v + 1 == tok ? 1.0f : 0.0f, v + 2 == tok ? 1.0f : 0.0f,
                         v + 3 == tok ? 1.0f : 0.0f};
-        *reinterpret_cast<fx4_t*>(a.q + row + v) = out;
+        *reinterpret_cast<fx4_t*>(qrow + v) = out;
       }
     }
     return;
@@ -919,13 +926,13 @@ __device__ __forceinline__ void proposal_block(const PropArgs& a, int b, int k, 
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
     const int v = c0 + j * kThreads * 4;
-    if (in_row(v)) {
+    if (q_ok && in_row(v)) {
       fx4_t out;
       out.x = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].x, invT), st.m)), invS);
       out.y = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].y, invT), st.m)), invS);
       out.z = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].z, invT), st.m)), invS);
       out.w = __fmul_rn(__expf(__fsub_rn(__fmul_rn(lg[j].w, invT), st.m)), invS);
-      *reinterpret_cast<fx4_t*>(a.q + row + v) = out;
+      *reinterpret_cast<fx4_t*>(qrow + v) = out;
     }
   }
 }
@@ -3145,7 +3152,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
                      int chunk_cols, int32_t* tokens, float* logits, float* q, void* workspace,
                      size_t workspace_bytes, void* stream_ptr, void* const* events = nullptr,
                      int n_events = 0, bool use_scratch = false, const void* W_packed = nullptr,
-                     size_t packed_bytes = 0) {
+                     size_t packed_bytes = 0, const int32_t* slot_index = nullptr, int n_slots = 0) {
   int rc = check_sizes(B, K, V, r);
   if (rc != DSPARK_OK) return rc;
   const bool packed = W_packed != nullptr;
@@ -3166,6 +3173,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   }
   // the packed copy must be this device's, for these sizes (its size says so)
   if (packed && packed_bytes != packed_w_bytes(V, r)) return DSPARK_ERR_ARG;
+  if (slot_index && n_slots <= 0) return DSPARK_ERR_ARG;
 
   Plan plan;
   rc = make_plan(B, K, V, r, explicit_chunk ? chunk_cols : 0, &plan);
@@ -3274,6 +3282,7 @@ int draft_block_impl(const void* base, int base_dtype, const uint16_t* E, const 
   pr.logits = logits; pr.temperature = temperature; pr.tokens = tokens; pr.row_stat = ws.row_stat;
   pr.last_key = ws.part_key[(K - 1) & 1]; pr.last_stat = ws.part_stat[(K - 1) & 1];
   pr.q = q; pr.B = B; pr.K = K; pr.V = V; pr.n_chunks = n_chunks;
+  pr.slot = slot_index; pr.n_slots = slot_index ? n_slots : B;
   pr.last_from_partials = (in_kernel_pick && !resident) ? 1 : 0;
   pr.part_stat = resident ? ws.stat_part : nullptr;
   pr.n_part = resident ? G : 0;
@@ -3540,6 +3549,19 @@ int dspark_draft_block_packed(const void* base_logits, int base_dtype, const uin
                                   n_real, B, K, V, r, 0, tokens, logits_f32, draft_probs, workspace,
                                   workspace_bytes, stream, events, events ? n_events : 0, false, W_packed,
                                   packed_bytes);
+}
+
+int dspark_draft_block_slots(const void* base_logits, int base_dtype, const uint16_t* E, const uint16_t* W,
+                             const void* W_packed, size_t packed_bytes, const int32_t* prev_token,
+                             const int64_t* seed, const int64_t* offset, const float* temperature,
+                             const int32_t* n_real, const int32_t* slot_index, int n_slots, int B, int K,
+                             int V, int r, int32_t* tokens, float* logits_f32, float* draft_probs,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!slot_index) return DSPARK_ERR_ARG;
+  return dspark::draft_block_impl(base_logits, base_dtype, E, W, prev_token, seed, offset, temperature,
+                                  n_real, B, K, V, r, 0, tokens, logits_f32, draft_probs, workspace,
+                                  workspace_bytes, stream, nullptr, 0, false, W_packed,
+                                  W_packed ? packed_bytes : 0, slot_index, n_slots);
 }
 
 int dspark_launch_plan(int B, int K, int V, int r, int* kinds, int max_kinds) {

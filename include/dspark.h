@@ -220,6 +220,33 @@ int dspark_draft_block_packed(
     void* workspace, size_t workspace_bytes, void* stream,
     void* const* events, int n_events);
 
+/* dspark_draft_block with the proposals written by slot: the proposal pass
+ * stores row b's q_k into row slot_index[b] of draft_probs [n_slots, K, V]
+ * instead of row b ("brb-nv/TensorRT-LLM pull 27", section "2. One fused
+ * kernel per draft position": the proposals go into draft_probs indexed by
+ * the request's slot). tokens [B, K] and logits_f32 [B, K, V] stay indexed by
+ * row. W_packed may be NULL (W alone is used); if not, it and packed_bytes are
+ * as for dspark_draft_block_packed.
+ *   slot_index   [B]     int32, device; a slot outside [0, n_slots) stores no
+ *                        proposal for that row (its tokens and logits are
+ *                        still written); two rows with one slot race, so slots
+ *                        should be distinct
+ *   n_slots               rows of draft_probs (host int, > 0)
+ *   draft_probs  [n_slots, K, V] float32, device, 16-byte aligned; rows no
+ *                        row is sent to are left as they were
+ * Same launches, tokens and logits as dspark_draft_block, and the same q bit
+ * for bit in each written slot. DSPARK_ERR_ARG for a NULL slot_index or
+ * n_slots <= 0, otherwise the errors of dspark_draft_block(_packed). */
+int dspark_draft_block_slots(
+    const void* base_logits, int base_dtype,
+    const uint16_t* E, const uint16_t* W, const void* W_packed, size_t packed_bytes,
+    const int32_t* prev_token, const int64_t* seed, const int64_t* offset,
+    const float* temperature, const int32_t* n_real,
+    const int32_t* slot_index, int n_slots,
+    int B, int K, int V, int r,
+    int32_t* tokens, float* logits_f32, float* draft_probs,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kinds of kernel launch a block is made of. */
 typedef enum {
     DSPARK_LAUNCH_FUSED_POSITION = 0,  /* markov_bias_gumbel_argmax for one position */

@@ -80,6 +80,17 @@ int main(void) {
           DSPARK_ERR_UNSUPPORTED);
     CHECK(dspark_draft_block_packed(P, 0, P, P, P, 1, P, P, P, P, NULL, 2, 7, 4096, 32, P, P, P, NULL, ws, NULL, NULL, 0) ==
           DSPARK_ERR_WORKSPACE);
+    /* the slot-indexed entry */
+    CHECK(dspark_draft_block_slots(P, 0, P, P, NULL, 0, P, P, P, P, NULL, NULL, 4, 2, 7, 4096, 32, P, P, P, P, ws,
+                                   NULL) == DSPARK_ERR_ARG);
+    CHECK(dspark_draft_block_slots(P, 0, P, P, NULL, 0, P, P, P, P, NULL, P, 0, 2, 7, 4096, 32, P, P, P, P, ws,
+                                   NULL) == DSPARK_ERR_ARG);
+    CHECK(dspark_draft_block_slots(P, 0, P, P, NULL, 0, P, P, P, P, NULL, P, 4, 2, 7, 4100, 32, P, P, P, P, ws,
+                                   NULL) == DSPARK_ERR_UNSUPPORTED);
+    CHECK(dspark_draft_block_slots(P, 0, P, P, NULL, 0, P, P, P, P, NULL, P, 4, 2, 7, 4096, 32, P, P, M, P, ws,
+                                   NULL) == DSPARK_ERR_ARG);
+    CHECK(dspark_draft_block_slots(P, 0, P, P, NULL, 0, P, P, P, P, NULL, P, 4, 2, 7, 4096, 32, P, P, P, NULL, ws,
+                                   NULL) == DSPARK_ERR_WORKSPACE);
     CHECK(dspark_launch_plan(2, 7, 4100, 32, NULL, 0) == DSPARK_ERR_UNSUPPORTED);
     CHECK(dspark_launch_plan(0, 7, 4096, 32, NULL, 0) == 0);
 

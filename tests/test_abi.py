@@ -148,6 +148,31 @@ def test_packed_w_host_checks(lib):
         call(W_packed=FAKE, packed_bytes=1, chunk_cols=128)
 
 
+def call_slots(**kw):
+    args = dict(base_logits=FAKE, base_dtype=adt.DSPARK_F32, E=FAKE, W=FAKE, prev_token=FAKE,
+                seed=FAKE, offset=FAKE, temperature=FAKE, n_real=None, slot_index=FAKE, n_slots=4,
+                B=2, K=7, V=4096, r=32, tokens=FAKE, logits_f32=FAKE, draft_probs=FAKE, workspace=FAKE,
+                workspace_bytes=adt.dspark_workspace_bytes(2, 7, 4096, 32), stream=0, check=False)
+    args.update(kw)
+    return adt.dspark_draft_block_slots(**args)
+
+
+def test_slot_entry_host_checks(lib):
+    """The slot-indexed entry's checks that need no device (every call here
+    returns before a HIP call)."""
+    assert call_slots(slot_index=None) == adt.DSPARK_ERR_ARG
+    assert call_slots(n_slots=0) == adt.DSPARK_ERR_ARG
+    assert call_slots(n_slots=-3) == adt.DSPARK_ERR_ARG
+    assert call_slots(V=4100) == adt.DSPARK_ERR_UNSUPPORTED
+    assert call_slots(draft_probs=FAKE + 4) == adt.DSPARK_ERR_ARG
+    assert call_slots(workspace=None) == adt.DSPARK_ERR_WORKSPACE
+    assert call_slots(W_packed=FAKE + 8, packed_bytes=1) == adt.DSPARK_ERR_ARG
+    assert call_slots(W_packed=FAKE, packed_bytes=1, V=4100) == adt.DSPARK_ERR_UNSUPPORTED
+    assert call_slots(B=0, tokens=None) == adt.DSPARK_OK
+    with pytest.raises(adt.DSparkError):
+        call_slots(n_slots=0, check=True)
+
+
 def test_block_status_checks_its_pointer(lib):
     assert lib.dspark_block_status(None, None) == adt.DSPARK_ERR_ARG
 
