@@ -1534,8 +1534,9 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       reduce_scatter<RB>(acc, js, bias_l);
     }
 
-    // ---- epilogue of the lane's quads: logits and argmax keys now; the scaled
-    // logits are kept for the softmax statistics, which only the proposal reads
+    // ---- epilogue of the lane's column(s): logits and argmax keys now; the
+    // scaled logits are kept for the softmax statistics, which only the
+    // proposal reads
     uint64_t best = 0;
     float sr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     {
@@ -1583,8 +1584,8 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     // t % RB (RB is a power of two dividing the thread count) of workgroups
     // t / RB, t / RB + 512 / RB, ...; rows >= B are padding and not polled.
     // The first read of the first word goes out now: the statistics and
-    // position k+1's noise and base are computed while it is in flight, and
-    // the second read follows it by that time.
+    // position k+1's noise are computed while it is in flight, and the second
+    // read follows it by that time.
     const int xr = t % RB;
     const bool polls = xr < B && t / RB < G && a.spin_limit != 0;
     const uint64_t* pw_first = &a.ex->xrow[k & 1][t / RB][xr];
@@ -1628,10 +1629,11 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     uint64_t xb = 0;
     bool failed = false;
     const uint64_t tag = res_tag(cpar, k) >> kResTagShift;
-    // two reads of a word in flight, staggered (the first word by the work
-    // above, the others by ~1500 cycles) and checked in turn, so a word that
-    // lands is seen about half a round trip later on average (three in
-    // flight were no better: more traffic)
+    // two reads of a word in flight, checked in turn: the first two are
+    // staggered (the first word's by the work above, the others' by ~1500
+    // cycles), so a word that lands between them is seen half a round trip
+    // sooner; later rounds read it twice again (three in flight were no
+    // better: more traffic)
     auto poll_word = [&](const uint64_t* pw, uint64_t w0, uint64_t w1) -> bool {
       for (unsigned reads = 2;; reads += 2) {
         if ((w0 >> kResTagShift) == tag) { xb = umax64(xb, w0); return true; }
