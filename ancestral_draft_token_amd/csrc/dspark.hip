@@ -370,19 +370,34 @@ __device__ __forceinline__ void load_base4(Base4<kBf16Base>& bv, const void* bas
   }
 }
 
-// The base logit of one column (its bf16 in h.x, or its float in f.x).
-template <bool kBf16Base>
-__device__ __forceinline__ void load_base1(Base4<kBf16Base>& bv, const void* base, size_t off) {
+// The base logits of N = 1 or 2 consecutive columns (N = 2: off even): their
+// bf16 in h.x, or their floats in f.x, f.y.
+template <bool kBf16Base, int N>
+__device__ __forceinline__ void load_base_n(Base4<kBf16Base>& bv, const void* base, size_t off) {
+  static_assert(N == 1 || N == 2, "columns");
   if (kBf16Base) {
-    bv.h.x = (uint32_t)__builtin_nontemporal_load(static_cast<const uint16_t*>(base) + off);
+    if constexpr (N == 1) bv.h.x = (uint32_t)__builtin_nontemporal_load(static_cast<const uint16_t*>(base) + off);
+    else bv.h.x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + off));
   } else {
-    bv.f.x = __builtin_nontemporal_load(static_cast<const float*>(base) + off);
+    if constexpr (N == 1) {
+      bv.f.x = __builtin_nontemporal_load(static_cast<const float*>(base) + off);
+    } else {
+      const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(static_cast<const float*>(base) + off));
+      bv.f.x = __uint_as_float(x.x);
+      bv.f.y = __uint_as_float(x.y);
+    }
   }
 }
 
-template <bool kBf16Base>
-__device__ __forceinline__ float widen_base1(const Base4<kBf16Base>& bv) {
-  return kBf16Base ? __uint_as_float(bv.h.x << 16) : bv.f.x;
+template <bool kBf16Base, int N>
+__device__ __forceinline__ void widen_base_n(const Base4<kBf16Base>& bv, float out[N]) {
+  if (kBf16Base) {
+    out[0] = bf16_lo(bv.h.x);
+    if constexpr (N == 2) out[1] = bf16_hi(bv.h.x);
+  } else {
+    out[0] = bv.f.x;
+    if constexpr (N == 2) out[1] = bv.f.y;
+  }
 }
 
 template <bool kBf16Base>
@@ -961,12 +976,12 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
 // bf16 pairs (rows 2p, 2p+1 packed in one dword); groups 0..63 live in VGPRs
 // (thread = one unit), groups 64..97 in LDS. The bias GEMV is v_dot2 of those
 // pairs with the embedding pairs, then a reduce-scatter over the 8 rank
-// slices leaves each lane one column (one row) or 4 consecutive columns of one
-// row (two rows; one Philox block serves them). Positions are separated by an
-// exchange: each workgroup publishes its per-row argmax key as one 64-bit word
-// tagged with the position as soon as it is merged, and every workgroup polls
-// all words (a bounded wait) and reduces them in the same order, so all agree
-// on d_k. The softmax statistics (read only by the proposal) and the Gumbel
+// slices leaves every lane of the epilogue one column (one row) or 2
+// consecutive columns of one row (two rows; two lanes share a Philox block).
+// Positions are separated by an exchange: each workgroup publishes its
+// per-row argmax key as one 64-bit word tagged with the position as soon as
+// it is merged, and every workgroup polls all words (a bounded wait) and
+// reduces them in the same order, so all agree on d_k. The softmax statistics (read only by the proposal) and the Gumbel
 // noise of position k+1 do not depend on d_k and are computed while the
 // first reads are in flight; the base logits of k+1 are loaded with the E
 // rows of d_k.
@@ -1126,46 +1141,17 @@ __device__ __forceinline__ float dpp_xor1(float x) {
 }
 
 // Reduce-scatter of acc[RB][8] over the 8 rank-slice lanes of a column group
-// (lanes differing in bits 0..2): lane js ends with the sums of 4 columns
-// (4 * (js & 1) ..) of row er (RB = 4: js >> 1; RB = 2: js >> 2), or with
-// the sum of column js alone (RB = 1).
-// The three exchange steps pair lanes of opposite bit 2 (by the mirror),
-// then of opposite bit 1, then of opposite bit 0; the mirror pairs 0-7, 1-6,
-// 2-5, 3-4, and the three steps still add every slice exactly once.
+// (lanes differing in bits 0..2): every step halves what a lane keeps, so
+// lane js (bits b2 b1 b0) ends with RB sums: one row, column js (RB = 1); two
+// rows, row b2, columns 2 (js & 3) and 2 (js & 3) + 1 (RB = 2). The three
+// exchange steps pair lanes of opposite bit 2 (by the half-row mirror, which
+// pairs 0-7, 1-6, 2-5, 3-4), then of opposite bit 1, then of opposite bit 0,
+// and still add every slice exactly once.
 template <int RB>
-__device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js, float bias[4]) {
+__device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js, float bias[RB]) {
+  static_assert(RB == 1 || RB == 2, "rows of the small-batch resident kernel");
   const int b0 = js & 1, b1 = (js >> 1) & 1, b2 = (js >> 2) & 1;
-  float h2[8];
-  if (RB == 4) {
-    float h[2][8];
-#pragma unroll
-    for (int r0 = 0; r0 < 2; ++r0)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float keep = b2 ? acc[(2 + r0) % RB][c] : acc[r0 % RB][c];
-        const float send = b2 ? acc[r0 % RB][c] : acc[(2 + r0) % RB][c];
-        h[r0][c] = __fadd_rn(keep, dpp_mirror8(send));
-      }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float keep = b1 ? h[1][c] : h[0][c];
-      const float send = b1 ? h[0][c] : h[1][c];
-      h2[c] = __fadd_rn(keep, dpp_xor2(send));
-    }
-  } else if (RB == 2) {
-    float h[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float keep = b2 ? acc[1 % RB][c] : acc[0][c];
-      const float send = b2 ? acc[0][c] : acc[1 % RB][c];
-      h[c] = __fadd_rn(keep, dpp_mirror8(send));
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) h2[c] = __fadd_rn(h[c], dpp_xor2(h[c]));
-  } else {
-    // one row: every step halves the columns a lane keeps, so lane js ends
-    // with column js (bit 2 of js chose the half at the mirror, bit 1 the
-    // quarter, bit 0 the column); bias[0] only
+  if constexpr (RB == 1) {
     float h[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1181,86 +1167,78 @@ __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js
       q[i] = __fadd_rn(keep, dpp_xor2(send));
     }
     bias[0] = __fadd_rn(b0 ? q[1] : q[0], dpp_xor1(b0 ? q[0] : q[1]));
-    return;
-  }
+  } else {
+    // the mirror keeps a row (b2), xor 2 half its columns (b1), xor 1 a pair (b0)
+    float h[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float keep = b0 ? h2[4 + i] : h2[i];
-    const float send = b0 ? h2[i] : h2[4 + i];
-    bias[i] = __fadd_rn(keep, dpp_xor1(send));
+    for (int c = 0; c < 8; ++c) {
+      const float keep = b2 ? acc[1 % RB][c] : acc[0][c];
+      const float send = b2 ? acc[0][c] : acc[1 % RB][c];
+      h[c] = __fadd_rn(keep, dpp_mirror8(send));
+    }
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b1 ? h[4 + i] : h[i];
+      const float send = b1 ? h[i] : h[4 + i];
+      q[i] = __fadd_rn(keep, dpp_xor2(send));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b0 ? q[2 + i] : q[i];
+      const float send = b0 ? q[i] : q[2 + i];
+      bias[i % RB] = __fadd_rn(keep, dpp_xor1(send));
+    }
   }
 }
 
-// Gumbel noise of column v at position k: component v % 4 of the block of
-// columns v - v % 4 .., the value noise4 gives that column.
-__device__ __forceinline__ float noise1(const RowState& rs, int k, uint32_t v) {
+// Gumbel noise of N = 1 or 2 consecutive columns v .. v + N - 1 at position k
+// (two columns start at an even v): components v % 4 .. of the Philox block
+// of columns v - v % 4 .., the values every column gets from its block.
+template <int N>
+__device__ __forceinline__ void noise_n(const RowState& rs, int k, uint32_t v, float g[N]) {
   const uint4 x = philox4x32_10(make_uint4(v >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
   const uint32_t c = v & 3u;
-  return gumbel_from_bits(c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w);
+  g[0] = gumbel_from_bits(c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w);
+  if constexpr (N == 2) g[1] = gumbel_from_bits(c == 0 ? x.y : x.w);
 }
 
-// The epilogue of one column in the same two parts (the arithmetic of one
-// column of epilogue4_key and epilogue4_stat).
-__device__ __forceinline__ void epilogue1_key(const RowState& rs, uint32_t v, float base, float bias, float g,
-                                              float* logit_out, uint64_t& best, float& s) {
-  const float lg = __fadd_rn(base, bias);
-  *logit_out = lg;
-  if (rs.greedy) {
-    best = umax64(best, score_key(lg, v));
-    return;
-  }
-  s = __fmul_rn(lg, rs.invT);
-  best = umax64(best, score_key(__fadd_rn(s, g), v));
-}
-
-__device__ __forceinline__ void epilogue1_stat(float s, Stat& st) {
-  const float m = fmaxf(-INFINITY, s);   // NaN counts as -inf, as in epilogue4_stat
-  const float l = m != -INFINITY ? __expf(__fsub_rn(s, m)) : 0.0f;
-  st = stat_merge(st, Stat{m, l});
-}
-
-// Gumbel noise of the 4 columns v0..v0+3 at position k.
-__device__ __forceinline__ void noise4(const RowState& rs, int k, uint32_t v0, float g[4]) {
-  const uint4 x = philox4x32_10(make_uint4(v0 >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
-  g[0] = gumbel_from_bits(x.x);
-  g[1] = gumbel_from_bits(x.y);
-  g[2] = gumbel_from_bits(x.z);
-  g[3] = gumbel_from_bits(x.w);
-}
-
-// The epilogue of 4 columns with the noise already drawn, in two parts (the
-// same arithmetic as epilogue4): the logits and the argmax key first, keeping
-// the scaled logits s, and the softmax statistics of s later.
-__device__ __forceinline__ void epilogue4_key(const RowState& rs, uint32_t v0, const float base[4],
-                                              const float bias[4], const float g[4], float* logits_out,
-                                              uint64_t& best, float s[4]) {
-  float lg[4];
+// The epilogue of N consecutive columns with the noise already drawn, in two
+// parts (the arithmetic of epilogue4 per column): the logits and the argmax
+// key first, keeping the scaled logits s, and the softmax statistics of s
+// later (only the proposal reads them).
+template <int N>
+__device__ __forceinline__ void epilogue_n_key(const RowState& rs, uint32_t v, const float base[N],
+                                               const float bias[N], const float g[N], float* logits_out,
+                                               uint64_t& best, float s[N]) {
+  float lg[N];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lg[i] = __fadd_rn(base[i], bias[i]);
-  *reinterpret_cast<float4*>(logits_out) = make_float4(lg[0], lg[1], lg[2], lg[3]);
+  for (int i = 0; i < N; ++i) lg[i] = __fadd_rn(base[i], bias[i]);
+  if constexpr (N == 1) *logits_out = lg[0];
+  else *reinterpret_cast<float2*>(logits_out) = make_float2(lg[0], lg[1]);
   if (rs.greedy) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) best = umax64(best, score_key(lg[i], v0 + i));
+    for (int i = 0; i < N; ++i) best = umax64(best, score_key(lg[i], v + i));
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < N; ++i) {
     s[i] = __fmul_rn(lg[i], rs.invT);
-    const float z = __fadd_rn(s[i], g[i]);
-    best = umax64(best, score_key(z, v0 + i));
+    best = umax64(best, score_key(__fadd_rn(s[i], g[i]), v + i));
   }
 }
 
-__device__ __forceinline__ void epilogue4_stat(const float s[4], Stat& st) {
-  float m4 = -INFINITY;
+template <int N>
+__device__ __forceinline__ void epilogue_n_stat(const float s[N], Stat& st) {
+  float m = -INFINITY;   // a NaN score counts as -inf
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m4 = fmaxf(m4, s[i]);
-  float l4 = 0.0f;
-  if (m4 != -INFINITY) {
+  for (int i = 0; i < N; ++i) m = fmaxf(m, s[i]);
+  float l = 0.0f;
+  if (m != -INFINITY) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l4 = __fadd_rn(l4, __expf(__fsub_rn(s[i], m4)));
+    for (int i = 0; i < N; ++i) l = __fadd_rn(l, __expf(__fsub_rn(s[i], m)));
   }
-  st = stat_merge(st, Stat{m4, l4});
+  st = stat_merge(st, Stat{m, l});
 }
 
 template <int RB, bool kBf16Base, bool kPacked>
@@ -1288,13 +1266,12 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
   const bool lds_ok = t < n_lds_units;        // this thread's LDS unit (if any) is unit t
   const int cg_l = kResRegGroups + (t >> 3);
 
-  // epilogue lane mapping after the reduce-scatter
-  // (RB = 1: every lane, column js of its group; RB = 2: 4 columns 4 eh .. of row er)
+  // epilogue lane mapping after the reduce-scatter: every lane has RB columns
+  // (RB = 1: column js of its group; RB = 2: columns 2 (js & 3) .. + 1 of row er)
   static_assert(RB == 1 || RB == 2, "rows of the small-batch resident kernel");
   const int er = RB == 2 ? (js >> 2) : 0;
-  const int eh = js & 1;
-  const bool e_act = (RB == 2 ? ((js >> 1) & 1) == 0 : true) && er < B;
-  const int ecol = RB == 1 ? js : 4 * eh;
+  const bool e_act = er < B;
+  const int ecol = RB == 1 ? js : 2 * (js & 3);
   const uint32_t v_r = (uint32_t)(col0 + 8 * cg_r + ecol);   // epilogue column(s), VGPR unit
   const uint32_t v_l = (uint32_t)(col0 + 8 * cg_l + ecol);   // epilogue column(s), LDS unit
   const bool ep_r = e_act && reg_ok;
@@ -1332,30 +1309,20 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
       if (er == rr) rs = rows[rr];
   };
 
-  // ---- noise and base logits of a position for this lane's epilogue quads
-  float gq[2][4];
+  // ---- noise and base logits of a position for this lane's epilogue columns
+  float gq[2][RB];
   Base4<kBf16Base> bq[2];
   auto make_noise = [&](int k) {
     if (e_act && !rs.greedy) {
-      if constexpr (RB == 1) {
-        gq[0][0] = noise1(rs, k, v_r);
-        if (lds_ok) gq[1][0] = noise1(rs, k, v_l);
-      } else {
-        noise4(rs, k, v_r, gq[0]);
-        if (lds_ok) noise4(rs, k, v_l, gq[1]);
-      }
+      noise_n<RB>(rs, k, v_r, gq[0]);
+      if (lds_ok) noise_n<RB>(rs, k, v_l, gq[1]);
     }
   };
   auto load_base = [&](int k) {
     const size_t row_off = ((size_t)er * K + k) * (size_t)V;
     const bool br = ep_r && !rs.pad, bl = ep_l && !rs.pad;
-    if constexpr (RB == 1) {
-      load_base1<kBf16Base>(bq[0], a.base, br ? row_off + v_r : 0);
-      load_base1<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
-    } else {
-      load_base4<kBf16Base>(bq[0], a.base, br ? row_off + v_r : 0);
-      load_base4<kBf16Base>(bq[1], a.base, bl ? row_off + v_l : 0);
-    }
+    load_base_n<kBf16Base, RB>(bq[0], a.base, br ? row_off + v_r : 0);
+    load_base_n<kBf16Base, RB>(bq[1], a.base, bl ? row_off + v_l : 0);
   };
   auto prepare = [&](int k) {
     make_noise(k);
@@ -1476,7 +1443,9 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
 
   for (int k = 0; k < K; ++k) {
     // ---- bias GEMV: VGPR unit, then LDS unit; reduce-scatter over the rank slices
-    float bias_r[4], bias_l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float bias_r[RB], bias_l[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) bias_l[i] = 0.0f;
     {
       float acc[RB][8];
 #pragma unroll
@@ -1538,27 +1507,24 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     // scaled logits are kept for the softmax statistics, which only the
     // proposal reads
     uint64_t best = 0;
-    float sr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sr[RB], sl[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) sr[i] = sl[i] = 0.0f;
     {
       float* out = a.logits + ((size_t)er * K + k) * (size_t)V;
-      if constexpr (RB == 1) {
-        if (ep_r)
-          epilogue1_key(rs, v_r, rs.pad ? 0.0f : widen_base1<kBf16Base>(bq[0]), bias_r[0], gq[0][0], out + v_r,
-                        best, sr[0]);
-        if (ep_l)
-          epilogue1_key(rs, v_l, rs.pad ? 0.0f : widen_base1<kBf16Base>(bq[1]), bias_l[0], gq[1][0], out + v_l,
-                        best, sl[0]);
-      } else {
-        if (ep_r) {
-          float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (!rs.pad) widen_base4<kBf16Base>(bq[0], base);
-          epilogue4_key(rs, v_r, base, bias_r, gq[0], out + v_r, best, sr);
-        }
-        if (ep_l) {
-          float base[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (!rs.pad) widen_base4<kBf16Base>(bq[1], base);
-          epilogue4_key(rs, v_l, base, bias_l, gq[1], out + v_l, best, sl);
-        }
+      if (ep_r) {
+        float base[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) base[i] = 0.0f;
+        if (!rs.pad) widen_base_n<kBf16Base, RB>(bq[0], base);
+        epilogue_n_key<RB>(rs, v_r, base, bias_r, gq[0], out + v_r, best, sr);
+      }
+      if (ep_l) {
+        float base[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) base[i] = 0.0f;
+        if (!rs.pad) widen_base_n<kBf16Base, RB>(bq[1], base);
+        epilogue_n_key<RB>(rs, v_l, base, bias_l, gq[1], out + v_l, best, sl);
       }
     }
 
@@ -1597,13 +1563,8 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
     {
       Stat st{-INFINITY, 0.0f};
       if (!rs.greedy) {
-        if constexpr (RB == 1) {
-          if (ep_r) epilogue1_stat(sr[0], st);
-          if (ep_l) epilogue1_stat(sl[0], st);
-        } else {
-          if (ep_r) epilogue4_stat(sr, st);
-          if (ep_l) epilogue4_stat(sl, st);
-        }
+        if (ep_r) epilogue_n_stat<RB>(sr, st);
+        if (ep_l) epilogue_n_stat<RB>(sl, st);
       }
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
