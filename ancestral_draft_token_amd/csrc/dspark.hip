@@ -981,10 +981,10 @@ __global__ __launch_bounds__(kThreads) void proposal_softmax(PropArgs a) {
 // Positions are separated by an exchange: each workgroup publishes its
 // per-row argmax key as one 64-bit word tagged with the position as soon as
 // it is merged, and every workgroup polls all words (a bounded wait) and
-// reduces them in the same order, so all agree on d_k. The softmax statistics (read only by the proposal) and the Gumbel
-// noise of position k+1 do not depend on d_k and are computed while the
-// first reads are in flight; the base logits of k+1 are loaded with the E
-// rows of d_k.
+// reduces them in the same order, so all agree on d_k. The softmax
+// statistics (read only by the proposal) and the Gumbel noise of position k+1
+// do not depend on d_k and are computed while the first reads are in flight;
+// the base logits of k+1 are loaded with the E rows of d_k.
 // ---------------------------------------------------------------------------
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / 64;
@@ -1197,7 +1197,15 @@ __device__ __forceinline__ void reduce_scatter(const float (&acc)[RB][8], int js
 // of columns v - v % 4 .., the values every column gets from its block.
 template <int N>
 __device__ __forceinline__ void noise_n(const RowState& rs, int k, uint32_t v, float g[N]) {
-  const uint4 x = philox4x32_10(make_uint4(v >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), rs.key0, rs.key1);
+  uint32_t k0 = rs.key0, k1 = rs.key1;
+  if constexpr (N == 2) {
+    // two rows: the keys differ by lane; taken through an opaque copy, the
+    // round keys are formed here instead of being precomputed and held in
+    // vector registers across the position loop (which spilled them)
+    asm volatile("v_mov_b32 %0, %1" : "=v"(k0) : "v"(rs.key0));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(k1) : "v"(rs.key1));
+  }
+  const uint4 x = philox4x32_10(make_uint4(v >> 2, (uint32_t)k, rs.ctr2, rs.ctr3), k0, k1);
   const uint32_t c = v & 3u;
   g[0] = gumbel_from_bits(c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w);
   if constexpr (N == 2) g[1] = gumbel_from_bits(c == 0 ? x.y : x.w);

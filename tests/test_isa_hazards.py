@@ -1,5 +1,6 @@
 """Checks on the gfx950 assembly of the large-batch (MFMA) kernel, and on the
-compiler's hazard model that its register reuse relies on.
+compiler's hazard model that its register reuse relies on; also that the
+small-batch resident kernel has no scratch.
 
 The kernel keeps W resident in registers: 62 of its 64 A-operand fragments
 per lane live in AGPRs for the whole launch, read there by the matrix
@@ -97,6 +98,25 @@ def test_no_agpr_spill(asm, variant):
 def test_no_spill_in_inner_loops(asm, variant):
     bad = [s for d, s in _scratch_by_depth(_function(asm, variant)) if d >= 2]
     assert not bad, bad[:5]
+
+
+# The small-batch (VALU) resident kernel, <rows, bf16 base, packed W>: no
+# scratch at all. Its position loop polls exchange words while the next
+# position's noise and statistics are computed; a spill reload there waits for
+# every load in flight, the polls included (a two-row build spilled Philox
+# round keys, reloaded in the next position's noise).
+SMALL = [f"ILi{rb}ELb{b}ELb{p}EE" for rb in (1, 2) for b in (0, 1) for p in (0, 1)]
+
+
+@pytest.mark.parametrize("variant", SMALL)
+def test_small_batch_kernel_has_no_scratch(asm, variant):
+    kernel = "markov_bias_gumbel_argmax_resident"
+    name = f"_ZN6dspark{len(kernel)}{kernel}{variant}EvNS_7ResArgsE"
+    desc = re.search(r"\.amdhsa_kernel " + re.escape(name) + r"\n(.*?)\.end_amdhsa_kernel", asm, re.S).group(1)
+    assert int(re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", desc).group(1)) == 0
+    start = asm.index(f"\n{name}:")
+    body = asm[start:asm.index(".Lfunc_end", start)]
+    assert "scratch_" not in body
 
 
 def test_depth_parser():
