@@ -53,7 +53,7 @@ def algorithmic_bytes(w, resident):
     written; the proposal re-reads the logits and writes q. A kernel cannot
     move fewer bytes than these, so their rate is at most the HBM peak.
 
-    method (the survey's model): the same with W read once per position, as
+    method (the method's own model): the same with W read once per position, as
     the method defines the bias of each position. The resident plans keep W
     on chip for the whole block, so their rate under this model can exceed
     the HBM peak; it is reported, labelled, and never used as the fraction.

@@ -15,17 +15,17 @@ def require_gpu():
         pytest.skip("no GPU")
 
 
-_REPORT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out", "gpu_tests.log")
+_REPORT = os.environ.get("DSPARK_TEST_LOG", "")
 
 
 def say(msg: str):
     """Name the case before each GPU step, flushed, so a crash still says where it
-    was. Parity reports (near-tie counts, largest errors) also go to
-    gpurun_out/gpu_tests.log when that folder exists, since pytest keeps a
+    was. Parity reports (near-tie counts, largest errors) are also appended to
+    the file that DSPARK_TEST_LOG names, if it is set, since pytest keeps a
     passing test's output to itself."""
     print(f"[gpu] {msg}", flush=True)
     sys.stdout.flush()
-    if os.path.isdir(os.path.dirname(_REPORT)):
+    if _REPORT:
         with open(_REPORT, "a") as f:
             f.write(f"[gpu] {msg}\n")
 
