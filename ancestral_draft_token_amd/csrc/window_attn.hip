@@ -63,6 +63,7 @@ constexpr int kLdsV = kD * kVRow;            // 18,432
 constexpr int kSlots = 512;                  // resident workgroups: two per CU on 256 CUs
 constexpr int kMaxSplits = 128;              // splits of one key range at most (wa_combine_splits' table)
 constexpr int kFewSplits = 16;               // up to this many, each merge thread walks the splits itself
+constexpr double kMergeBatchCost = 0.2;      // one batch of eight splits' reads in the merge, in tiles
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -775,9 +776,13 @@ inline int check(int B, int K, int Hq, int Hkv, int D, int L, int W) {
 // V (32 KB): a round of resident workgroups (two per CU) takes as long as
 // its largest split plus the partial output it writes (16 heads x K
 // positions x 128 floats, ~1.8 tiles at K = 7), and the merge reads every
-// partial once more, spread over the GPU. B=88, 4 heads: 4 splits (1408
-// workgroups in 3 rounds) against 3 (1056 in 3 rounds of larger splits) or
-// 13 (fuller rounds, 4x the partials). B=1: 65 splits of one tile.
+// partial once more, spread over the GPU, with its reads of one output's
+// splits in dependent batches of eight (kMergeBatchCost tiles each: about
+// a memory round trip against a latency-bound tile of a split). B=88, 4
+// heads: 4 splits (1408 workgroups in 3 rounds) against 3 (1056 in 3 rounds
+// of larger splits) or 13 (fuller rounds, 4x the partials). B=1, window
+// 4096: 33 splits of two tiles (18.7 us a call against 23.0 with 65 of one,
+// 20.0 with 17 of four, 26.9 with 9 of eight).
 inline Plan plan(int B, int K, int Hkv, int W) {
   const long long span = (long long)W - 1 + K;                 // keys of the widest range
   const long long tiles = (span + kTileKeys - 1) / kTileKeys;
@@ -790,7 +795,8 @@ inline Plan plan(int B, int K, int Hkv, int W) {
     const long long per = (tiles + S - 1) / S;                 // tiles per split
     const long long ns = (tiles + per - 1) / per;              // splits actually used
     const long long rounds = (pairs * ns + kSlots - 1) / kSlots;
-    const double cost = (double)rounds * ((double)per + part) + (double)(pairs * ns) * part / kSlots;
+    const double cost = (double)rounds * ((double)per + part) + (double)(pairs * ns) * part / kSlots +
+                        (ns > 1 ? kMergeBatchCost * (double)((ns + 7) / 8) : 0.0);
     if (S == 1 || cost < best_cost - 1e-9) {
       best_cost = cost;
       best = S;

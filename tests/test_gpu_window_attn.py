@@ -119,6 +119,7 @@ def check(o, lse, o_ref, lse_ref, tol_o):
     (3, 8, 16, 1, 40, 8, [0, 7, 30]),
     (2, 7, 64, 4, 9100, 4096, [4095, 9000]),
     (1, 1, 16, 1, 5000, 4096, [4999]),
+    (1, 7, 64, 4, 8200, 4096, [8192]),   # the benchmark's one-row shape: 33 splits of two tiles
 ])
 def test_window_attention_parity(B, K, Hq, Hkv, L, W, P):
     q, kc, vc = _inputs(B, K, Hq, Hkv, L, seed=B * 100 + K + W)
