@@ -1680,12 +1680,13 @@ __global__ __launch_bounds__(kResThreads, 1) void markov_bias_gumbel_argmax_resi
 
 // ---------------------------------------------------------------------------
 // Resident path, MFMA form (2 < B <= 128). Same block structure as the VALU
-// resident kernel: one persistent launch, one 512-thread workgroup per CU
-// owning up to 784 columns, W on chip for the whole block. Here the slice is
-// held as bf16 A-operand fragments of v_mfma_f32_16x16x32_bf16 (A = W^T: 16
-// columns x 32 rank rows; lane l holds column l % 16, rank rows 8 (l / 16) ..
-// + 7): M-tiles 0..31 in VGPRs (four per wave), 32..48 in LDS. The B operand
-// is the embedding rows of one N-tile of 16 rows, staged in LDS
+// resident kernel: one persistent launch, one workgroup per CU owning up to
+// 784 columns, W on chip for the whole block; here 256 threads, one wave per
+// SIMD with all 512 registers of a lane. The slice is held as bf16 A-operand
+// fragments of v_mfma_f32_16x16x32_bf16 (A = W^T: 16 columns x 32 rank rows;
+// lane l holds column l % 16, rank rows 8 (l / 16) .. + 7): M-tiles 0..31 in
+// registers (eight per wave, their fragments in AGPRs), 32..48 in LDS. The B
+// operand is the embedding rows of one N-tile of 16 rows, staged in LDS
 // (double-buffered) and held in registers while every M-tile of the wave
 // uses it. The accumulator leaves each lane 4 consecutive columns of one row
 // (rows 4 (l / 16) .. + 3 of D = columns, column l % 16 of D = row), the
