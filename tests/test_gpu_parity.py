@@ -102,6 +102,25 @@ def test_single_row_cases(case):
     full_check(w)
 
 
+@pytest.mark.parametrize("case", [
+    dict(temperature=lambda b: [0.0, 1.3][b]),
+    dict(n_real=1, pad_base="nan", base_dtype="bf16", temperature=0.8),
+    dict(n_real=0, temperature=lambda b: [1.0, 0.0][b]),
+    dict(V=1000, r=64, temperature=lambda b: [0.7, 2.5][b]),
+    dict(V=2056, r=96, K=5, temperature=lambda b: [0.4, 0.0][b], base_dtype="bf16"),
+], ids=["greedy_and_hot", "padding_nan_bf16", "all_padding", "v1000_ragged", "v2056_r96_bf16"])
+def test_two_row_cases(case):
+    """Two rows (the small-batch kernel's two-columns-per-lane form, each row
+    on half of every workgroup's lanes): a greedy row beside a sampling row,
+    a padding row with NaN base logits, both rows padding, a vocabulary that
+    is not a multiple of 16, and one that leaves most workgroups without
+    columns."""
+    from ancestral_draft_token_amd import dspark_launch_plan
+    w = inputs.tiny(B=2, fixed_seed=None, fixed_offset=None, data_seed=17, **case)
+    assert 4 in dspark_launch_plan(w.B, w.K, w.V, w.r), "a resident plan expected"
+    full_check(w)
+
+
 def test_prev_token_out_of_range_is_clamped():
     w = inputs.tiny(B=3, K=3, fixed_seed=None, fixed_offset=None)
     w.prev_token[:] = [-7, w.V, 2**30]
