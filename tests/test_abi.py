@@ -271,6 +271,21 @@ def test_window_attention_workspace_bytes(lib):
     assert adt.dspark_window_attention_workspace_bytes(1, 7, 64, 4, 128, 8199, 4) == 0      # K > W
 
 
+def test_window_attention_split_plan_at_one_row(lib):
+    """The split plan shows in the workspace size: partial outputs and (max,
+    sum) for B * Hkv * S * K * 16 rows, each region rounded up to 256 bytes.
+    One row of the benchmark shape (window 4096: 65 tiles of 64 keys) takes
+    33 splits of two tiles, the fastest measured (65 splits of one tile, the
+    choice when the merge's read batches were left out of the cost, was 23.0
+    against 18.7 us a call)."""
+    def size(S, B=1, K=7, Hkv=4):
+        rows = B * Hkv * S * K * 16
+        up = lambda x: (x + 255) // 256 * 256
+        return up(rows * 128 * 4) + up(rows * 2 * 4)
+    assert adt.dspark_window_attention_workspace_bytes(1, 7, 64, 4, 128, 8199, 4096) == size(33)
+    assert adt.dspark_window_attention_workspace_bytes(1, 8, 64, 4, 128, 8200, 4096) == size(33, K=8)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), adt.DSPARK_ERR_ARG),
     (dict(ctx=None), adt.DSPARK_ERR_ARG),
